@@ -1,0 +1,233 @@
+/*
+ * dg_canvas.h — C ABI of the MI355X (gfx950) per-step canvas sampler used by
+ * block-diffusion decoding.
+ *
+ * One sampler step turns the denoiser's logits for B canvases of L positions
+ * ([B*L, V] rows, V contiguous) into the next canvas and a stop decision:
+ *
+ *   per position  temperature-scaled softmax, its entropy (nats), the argmax of
+ *                 the raw logits and one multinomial sample;
+ *   per canvas    sort the L entropies ascending, accept the longest sorted
+ *                 prefix whose cumulative entropy minus its largest entropy is
+ *                 at most b, write the sample at accepted positions and a fresh
+ *                 uniform vocabulary token everywhere else, and evaluate the
+ *                 adaptive stop (argmax canvas unchanged from the previous step
+ *                 and mean entropy below a threshold).
+ *
+ * Sources (web pages on DiffusionGemma):
+ *   "DiffusionGemma Lab" (shadowgraph.io), §2 "The generation algorithm, as
+ *       written in the code", items 1-5 and 7; §3 EXP A and EXP B; "Side
+ *       finding: an upstream bug".
+ *   "DiffusionGemma: Parallel Denoising From an Autoregressive Checkpoint"
+ *       (boxwrench.dev), "Finding": Algorithm 1 (entropy-bounded acceptance,
+ *       temperature annealing, adaptive stopping) and the hardware paragraph.
+ *
+ * The pages fix the rules but not how the multinomial sample or the noise is
+ * drawn. This library fixes one random protocol so that its integer outputs
+ * are reproducible bit for bit (a "two-level Gumbel-max" over interleaved
+ * vocabulary blocks driven by Philox4x32-10, Salmon et al., SC'11):
+ *
+ *   key      = (low 32 bits of seed_c, high 32 bits of seed_c) for canvas c
+ *   counter  = (c0, position l, step s, tag)
+ *   tags     INIT = 0, BLOCK = 1, ELEM = 2, RENOISE = 3
+ *   uniform  U(w) = (2*(w >> 9) + 1) * 2^-24   (in (0,1), exact in fp32)
+ *   Gumbel   G(w) = -ln(-ln U(w))
+ *   blocks   vocabulary id v lies in block j = 64*(v >> 15) + ((v >> 3) & 63):
+ *            a block is one 8-id slot of each of the 64 consecutive 512-id
+ *            stripes of a 32768-id supergroup (512 ids when full).
+ *   sample   j* = argmax_j (LSE_{v in j}(z_v/T) + G(w0 of (j, l, s, BLOCK)));
+ *            y  = argmax_{v in j*} (z_v/T + G(word v&3 of (v>>2, l, s, ELEM)));
+ *            ties go to the lowest j, then the lowest v. By the Gumbel-max
+ *            property P(y = v) = softmax(z/T)_v exactly.
+ *   uniform token for position l at step s: floor(w0 * V / 2^32) with
+ *            w0 from (0, l, s, RENOISE); initial canvas: (0, l, 0, INIT).
+ *   temperature at step s: (float)(T0 + (T1-T0) * min(s, S-1) / (S-1)),
+ *            evaluated in double, T0 when S == 1.
+ *
+ * Conventions for every entry point
+ *   - Device pointers are addresses in the memory of the context's device;
+ *     host pointers are ordinary CPU memory. Each argument says which.
+ *   - The caller owns every buffer it passes. The context owns only its scratch,
+ *     sized at dg_create from max_batch and params.vocab; no call allocates
+ *     device memory after dg_create.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work on
+ *     it and return without waiting, except dg_run_canvas, which waits once per
+ *     step for the stop flags.
+ *   - Every argument is validated before anything is enqueued. On any error
+ *     nothing is written to any output; dg_last_error() names the offending
+ *     argument or the failing runtime call.
+ *   - A context is used by one host thread and one stream at a time.
+ *   - Logits must be finite or -inf (probability 0). A row needs at least one
+ *     finite logit. NaN and +inf are outside the contract.
+ */
+#ifndef DG_CANVAS_H
+#define DG_CANVAS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dg_ctx dg_ctx;
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1,   /* an argument is out of range or NULL       */
+  DG_ERR_UNSUPPORTED = 2,   /* valid request outside what is implemented */
+  DG_ERR_OUT_OF_MEMORY = 3, /* dg_create could not allocate its scratch  */
+  DG_ERR_DEVICE = 4,        /* a HIP runtime call failed                 */
+  DG_ERR_CALLBACK = 5       /* the denoiser callback returned non-zero   */
+} dg_status;
+
+typedef enum { DG_DTYPE_F32 = 0, DG_DTYPE_BF16 = 1 } dg_dtype;
+
+/* Sampler parameters. Defaults are the official ones reported on the pages:
+ * canvas of 256 ("DiffusionGemma Lab", §1), bound b = 0.1 (§2 item 2),
+ * temperature 0.8 -> 0.4 (§2 item 4), stop at mean entropy < 0.005 (§2 item 3),
+ * cap of 48 steps (boxwrench.dev, Algorithm 1, adaptive stopping). */
+typedef struct {
+  int32_t canvas_len;       /* L, 1..256                                   */
+  int32_t vocab;            /* V, 2..2^31-1                                */
+  float entropy_bound;      /* b >= 0 (b < 0 could accept nothing)         */
+  float temp_start;         /* T0 > 0                                      */
+  float temp_end;           /* T1 > 0                                      */
+  int32_t temp_steps;       /* S >= 1: steps over which T goes T0 -> T1    */
+  int32_t max_steps;        /* step cap >= 1                               */
+  float stop_mean_entropy;  /* > 0; stop needs mean entropy strictly below */
+} dg_params;
+
+/* Fills *p with the defaults above (vocab = 262144, temp_steps = max_steps =
+ * 48). Returns DG_ERR_INVALID_ARG if p is NULL. */
+dg_status dg_params_default(dg_params* p);
+
+/* Checks every field of *p against the ranges above. The error message names
+ * the first offending field (the pages report an upstream validator whose
+ * error path named the wrong attribute: "DiffusionGemma Lab", "Side finding").
+ * Host only; no context needed. Message via dg_last_error(NULL). */
+dg_status dg_params_check(const dg_params* p);
+
+/* Creates a context on HIP device `device` for batches of up to max_batch
+ * canvases (1..65536) with parameters *params (copied). Allocates the device
+ * scratch (per-row partials, tickets, argmax ping-pong buffers) and a small
+ * pinned host buffer. On failure *out is set to NULL and the message is
+ * available from dg_last_error(NULL). */
+dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params* params);
+
+/* Frees the context and its scratch. NULL is accepted. Waits for the device. */
+dg_status dg_destroy(dg_ctx* ctx);
+
+/* Message of the last failed call on ctx, or of the last failed context-free
+ * call (dg_create, dg_params_check, dg_temperature) of this thread when ctx is
+ * NULL. Never NULL; "" when there was no error. Valid until the next call. */
+const char* dg_last_error(const dg_ctx* ctx);
+
+/* Copy of the context's parameters. */
+dg_status dg_get_params(const dg_ctx* ctx, dg_params* out);
+
+/* Temperature at step `step` (>= 0) of the linear schedule of *p
+ * ("DiffusionGemma Lab", §2 item 4; boxwrench.dev, Algorithm 1, temperature
+ * annealing): (float)(T0 + (T1-T0)*min(step,S-1)/(S-1)) in double; T0 if S==1.
+ * Host only. */
+dg_status dg_temperature(const dg_params* p, int32_t step, float* out);
+
+/* Initial canvas ("DiffusionGemma Lab", §2 item 1: uniform random vocabulary
+ * tokens, not [MASK]). canvas[c*L + l] = floor(w0 * V / 2^32), w0 = word 0 of
+ * Philox(seed_c; (0, l, 0, INIT)).
+ *   B       1..max_batch
+ *   seeds   device, uint64 [B]
+ *   canvas  device, int32 [B, L], written */
+dg_status dg_canvas_init(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t* canvas,
+                         void* stream);
+
+/* Per-position statistics only (the streaming pass of a step). For every row
+ * r = c*L + l of an active canvas c:
+ *   entropy[r] = H of softmax(z_r / T_c), nats, >= +0  (fp32)
+ *   argmax[r]  = lowest v with z_rv = max_v z_rv (raw logits)
+ *   sample[r]  = the protocol's two-level Gumbel-max draw at step `step`
+ * Rows of inactive canvases are not written. Arguments:
+ *   logits       device, [B*L rows, row_stride elements] of `dtype`; base
+ *                16-byte aligned; row_stride >= V and a multiple of 8 (bf16)
+ *                or 4 (fp32), else DG_ERR_UNSUPPORTED
+ *   temperature  device, fp32 [B], each > 0 and finite
+ *   step         >= 0 (enters the random counters)
+ *   seeds        device, uint64 [B]
+ *   active       device, uint8 [B] (0 = skip canvas) or NULL = all active
+ *   entropy, argmax, sample  device outputs [B*L]; none may be NULL */
+dg_status dg_canvas_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                          int64_t row_stride, const float* temperature, int32_t step,
+                          const uint64_t* seeds, const uint8_t* active, float* entropy,
+                          int32_t* argmax, int32_t* sample, void* stream);
+
+/* Outputs of a step. Device pointers, caller-owned. canvas_out is required;
+ * any other may be NULL (not requested). Shapes: [B, L] or [B]. */
+typedef struct {
+  int32_t* canvas_out;       /* next canvas: sample at accepted positions, else a uniform token */
+  int32_t* argmax_out;       /* argmax canvas of this step (the decoded output when stopping)  */
+  int32_t* sample_out;       /* multinomial sample per position                                 */
+  uint8_t* accept_out;       /* 1 at accepted positions                                         */
+  float* entropy_out;        /* per-position entropy, nats                                      */
+  int32_t* n_accept_out;     /* [B] number of accepted positions (>= 1)                         */
+  float* mean_entropy_out;   /* [B] mean of the L entropies                                     */
+  uint8_t* stop_out;         /* [B] adaptive stop fired at this step                            */
+} dg_step_out;
+
+/* Acceptance, renoise and stop only, from given per-position statistics
+ * (entropy, argmax, sample: device [B*L]). Follows "DiffusionGemma Lab", §2
+ * items 2, 3, 5 and boxwrench.dev Algorithm 1:
+ *   order positions by (entropy, position) ascending; with C_i the inclusive
+ *   cumulative sum and M_i the running maximum over that order, accept the
+ *   longest prefix with C_i - M_i <= b (always >= 1 position);
+ *   canvas_out = sample where accepted, else floor(w0*V/2^32) with w0 from
+ *   Philox(seed_c; (0, l, step, RENOISE));
+ *   stop = (prev_argmax given) && argmax == prev_argmax at all L positions
+ *          && mean entropy < stop_mean_entropy.
+ *   prev_argmax  device int32 [B, L], or NULL when there is no previous step
+ *   active       device uint8 [B] or NULL = all active; inactive canvases are
+ *                left untouched in every output. */
+dg_status dg_accept_renoise(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
+                            const int32_t* sample, int32_t step, const uint64_t* seeds,
+                            const int32_t* prev_argmax, const uint8_t* active,
+                            const dg_step_out* out, void* stream);
+
+/* One full sampler step: dg_canvas_stats followed by dg_accept_renoise, with
+ * the statistics kept in the context's scratch unless out requests them.
+ * Arguments as for those two calls. */
+dg_status dg_sampler_step(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                          int64_t row_stride, const float* temperature, int32_t step,
+                          const uint64_t* seeds, const int32_t* prev_argmax,
+                          const uint8_t* active, const dg_step_out* out, void* stream);
+
+/* Denoiser callback of dg_run_canvas: must enqueue on `stream` the writing of
+ * logits for step `step` into logits_dev ([B*L, V] rows of the run's dtype,
+ * row stride V) from the current canvas (device int32 [B, L]); canvases with
+ * active_dev[c] == 0 may be skipped. Returns 0 on success. */
+typedef int (*dg_denoise_fn)(void* user, int32_t step, const int32_t* canvas_dev,
+                             const uint8_t* active_dev, void* logits_dev, void* stream);
+
+/* Whole denoising of B canvases ("DiffusionGemma Lab", §2 items 1-5;
+ * boxwrench.dev Algorithm 1): initial uniform canvas, then for
+ * s = 0 .. max_steps-1: callback, T_s from the schedule, one step over the
+ * active canvases; a canvas whose stop fires is finished with that step's
+ * argmax canvas and leaves the batch; after max_steps the remaining canvases
+ * are finished with the last argmax canvas.
+ *   seeds           host uint64 [B]
+ *   logits_scratch  device, [B*L, V] of dtype (16-byte aligned; V a multiple of
+ *                   8 for bf16 or 4 for fp32), written by the callback
+ *   final_argmax    device int32 [B, L], written
+ *   steps_used      host int32 [B], written (1..max_steps)
+ *   stopped         host uint8 [B], written: 1 if the adaptive stop fired
+ * Returns DG_ERR_CALLBACK if the callback fails; steps_used then holds the
+ * steps completed so far (finished canvases keep their values). */
+dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
+                        void* user, dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
+                        int32_t* steps_used, uint8_t* stopped, void* stream);
+
+/* Library version string. */
+const char* dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_CANVAS_H */

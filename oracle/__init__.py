@@ -1,0 +1,29 @@
+"""Oracle of the canvas sampler: a plain, slow, fp64 CPU implementation of what
+the HIP path computes, written from the pages' description of the sampler.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and bench.py's
+CPU-baseline leg may import it. The product path (canvas_sampler_amd and the
+HIP library) never calls it, and the two share no code.
+
+Pins (tests/test_oracle_*.py, run with -m "not gpu"):
+  philox.philox4x32_10   Random123 known-answer vectors; PyTorch ATen engine
+  philox.uniform_open01  exact endpoints, chi-square uniformity
+  sampler.temperature    numpy.linspace in fp32; clamp; single-step schedule
+  sampler.entropy        closed forms (ln V, 0, ln k), scipy.stats.entropy,
+                         6.91 nats at V = 1000 ("DiffusionGemma Lab" EXP A)
+  sampler.argmax_raw     planted maxima and ties, brute-force loop
+  sampler.block_*        brute-force membership loop, partition of [0, V)
+  sampler.sample_*       chi-square against softmax; planted dominant id;
+                         two-level vs per-element agreement in distribution
+  sampler.accept         brute-force subset enumeration (L <= 12); equal-
+                         entropy closed form; >= 1 commit; monotone in b
+  sampler.uniform_tokens chi-square; top-bits formula for power-of-two V
+  sampler.stop_test      truth table
+  sampler.step / run     constant canvas (ln V, 1 commit, no stop); one-hot
+                         canvas (H = 0, all commit, stops at the 2nd step);
+                         low-confidence canvas (1 commit/step, 48-step cap);
+                         trend directions of "DiffusionGemma Lab" EXP B.
+No function is parity-unpinned; the bit-level choice of random protocol is
+pinned only by agreement of the two independent implementations.
+"""
+from . import philox, sampler  # noqa: F401
