@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Throughput of one canvas-sampler step on one MI355X.
+
+A step is the whole per-step hot path on one batch of synthetic logits that
+are already resident in HBM: the streaming statistics kernel (entropy, argmax,
+two-level Gumbel-max sample per position) followed by the per-canvas
+accept/renoise/stop kernel. Workload: one canvas of 256 positions, a
+262,144-token vocabulary, bf16 logits from the sharpening denoiser; the logits
+rotate over several 128 MiB buffers so that each step reads from HBM rather
+than from the 256 MB last-level cache. Each step is replayed from a captured
+HIP graph (one graph per buffer), so host launch cost is not what is timed.
+
+Prints one JSON line: steps/s (value), positions/s, the statistics kernel's
+achieved HBM bandwidth against the 8 TB/s peak (HIP events on the launch
+stream), and the oracle's rate on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sampler steps/sec & canvas-positions/sec at 256xV=262144 bf16; % HBM peak"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "canvas_stats_traffic.json")
+STATS_SRC = os.path.join(ROOT, "canvas_sampler_amd", "csrc", "canvas_stats.hip")
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(bytes_per_launch):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != _sha(STATS_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _time_graphs(graphs, k, torch):
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(k):
+        graphs[i % len(graphs)].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--rotate", type=int, default=4, help="logits buffers (>= 4 beats the LLC)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(canvases shard without communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from canvas_sampler_amd import binding as B
+    from canvas_sampler_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L, V, Bn = 256, 262144, 1
+    R = max(1, args.rotate)
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=16)
+    ctx = B.Context(params, max_batch=Bn)
+    dev = "cuda"
+    logits = [synth.sharpening_logits(1002, r, L, V, m0_max=6.0, dtype=torch.bfloat16, device=dev)
+              for r in range(R)]
+    temps = [torch.tensor([B.dg_temperature(params, r)], device=dev) for r in range(R)]
+    seeds = torch.tensor([0], dtype=torch.int64, device=dev)
+    am = [torch.empty(L, dtype=torch.int32, device=dev) for _ in range(2)]
+    canvas = torch.empty(L, dtype=torch.int32, device=dev)
+    stop = torch.empty(1, dtype=torch.uint8, device=dev)
+    nacc = torch.empty(1, dtype=torch.int32, device=dev)
+    ent = torch.empty(L, device=dev)
+    smp = torch.empty(L, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+
+    def full_step(r):
+        out = ctx.step_out(canvas, argmax_out=am[r & 1], stop_out=stop, n_accept_out=nacc)
+        ctx.dg_sampler_step(logits[r], temps[r], r, seeds, out, prev_argmax=am[(r + 1) & 1])
+
+    def stats_only(r):
+        ctx.dg_canvas_stats(logits[r], temps[r], r, seeds, ent, am[r & 1], smp)
+
+    def capture(fn):
+        graphs = []
+        with torch.cuda.stream(stream):
+            for r in range(R):
+                fn(r)                      # eager warm-up outside capture
+            torch.cuda.synchronize()
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    fn(r)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    step_graphs = capture(full_step)
+    stats_graphs = capture(stats_only)
+
+    with torch.cuda.stream(stream):
+        _time_graphs(step_graphs, args.warmup, torch)
+        t_step = _time_graphs(step_graphs, args.steps, torch)
+        _time_graphs(stats_graphs, args.warmup, torch)
+        t_stats = _time_graphs(stats_graphs, args.steps, torch)
+        # eager (no graph) rate, for reference
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            full_step(i % R)
+        torch.cuda.synchronize()
+        t_eager = time.perf_counter() - t0
+
+    steps_per_s = args.steps / t_step
+    bytes_per_launch = Bn * L * V * 2
+    stats_s = t_stats / args.steps
+    achieved = bytes_per_launch / stats_s / 1e9
+    traffic = _traffic(bytes_per_launch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import sampler as O
+        z = logits[0].to("cpu").to(torch.float64).numpy()
+        temp = np.float32(temps[0].item())
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            O.step(z, temp, 0, 0)
+            n += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} full oracle steps of the same workload (256 rows x 262144 bf16 "
+                         f"logits, fp64 numpy, one thread) on {os.cpu_count()} host cores"}
+
+    rec = {
+        "metric": METRIC, "value": steps_per_s, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * t_step / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "single canvas, 256 positions x 262144 vocab, bf16 sharpening "
+                               f"logits, {R} rotating 128 MiB buffers, graph-replayed steps",
+                   "batch": Bn, "canvas_len": L, "vocab": V, "entropy_bound": 0.1,
+                   "temperature": "0.8->0.4 over 16 steps"},
+        "positions_per_s": steps_per_s * Bn * L,
+        "eager_steps_per_s": args.steps / t_eager,
+        "roofline": {"bound": "hbm", "kernel": "canvas_stats_kernel", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic, "avg_kernel_us": stats_s * 1e6,
+                     "algorithmic_bytes_per_launch": bytes_per_launch},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

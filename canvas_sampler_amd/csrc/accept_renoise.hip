@@ -1,0 +1,159 @@
+// accept_renoise_kernel and canvas_init_kernel: the per-canvas decisions of a
+// sampler step and the initial canvas.
+//
+// One 256-thread workgroup per canvas, one thread per position:
+//   - sort the L keys (entropy bits << 32 | position) ascending in LDS with a
+//     bitonic network (entropies are >= +0, so their fp32 bit patterns order
+//     like the values; equal entropies fall back to position order);
+//   - inclusive fp64 scan C_i of the sorted entropies; position i of the
+//     order is acceptable while C_i - H_i <= b (H_i is the running maximum of
+//     an ascending order), and the accepted set is the longest acceptable
+//     prefix ("DiffusionGemma Lab", §2 item 2; boxwrench.dev, Algorithm 1,
+//     entropy-bounded acceptance); it is never empty since C_0 - H_0 = 0;
+//   - next canvas: the sample where accepted, else a fresh uniform token
+//     (boxwrench.dev, Algorithm 1: the remainder is renoised uniformly);
+//   - stop = previous argmax given, equal at all positions, and mean entropy
+//     below the threshold ("DiffusionGemma Lab", §2 item 3).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dg {
+namespace {
+
+constexpr int kWaves = kAcceptThreads / kWave;
+
+__global__ __launch_bounds__(kAcceptThreads) void accept_renoise_kernel(AcceptArgs a) {
+  __shared__ uint64_t s_key[kAcceptThreads];
+  __shared__ double s_wsum[kWaves];
+  __shared__ int32_t s_wmin[kWaves];
+  __shared__ uint8_t s_acc[kAcceptThreads];
+
+  const int32_t canvas = blockIdx.x;
+  if (a.active != nullptr && a.active[canvas] == 0) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int32_t L = a.canvas_len;
+  const int64_t base = static_cast<int64_t>(canvas) * L;
+  const bool valid = tid < L;
+
+  float h = 0.0f;
+  int32_t am = 0, smp = 0;
+  if (valid) {
+    h = a.entropy[base + tid];
+    am = a.argmax[base + tid];
+    smp = a.sample[base + tid];
+  }
+  s_key[tid] = valid ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(tid))
+                     : ~0ull;
+  __syncthreads();
+
+  // bitonic sort of 256 keys, ascending
+  for (int k = 2; k <= kAcceptThreads; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int partner = tid ^ j;
+      uint64_t mine = s_key[tid];
+      const uint64_t other = s_key[partner];
+      const bool ascending = (tid & k) == 0;
+      const bool lower = tid < partner;
+      const uint64_t lo = mine < other ? mine : other;
+      const uint64_t hi = mine < other ? other : mine;
+      mine = (lower == ascending) ? lo : hi;
+      __syncthreads();
+      s_key[tid] = mine;
+      __syncthreads();
+    }
+  }
+
+  // inclusive fp64 scan of sorted entropies (wave scan + wave offsets)
+  const uint64_t key = s_key[tid];
+  const double hs = valid ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(key >> 32))) : 0.0;
+  double incl = hs;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += s_wsum[w];
+
+  // first sorted index that is not acceptable; k* = that index (or L)
+  const bool ok = valid && (incl - hs) <= static_cast<double>(a.bound);
+  int32_t first_bad = (valid && !ok) ? tid : L;
+  first_bad = wave_min_int(first_bad);
+  __syncthreads();
+  if (lane == 0) s_wmin[wave] = first_bad;
+  __syncthreads();
+  int32_t kstar = s_wmin[0];
+  for (int w = 1; w < kWaves; ++w) kstar = min(kstar, s_wmin[w]);
+  if (valid) s_acc[static_cast<uint32_t>(key)] = static_cast<uint8_t>(tid < kstar);
+
+  // mean entropy (fp64, in position order) and argmax stability
+  double hsum = valid ? static_cast<double>(h) : 0.0;
+  hsum = wave_sum(hsum);
+  const bool same = !valid || (a.prev_argmax != nullptr && a.prev_argmax[base + tid] == am);
+  __syncthreads();
+  if (lane == 0) s_wsum[wave] = hsum;
+  const int all_same = __syncthreads_and(same ? 1 : 0);
+  double total = 0.0;
+  for (int w = 0; w < kWaves; ++w) total += s_wsum[w];
+  const double mean_h = total / static_cast<double>(L);
+
+  if (valid) {
+    const bool accepted = s_acc[tid] != 0;
+    int32_t tok = smp;
+    if (!accepted) {
+      const uint64_t seed = a.seeds[canvas];
+      const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(a.step),
+                                      kTagRenoise, static_cast<uint32_t>(seed),
+                                      static_cast<uint32_t>(seed >> 32));
+      tok = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
+    }
+    a.canvas_out[base + tid] = tok;
+    if (a.accept_out) a.accept_out[base + tid] = accepted ? 1 : 0;
+    if (a.argmax_out) a.argmax_out[base + tid] = am;
+    if (a.sample_out) a.sample_out[base + tid] = smp;
+    if (a.entropy_out) a.entropy_out[base + tid] = h;
+  }
+  if (tid == 0) {
+    const bool stop = a.prev_argmax != nullptr && all_same &&
+                      mean_h < static_cast<double>(a.stop_mean_entropy);
+    if (a.n_accept_out) a.n_accept_out[canvas] = kstar;
+    if (a.mean_entropy_out) a.mean_entropy_out[canvas] = static_cast<float>(mean_h);
+    if (a.stop_out) a.stop_out[canvas] = stop ? 1 : 0;
+  }
+}
+
+// Initial canvas: position l of canvas c gets floor(w0 * V / 2^32) with w0
+// from Philox(seed_c; (0, l, 0, INIT)) ("DiffusionGemma Lab", §2 item 1).
+__global__ void canvas_init_kernel(const uint64_t* __restrict__ seeds, int32_t canvas_len,
+                                   int32_t vocab, int64_t total, int32_t* __restrict__ canvas) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int32_t c = static_cast<int32_t>(i / canvas_len);
+  const int32_t l = static_cast<int32_t>(i % canvas_len);
+  const uint64_t seed = seeds[c];
+  const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(l), 0u, kTagInit,
+                                  static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  canvas[i] = uniform_token(rw.w[0], static_cast<uint32_t>(vocab));
+}
+
+}  // namespace
+
+hipError_t launch_accept_renoise(const AcceptArgs& a, int32_t batch, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_renoise_kernel, dim3(batch), dim3(kAcceptThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_canvas_init(const uint64_t* seeds, int32_t batch, int32_t canvas_len,
+                              int32_t vocab, int32_t* canvas, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(batch) * canvas_len;
+  const int threads = 256;
+  const unsigned blocks = static_cast<unsigned>((total + threads - 1) / threads);
+  hipLaunchKernelGGL(canvas_init_kernel, dim3(blocks), dim3(threads), 0, stream, seeds,
+                     canvas_len, vocab, total, canvas);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,467 @@
+// C ABI of the canvas sampler (include/dg_canvas.h): context and scratch,
+// argument validation, kernel launches and the host-driven denoising loop.
+#include "../../include/dg_canvas.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+struct dg_ctx {
+  int device = 0;
+  int32_t max_batch = 0;
+  dg_params p{};
+  int32_t nsplit_override = 0;
+  int32_t nsplit_max = 8;
+  // device scratch
+  dg::RowPartial* partials = nullptr;   // [max_rows * nsplit_max]
+  uint32_t* tickets = nullptr;          // [max_rows], zero between launches
+  float* entropy = nullptr;             // [max_rows]
+  int32_t* argmax[2] = {nullptr, nullptr};
+  int32_t* sample = nullptr;
+  int32_t* canvas = nullptr;
+  uint64_t* seeds = nullptr;            // [max_batch]
+  float* temperature = nullptr;
+  uint8_t* active = nullptr;
+  uint8_t* stop = nullptr;
+  // pinned host staging
+  uint8_t* stop_host = nullptr;
+  uint8_t* active_host = nullptr;
+  float* temp_host = nullptr;
+  std::string err;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+dg_status set_err(dg_ctx* ctx, dg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (ctx)
+    ctx->err = buf;
+  else
+    g_err = buf;
+  return st;
+}
+
+#define DG_CHECK_HIP(ctx, call)                                                              \
+  do {                                                                                       \
+    hipError_t e_ = (call);                                                                  \
+    if (e_ != hipSuccess)                                                                    \
+      return set_err((ctx), DG_ERR_DEVICE, "%s failed: %s", #call, hipGetErrorString(e_));   \
+  } while (0)
+
+// Makes the context's device current for the duration of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
+
+dg_status check_params(dg_ctx* ctx, const dg_params* p) {
+  if (!p) return set_err(ctx, DG_ERR_INVALID_ARG, "params is NULL");
+  if (p->canvas_len < 1 || p->canvas_len > 256)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "params.canvas_len = %d is outside 1..256", p->canvas_len);
+  if (p->vocab < 2)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "params.vocab = %d is below 2", p->vocab);
+  if (!(p->entropy_bound >= 0.0f) || !std::isfinite(p->entropy_bound))
+    return set_err(ctx, DG_ERR_INVALID_ARG,
+                   "params.entropy_bound = %g must be finite and >= 0 (a negative bound could accept no position)",
+                   static_cast<double>(p->entropy_bound));
+  if (!finite_positive(p->temp_start))
+    return set_err(ctx, DG_ERR_INVALID_ARG, "params.temp_start = %g must be finite and > 0",
+                   static_cast<double>(p->temp_start));
+  if (!finite_positive(p->temp_end))
+    return set_err(ctx, DG_ERR_INVALID_ARG, "params.temp_end = %g must be finite and > 0",
+                   static_cast<double>(p->temp_end));
+  if (p->temp_steps < 1)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "params.temp_steps = %d must be >= 1", p->temp_steps);
+  if (p->max_steps < 1)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "params.max_steps = %d must be >= 1", p->max_steps);
+  if (!finite_positive(p->stop_mean_entropy))
+    return set_err(ctx, DG_ERR_INVALID_ARG, "params.stop_mean_entropy = %g must be finite and > 0",
+                   static_cast<double>(p->stop_mean_entropy));
+  return DG_OK;
+}
+
+dg_status check_batch(dg_ctx* ctx, int32_t B) {
+  if (B < 1 || B > ctx->max_batch)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "B = %d is outside 1..max_batch (%d)", B, ctx->max_batch);
+  return DG_OK;
+}
+
+dg_status check_logits(dg_ctx* ctx, const void* logits, dg_dtype dtype, int64_t row_stride) {
+  if (!logits) return set_err(ctx, DG_ERR_INVALID_ARG, "logits is NULL");
+  if (dtype != DG_DTYPE_F32 && dtype != DG_DTYPE_BF16)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "dtype = %d is not DG_DTYPE_F32 or DG_DTYPE_BF16",
+                   static_cast<int>(dtype));
+  if (row_stride < ctx->p.vocab)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "row_stride = %lld is below vocab (%d)",
+                   static_cast<long long>(row_stride), ctx->p.vocab);
+  if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "logits is not 16-byte aligned");
+  const int64_t per16 = dtype == DG_DTYPE_BF16 ? 8 : 4;
+  if (row_stride % per16 != 0)
+    return set_err(ctx, DG_ERR_UNSUPPORTED,
+                   "row_stride = %lld must be a multiple of %lld elements (16 bytes)",
+                   static_cast<long long>(row_stride), static_cast<long long>(per16));
+  return DG_OK;
+}
+
+int32_t effective_nsplit(const dg_ctx* ctx, int32_t rows) {
+  int32_t n = ctx->nsplit_override > 0 ? ctx->nsplit_override : dg::choose_nsplit(rows, ctx->p.vocab);
+  if (n > ctx->nsplit_max) n = ctx->nsplit_max;
+  return n < 1 ? 1 : n;
+}
+
+dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                        int64_t row_stride, const float* temperature, int32_t step,
+                        const uint64_t* seeds, const uint8_t* active, float* entropy,
+                        int32_t* argmax, int32_t* sample, hipStream_t stream) {
+  dg::StatsArgs a{};
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = ctx->p.vocab;
+  a.canvas_len = ctx->p.canvas_len;
+  a.rows = B * ctx->p.canvas_len;
+  a.nsplit = effective_nsplit(ctx, a.rows);
+  a.temperature = temperature;
+  a.seeds = seeds;
+  a.step = step;
+  a.active = active;
+  a.entropy = entropy;
+  a.argmax = argmax;
+  a.sample = sample;
+  a.partials = ctx->partials;
+  a.tickets = ctx->tickets;
+  DG_CHECK_HIP(ctx, dg::launch_canvas_stats(a, dtype == DG_DTYPE_BF16, stream));
+  return DG_OK;
+}
+
+dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
+                         const int32_t* sample, int32_t step, const uint64_t* seeds,
+                         const int32_t* prev_argmax, const uint8_t* active, const dg_step_out* out,
+                         bool copy_stats, hipStream_t stream) {
+  dg::AcceptArgs a{};
+  a.entropy = entropy;
+  a.argmax = argmax;
+  a.sample = sample;
+  a.seeds = seeds;
+  a.prev_argmax = prev_argmax;
+  a.active = active;
+  a.step = step;
+  a.canvas_len = ctx->p.canvas_len;
+  a.vocab = ctx->p.vocab;
+  a.bound = ctx->p.entropy_bound;
+  a.stop_mean_entropy = ctx->p.stop_mean_entropy;
+  a.canvas_out = out->canvas_out;
+  if (copy_stats) {
+    a.argmax_out = out->argmax_out;
+    a.sample_out = out->sample_out;
+    a.entropy_out = out->entropy_out;
+  }
+  a.accept_out = out->accept_out;
+  a.n_accept_out = out->n_accept_out;
+  a.mean_entropy_out = out->mean_entropy_out;
+  a.stop_out = out->stop_out;
+  DG_CHECK_HIP(ctx, dg::launch_accept_renoise(a, B, stream));
+  return DG_OK;
+}
+
+template <typename T>
+hipError_t dev_alloc(T** p, size_t n) {
+  return hipMalloc(reinterpret_cast<void**>(p), n * sizeof(T) + 16);
+}
+
+void free_ctx(dg_ctx* c) {
+  if (!c) return;
+  hipFree(c->partials);
+  hipFree(c->tickets);
+  hipFree(c->entropy);
+  hipFree(c->argmax[0]);
+  hipFree(c->argmax[1]);
+  hipFree(c->sample);
+  hipFree(c->canvas);
+  hipFree(c->seeds);
+  hipFree(c->temperature);
+  hipFree(c->active);
+  hipFree(c->stop);
+  hipHostFree(c->stop_host);
+  hipHostFree(c->active_host);
+  hipHostFree(c->temp_host);
+  delete c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dg_version(void) { return "dgcanvas 0.1 (gfx950)"; }
+
+dg_status dg_params_default(dg_params* p) {
+  if (!p) return set_err(nullptr, DG_ERR_INVALID_ARG, "p is NULL");
+  p->canvas_len = 256;
+  p->vocab = 262144;
+  p->entropy_bound = 0.1f;
+  p->temp_start = 0.8f;
+  p->temp_end = 0.4f;
+  p->temp_steps = 48;
+  p->max_steps = 48;
+  p->stop_mean_entropy = 0.005f;
+  return DG_OK;
+}
+
+dg_status dg_params_check(const dg_params* p) { return check_params(nullptr, p); }
+
+const char* dg_last_error(const dg_ctx* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+dg_status dg_get_params(const dg_ctx* ctx, dg_params* out) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  if (!out) return set_err(const_cast<dg_ctx*>(ctx), DG_ERR_INVALID_ARG, "out is NULL");
+  *out = ctx->p;
+  return DG_OK;
+}
+
+dg_status dg_temperature(const dg_params* p, int32_t step, float* out) {
+  dg_status st = check_params(nullptr, p);
+  if (st != DG_OK) return st;
+  if (step < 0) return set_err(nullptr, DG_ERR_INVALID_ARG, "step = %d is negative", step);
+  if (!out) return set_err(nullptr, DG_ERR_INVALID_ARG, "out is NULL");
+  const double t0 = p->temp_start, t1 = p->temp_end;
+  if (p->temp_steps == 1) {
+    *out = static_cast<float>(t0);
+  } else {
+    const int32_t s = step < p->temp_steps - 1 ? step : p->temp_steps - 1;
+    *out = static_cast<float>(t0 + (t1 - t0) * static_cast<double>(s) / static_cast<double>(p->temp_steps - 1));
+  }
+  return DG_OK;
+}
+
+dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params* params) {
+  if (!out) return set_err(nullptr, DG_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  dg_status st = check_params(nullptr, params);
+  if (st != DG_OK) return st;
+  if (max_batch < 1 || max_batch > 65536)
+    return set_err(nullptr, DG_ERR_INVALID_ARG, "max_batch = %d is outside 1..65536", max_batch);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1)
+    return set_err(nullptr, DG_ERR_DEVICE, "no HIP device is available");
+  if (device < 0 || device >= ndev)
+    return set_err(nullptr, DG_ERR_INVALID_ARG, "device = %d is outside 0..%d", device, ndev - 1);
+  DeviceGuard guard(device);
+  if (!guard.ok) return set_err(nullptr, DG_ERR_DEVICE, "hipSetDevice(%d) failed", device);
+
+  dg_ctx* c = new dg_ctx();
+  c->device = device;
+  c->max_batch = max_batch;
+  c->p = *params;
+  const size_t rows = static_cast<size_t>(max_batch) * params->canvas_len;
+  bool ok = dev_alloc(&c->partials, rows * c->nsplit_max) == hipSuccess &&
+            dev_alloc(&c->tickets, rows) == hipSuccess && dev_alloc(&c->entropy, rows) == hipSuccess &&
+            dev_alloc(&c->argmax[0], rows) == hipSuccess && dev_alloc(&c->argmax[1], rows) == hipSuccess &&
+            dev_alloc(&c->sample, rows) == hipSuccess && dev_alloc(&c->canvas, rows) == hipSuccess &&
+            dev_alloc(&c->seeds, max_batch) == hipSuccess &&
+            dev_alloc(&c->temperature, max_batch) == hipSuccess &&
+            dev_alloc(&c->active, max_batch) == hipSuccess && dev_alloc(&c->stop, max_batch) == hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&c->stop_host), max_batch) == hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&c->active_host), max_batch) == hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&c->temp_host), sizeof(float) * max_batch) == hipSuccess;
+  if (!ok) {
+    free_ctx(c);
+    (void)hipGetLastError();
+    return set_err(nullptr, DG_ERR_OUT_OF_MEMORY, "could not allocate scratch for max_batch = %d", max_batch);
+  }
+  if (hipMemset(c->tickets, 0, rows * sizeof(uint32_t)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    free_ctx(c);
+    return set_err(nullptr, DG_ERR_DEVICE, "could not clear the ticket scratch");
+  }
+  *out = c;
+  return DG_OK;
+}
+
+dg_status dg_destroy(dg_ctx* ctx) {
+  if (!ctx) return DG_OK;
+  DeviceGuard guard(ctx->device);
+  (void)hipDeviceSynchronize();
+  free_ctx(ctx);
+  return DG_OK;
+}
+
+dg_status dg_set_stats_split(dg_ctx* ctx, int32_t nsplit) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  if (nsplit < 0 || nsplit > ctx->nsplit_max)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "nsplit = %d is outside 0..%d", nsplit, ctx->nsplit_max);
+  ctx->nsplit_override = nsplit;
+  return DG_OK;
+}
+
+dg_status dg_canvas_init(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t* canvas, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!canvas) return set_err(ctx, DG_ERR_INVALID_ARG, "canvas is NULL");
+  DeviceGuard guard(ctx->device);
+  DG_CHECK_HIP(ctx, dg::launch_canvas_init(seeds, B, ctx->p.canvas_len, ctx->p.vocab, canvas,
+                                           static_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_canvas_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                          int64_t row_stride, const float* temperature, int32_t step,
+                          const uint64_t* seeds, const uint8_t* active, float* entropy,
+                          int32_t* argmax, int32_t* sample, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  if ((st = check_logits(ctx, logits, dtype, row_stride)) != DG_OK) return st;
+  if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
+  if (step < 0) return set_err(ctx, DG_ERR_INVALID_ARG, "step = %d is negative", step);
+  if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!entropy) return set_err(ctx, DG_ERR_INVALID_ARG, "entropy is NULL");
+  if (!argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "argmax is NULL");
+  if (!sample) return set_err(ctx, DG_ERR_INVALID_ARG, "sample is NULL");
+  DeviceGuard guard(ctx->device);
+  return enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, seeds, active, entropy,
+                       argmax, sample, static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_accept_renoise(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
+                            const int32_t* sample, int32_t step, const uint64_t* seeds,
+                            const int32_t* prev_argmax, const uint8_t* active,
+                            const dg_step_out* out, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  if (!entropy) return set_err(ctx, DG_ERR_INVALID_ARG, "entropy is NULL");
+  if (!argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "argmax is NULL");
+  if (!sample) return set_err(ctx, DG_ERR_INVALID_ARG, "sample is NULL");
+  if (step < 0) return set_err(ctx, DG_ERR_INVALID_ARG, "step = %d is negative", step);
+  if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
+  if (!out->canvas_out) return set_err(ctx, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
+  DeviceGuard guard(ctx->device);
+  return enqueue_accept(ctx, B, entropy, argmax, sample, step, seeds, prev_argmax, active, out,
+                        true, static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_sampler_step(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                          int64_t row_stride, const float* temperature, int32_t step,
+                          const uint64_t* seeds, const int32_t* prev_argmax,
+                          const uint8_t* active, const dg_step_out* out, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  if ((st = check_logits(ctx, logits, dtype, row_stride)) != DG_OK) return st;
+  if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
+  if (step < 0) return set_err(ctx, DG_ERR_INVALID_ARG, "step = %d is negative", step);
+  if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
+  if (!out->canvas_out) return set_err(ctx, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
+  DeviceGuard guard(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // statistics go straight to the caller's buffers when requested
+  float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;
+  int32_t* am = out->argmax_out ? out->argmax_out : ctx->argmax[0];
+  int32_t* smp = out->sample_out ? out->sample_out : ctx->sample;
+  st = enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, seeds, active, ent, am, smp, s);
+  if (st != DG_OK) return st;
+  return enqueue_accept(ctx, B, ent, am, smp, step, seeds, prev_argmax, active, out, false, s);
+}
+
+dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
+                        void* user, dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
+                        int32_t* steps_used, uint8_t* stopped, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!denoise) return set_err(ctx, DG_ERR_INVALID_ARG, "denoise is NULL");
+  const int64_t V = ctx->p.vocab;
+  if ((st = check_logits(ctx, logits_scratch, dtype, V)) != DG_OK) {
+    if (st == DG_ERR_UNSUPPORTED && std::strstr(ctx->err.c_str(), "row_stride"))
+      return set_err(ctx, DG_ERR_UNSUPPORTED,
+                     "vocab = %lld must be a multiple of %d for dg_run_canvas with this dtype",
+                     static_cast<long long>(V), dtype == DG_DTYPE_BF16 ? 8 : 4);
+    if (std::strstr(ctx->err.c_str(), "logits"))
+      return set_err(ctx, st, "logits_scratch: %s", ctx->err.c_str());
+    return st;
+  }
+  if (!final_argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "final_argmax is NULL");
+  if (!steps_used) return set_err(ctx, DG_ERR_INVALID_ARG, "steps_used is NULL");
+  if (!stopped) return set_err(ctx, DG_ERR_INVALID_ARG, "stopped is NULL");
+  DeviceGuard guard(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t L = ctx->p.canvas_len;
+
+  for (int32_t c = 0; c < B; ++c) {
+    steps_used[c] = 0;
+    stopped[c] = 0;
+    ctx->active_host[c] = 1;
+  }
+  DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->seeds, seeds, sizeof(uint64_t) * B, hipMemcpyHostToDevice, s));
+  DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->active, ctx->active_host, B, hipMemcpyHostToDevice, s));
+  DG_CHECK_HIP(ctx, dg::launch_canvas_init(ctx->seeds, B, L, ctx->p.vocab, ctx->canvas, s));
+
+  int32_t remaining = B;
+  for (int32_t step = 0; step < ctx->p.max_steps && remaining > 0; ++step) {
+    if (denoise(user, step, ctx->canvas, ctx->active, logits_scratch, stream) != 0)
+      return set_err(ctx, DG_ERR_CALLBACK, "denoise callback failed at step %d", step);
+    float t = 0.0f;
+    (void)dg_temperature(&ctx->p, step, &t);
+    for (int32_t c = 0; c < B; ++c) ctx->temp_host[c] = t;
+    DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->temperature, ctx->temp_host, sizeof(float) * B,
+                                     hipMemcpyHostToDevice, s));
+    int32_t* am_cur = ctx->argmax[step & 1];
+    const int32_t* am_prev = step > 0 ? ctx->argmax[(step - 1) & 1] : nullptr;
+    st = enqueue_stats(ctx, B, logits_scratch, dtype, V, ctx->temperature, step, ctx->seeds,
+                       ctx->active, ctx->entropy, am_cur, ctx->sample, s);
+    if (st != DG_OK) return st;
+    dg_step_out o{};
+    o.canvas_out = ctx->canvas;           // the denoiser has consumed the old canvas
+    o.argmax_out = final_argmax;          // holds each canvas's latest argmax canvas
+    o.stop_out = ctx->stop;
+    st = enqueue_accept(ctx, B, ctx->entropy, am_cur, ctx->sample, step, ctx->seeds, am_prev,
+                        ctx->active, &o, true, s);
+    if (st != DG_OK) return st;
+    DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->stop_host, ctx->stop, B, hipMemcpyDeviceToHost, s));
+    DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
+    bool changed = false;
+    for (int32_t c = 0; c < B; ++c) {
+      if (!ctx->active_host[c]) continue;
+      steps_used[c] = step + 1;
+      if (ctx->stop_host[c]) {
+        stopped[c] = 1;
+        ctx->active_host[c] = 0;
+        --remaining;
+        changed = true;
+      }
+    }
+    if (changed && remaining > 0)
+      DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->active, ctx->active_host, B, hipMemcpyHostToDevice, s));
+  }
+  return DG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Per-(row, split) partial result of the statistics pass (32 bytes).
+//   s, w   sums of 2^t and t*2^t over the split's ids, t = z*c - ref with
+//          c = log2(e)/T and ref an fp32 value at most the split's max z*c
+//          (ref = -inf when the split saw no finite logit)
+//   ref    that reference
+//   m      largest raw logit; search = index of the 8192-id unit holding its
+//          first occurrence
+//   best   largest block score (log2 units) and bestj its block
+struct RowPartial {
+  double s;
+  double w;
+  float ref;
+  float m;
+  int32_t search;
+  float best;
+  int32_t bestj;
+  int32_t pad;
+};
+
+struct StatsArgs {
+  const void* logits;
+  int64_t row_stride;      // elements
+  int32_t vocab;
+  int32_t canvas_len;
+  int32_t rows;            // B * L
+  int32_t nsplit;          // workgroups per row
+  const float* temperature;
+  const uint64_t* seeds;
+  int32_t step;
+  const uint8_t* active;   // may be null
+  float* entropy;
+  int32_t* argmax;
+  int32_t* sample;
+  RowPartial* partials;    // [rows * nsplit] when nsplit > 1
+  uint32_t* tickets;       // [rows], zero between launches
+};
+
+struct AcceptArgs {
+  const float* entropy;
+  const int32_t* argmax;
+  const int32_t* sample;
+  const uint64_t* seeds;
+  const int32_t* prev_argmax;  // may be null
+  const uint8_t* active;       // may be null
+  int32_t step;
+  int32_t canvas_len;
+  int32_t vocab;
+  float bound;
+  float stop_mean_entropy;
+  int32_t* canvas_out;
+  int32_t* argmax_out;         // may be null: copy of argmax
+  int32_t* sample_out;         // may be null: copy of sample
+  float* entropy_out;          // may be null: copy of entropy
+  uint8_t* accept_out;         // may be null
+  int32_t* n_accept_out;       // may be null
+  float* mean_entropy_out;     // may be null
+  uint8_t* stop_out;           // may be null
+};
+
+constexpr int kStatsThreads = 256;
+constexpr int kAcceptThreads = 256;
+
+// Chooses the number of workgroups per row for `rows` rows of `vocab` ids.
+int32_t choose_nsplit(int32_t rows, int32_t vocab);
+
+hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_accept_renoise(const AcceptArgs& a, int32_t batch, hipStream_t stream);
+hipError_t launch_canvas_init(const uint64_t* seeds, int32_t batch, int32_t canvas_len,
+                              int32_t vocab, int32_t* canvas, hipStream_t stream);
+
+}  // namespace dg

@@ -131,6 +131,12 @@ dg_status dg_get_params(const dg_ctx* ctx, dg_params* out);
  * Host only. */
 dg_status dg_temperature(const dg_params* p, int32_t step, float* out);
 
+/* Sets how many workgroups share one row in the statistics pass (1..8), or 0
+ * for the automatic choice (the default). Meant for tuning and tests: the
+ * argmax does not depend on it, and the other outputs only through
+ * last-bit rounding of the block scores and entropies. */
+dg_status dg_set_stats_split(dg_ctx* ctx, int32_t nsplit);
+
 /* Initial canvas ("DiffusionGemma Lab", §2 item 1: uniform random vocabulary
  * tokens, not [MASK]). canvas[c*L + l] = floor(w0 * V / 2^32), w0 = word 0 of
  * Philox(seed_c; (0, l, 0, INIT)).

@@ -111,13 +111,16 @@ def block_logsumexp(x):
     return lse.reshape(rows, n_sg * SLOTS)
 
 
-def sample_two_level(z, temp, seed, positions, step):
+def sample_two_level_detail(z, temp, seed, positions, step):
     """Multinomial sample of softmax(z/T) per row by the two-level Gumbel-max
     protocol: block j* = argmax_j (LSE_j + G_j), then the id inside j* with the
     largest z_v/T + G_v. Ties go to the lowest block, then the lowest id. Exact
     in distribution by the Gumbel-max property applied twice.
 
-    z: [rows, V]; positions: [rows] canvas positions (counter word 1)."""
+    z: [rows, V]; positions: [rows] canvas positions (counter word 1).
+    Returns (samples, block_best, block_gap, elem_best, elem_gap): the winning
+    scores of both levels and their margins over the runner-up (inf when there
+    is none), used to recognise near-ties between implementations."""
     x = np.asarray(z, dtype=np.float64) / np.float64(temp)
     rows, vocab = x.shape
     k0, k1 = seed_key(seed)
@@ -129,13 +132,28 @@ def sample_two_level(z, temp, seed, positions, step):
     block_score = lse + gumbel(w0)
     j_star = np.argmax(block_score, axis=1)
     out = np.empty(rows, dtype=np.int64)
+    detail = np.full((4, rows), np.inf)
     for r in range(rows):
         v = block_members(j_star[r], vocab)
         words = philox4x32_10(v >> 2, positions[r], step, TAG_ELEM, k0, k1)
         w = np.choose(v & 3, words)
         score = x[r, v] + gumbel(w)
         out[r] = v[np.argmax(score)]
-    return out
+        top_b = np.sort(block_score[r])[::-1]
+        top_e = np.sort(score)[::-1]
+        detail[0, r] = top_b[0]
+        detail[2, r] = top_e[0]
+        if len(top_b) > 1:
+            detail[1, r] = top_b[0] - top_b[1]
+        if len(top_e) > 1:
+            detail[3, r] = top_e[0] - top_e[1]
+    return (out,) + tuple(detail)
+
+
+def sample_two_level(z, temp, seed, positions, step):
+    """Multinomial sample per row by the two-level Gumbel-max protocol (see
+    sample_two_level_detail)."""
+    return sample_two_level_detail(z, temp, seed, positions, step)[0]
 
 
 def sample_per_element(z, temp, seed, positions, step):

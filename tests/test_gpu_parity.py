@@ -1,0 +1,245 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from canvas_sampler_amd import binding as B
+from canvas_sampler_amd import synth
+from oracle import philox as OP
+from oracle import sampler as O
+
+from gpu_util import (accept_near_tie, compare_stats, gpu, host_values, require_gpu,
+                      seeds_tensor)
+
+pytestmark = gpu
+
+
+def _ctx(L, V, max_batch=1, **kw):
+    require_gpu()
+    return B.Context(B.params_default(canvas_len=L, vocab=V, **kw), max_batch=max_batch)
+
+
+def _stats(ctx, logits, temps, seeds, step, batch, nsplit=None):
+    rows = batch * ctx.L
+    h = torch.full((rows,), -1.0, device="cuda")
+    am = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    smp = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    if nsplit is not None:
+        ctx.set_stats_split(nsplit)
+    ctx.dg_canvas_stats(logits, torch.tensor(temps, dtype=torch.float32, device="cuda"), step,
+                        seeds_tensor(seeds), h, am, smp, batch=batch)
+    torch.cuda.synchronize()
+    return h.cpu().numpy(), am.cpu().numpy(), smp.cpu().numpy()
+
+
+def _padded(z, stride):
+    """Copy of z [rows, V] inside a [rows, stride] buffer (padding = garbage 7.0)."""
+    buf = torch.full((z.shape[0], stride), 7.0, dtype=z.dtype, device=z.device)
+    buf[:, :z.shape[1]] = z
+    return buf
+
+
+def test_c1_stats_match_oracle():
+    # single canvas, V = 4096, fp32, margin logits (m ~ U[0,12]), T = 0.8, seed 0
+    L, V = 256, 4096
+    ctx = _ctx(L, V)
+    z = synth.margin_logits(1001, L, V, m_max=12.0, dtype=torch.float32, device="cuda")
+    h, am, smp = _stats(ctx, z, [0.8], [0], 0, 1)
+    rep = compare_stats(host_values(z), np.float32(0.8), 0, np.arange(L), 0, h, am, smp)
+    print("C1 stats", rep)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("V", [2, 7, 100, 1000, 4100, 33000, 70001])
+def test_ragged_vocab(dtype, V):
+    L = 40
+    ctx = _ctx(L, V)
+    per16 = 8 if dtype == torch.bfloat16 else 4
+    stride = -(-V // per16) * per16
+    z = synth.margin_logits(V, L, V, m_max=5.0, dtype=dtype, device="cuda")
+    zp = _padded(z, stride)
+    h, am, smp = _stats(ctx, zp, [0.7], [V * 31 + 5], 3, 1)
+    compare_stats(host_values(z), np.float32(0.7), V * 31 + 5, np.arange(L), 3, h, am, smp)
+
+
+def test_row_stride_padding_is_ignored():
+    L, V = 32, 4096
+    ctx = _ctx(L, V)
+    z = synth.margin_logits(7, L, V, dtype=torch.bfloat16, device="cuda")
+    zp = _padded(z, V + 64)
+    zp[:, V:] = 1e4   # huge values in the padding must not be read
+    h, am, smp = _stats(ctx, zp, [0.8], [1], 0, 1)
+    compare_stats(host_values(z), np.float32(0.8), 1, np.arange(L), 0, h, am, smp)
+
+
+def test_neg_inf_and_degenerate_rows():
+    L, V = 8, 70000
+    ctx = _ctx(L, V)
+    z = torch.randn(L, V, device="cuda")
+    z[0, :] = float("-inf")
+    z[0, 12345] = 0.5                       # single finite logit
+    z[1, :40000] = float("-inf")            # whole supergroup of -inf
+    z[2, ::3] = float("-inf")               # scattered -inf
+    z[3, :] = 1.0                           # constant row: H = ln V, argmax 0
+    z[4, :] = -3.0e4
+    z[4, 69999] = 0.0                       # finite one-hot at the last id
+    z[5, 100:200] = 50.0                    # 100-way tie at the max
+    h, am, smp = _stats(ctx, z, [0.8], [99], 2, 1)
+    zh = host_values(z)
+    compare_stats(zh, np.float32(0.8), 99, np.arange(L), 2, h, am, smp)
+    assert smp[0] == 12345 and h[0] == 0.0
+    assert am[3] == 0 and abs(h[3] - math.log(V)) < 1e-4
+    assert am[4] == 69999 and smp[4] == 69999 and h[4] == 0.0
+    assert am[5] == 100 and 100 <= smp[5] < 200 and abs(h[5] - math.log(100)) < 1e-4
+
+
+def test_batch_of_canvases_with_own_temperatures_and_seeds():
+    L, V, Bn = 64, 40000, 3
+    ctx = _ctx(L, V, max_batch=4)
+    zs = [synth.margin_logits(50 + c, L, V, m_max=3.0, dtype=torch.bfloat16, device="cuda")
+          for c in range(Bn)]
+    z = torch.cat(zs)
+    temps = [0.8, 0.4, 2.0]
+    seeds = [5, 2**63 + 12345, 2**64 - 1]
+    h, am, smp = _stats(ctx, z, temps, seeds, 7, Bn)
+    for c in range(Bn):
+        sl = slice(c * L, (c + 1) * L)
+        compare_stats(host_values(zs[c]), np.float32(temps[c]), seeds[c], np.arange(L), 7,
+                      h[sl], am[sl], smp[sl])
+
+
+def test_full_vocab_sampled_rows_every_split():
+    # the launch shape of the single-canvas bf16 benchmark (B=1, V=262144), and
+    # every split count; rows sampled for the oracle
+    L, V = 256, 262144
+    ctx = _ctx(L, V)
+    z = synth.sharpening_logits(1002, 3, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda")
+    rows = np.array([0, 1, 17, 63, 64, 100, 128, 200, 254, 255])
+    zh = host_values(z[torch.as_tensor(rows, device="cuda")])
+    base = None
+    for nsplit in (0, 1, 2, 4, 8):
+        h, am, smp = _stats(ctx, z, [0.7], [0], 3, 1, nsplit=nsplit)
+        compare_stats(zh, np.float32(0.7), 0, rows, 3, h[rows], am[rows], smp[rows])
+        if base is None:
+            base = (h, am, smp)
+        else:
+            assert np.array_equal(am, base[1])
+            assert np.max(np.abs(h - base[0])) < 1e-5
+            assert np.mean(smp == base[2]) > 0.99
+
+
+def test_init_canvas_matches_oracle():
+    L, V = 256, 262144
+    ctx = _ctx(L, V, max_batch=3)
+    seeds = [0, 1, 2**64 - 2]
+    canvas = torch.full((3, L), -1, dtype=torch.int32, device="cuda")
+    ctx.dg_canvas_init(seeds_tensor(seeds), canvas)
+    torch.cuda.synchronize()
+    for c, s in enumerate(seeds):
+        assert np.array_equal(canvas[c].cpu().numpy(), O.init_canvas(s, L, V))
+
+
+def _accept_case(rng, L, kind):
+    if kind == "random":
+        return rng.exponential(rng.choice([0.005, 0.03, 0.3]), size=L).astype(np.float32)
+    if kind == "ties":
+        h = np.round(rng.exponential(0.02, size=L), 3).astype(np.float32)
+        h[rng.integers(0, L, size=L // 3)] = 0.0
+        return h
+    if kind == "uniform":
+        return np.full(L, np.float32(math.log(262144)))
+    if kind == "zeros":
+        return np.zeros(L, dtype=np.float32)
+    if kind == "equal_small":
+        return np.full(L, np.float32(0.03125))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("L", [256, 100, 1])
+def test_accept_renoise_stop_exact_from_given_entropies(L):
+    V = 262144
+    kinds = ["random", "ties", "uniform", "zeros", "equal_small", "random"]
+    Bn = len(kinds)
+    ctx = _ctx(L, V, max_batch=Bn)
+    rng = np.random.default_rng(L)
+    H = np.stack([_accept_case(rng, L, k) for k in kinds])
+    am = rng.integers(0, V, size=(Bn, L)).astype(np.int32)
+    prev = am.copy()
+    prev[1, 0] ^= 1                          # canvas 1 not stable
+    smp = rng.integers(0, V, size=(Bn, L)).astype(np.int32)
+    seeds = [11, 12, 13, 14, 15, 2**63]
+    step = 5
+    dev = lambda a, dt: torch.as_tensor(a, dtype=dt, device="cuda")
+    canvas = torch.full((Bn, L), -1, dtype=torch.int32, device="cuda")
+    acc = torch.full((Bn, L), 7, dtype=torch.uint8, device="cuda")
+    nacc = torch.full((Bn,), -1, dtype=torch.int32, device="cuda")
+    meanh = torch.full((Bn,), -1.0, device="cuda")
+    stop = torch.full((Bn,), 7, dtype=torch.uint8, device="cuda")
+    out = ctx.step_out(canvas, accept_out=acc, n_accept_out=nacc, mean_entropy_out=meanh,
+                       stop_out=stop)
+    ctx.dg_accept_renoise(dev(H.ravel(), torch.float32), dev(am.ravel(), torch.int32),
+                          dev(smp.ravel(), torch.int32), step, seeds_tensor(seeds), out,
+                          prev_argmax=dev(prev.ravel(), torch.int32))
+    torch.cuda.synchronize()
+    for c in range(Bn):
+        mask, k = O.accept(H[c].astype(np.float64), np.float32(0.1))
+        ren = O.uniform_tokens(seeds[c], L, step, V, OP.TAG_RENOISE)
+        want = np.where(mask, smp[c], ren)
+        assert nacc[c].item() == k
+        assert np.array_equal(acc[c].cpu().numpy().astype(bool), mask)
+        assert np.array_equal(canvas[c].cpu().numpy(), want)
+        mh = float(np.mean(H[c].astype(np.float64)))
+        assert abs(meanh[c].item() - mh) < 1e-6 * max(1.0, mh)
+        want_stop = O.stop_test(am[c], prev[c], mh, np.float32(0.005))
+        assert bool(stop[c].item()) == want_stop
+    assert stop[3].item() == 1 and stop[1].item() == 0   # zeros canvas stops, canvas 1 changed
+
+
+def test_inactive_canvases_are_untouched():
+    L, V = 64, 4096
+    ctx = _ctx(L, V, max_batch=2)
+    z = synth.margin_logits(3, 2 * L, V, device="cuda")
+    temps = torch.tensor([0.8, 0.8], device="cuda")
+    active = torch.tensor([0, 1], dtype=torch.uint8, device="cuda")
+    canvas = torch.full((2, L), -5, dtype=torch.int32, device="cuda")
+    am = torch.full((2 * L,), -5, dtype=torch.int32, device="cuda")
+    stop = torch.full((2,), 9, dtype=torch.uint8, device="cuda")
+    out = ctx.step_out(canvas, argmax_out=am, stop_out=stop)
+    ctx.dg_sampler_step(z, temps, 0, seeds_tensor([1, 2]), out, active=active)
+    torch.cuda.synchronize()
+    assert torch.all(canvas[0] == -5) and torch.all(am[:L] == -5) and stop[0].item() == 9
+    assert torch.all(canvas[1] >= 0) and torch.all(am[L:] >= 0) and stop[1].item() == 0
+
+
+def test_sampler_step_full_outputs_match_oracle_c1():
+    L, V = 256, 4096
+    ctx = _ctx(L, V)
+    z = synth.margin_logits(1001, L, V, m_max=12.0, dtype=torch.float32, device="cuda")
+    t = torch.tensor([0.8], device="cuda")
+    bufs = dict(canvas_out=torch.empty(L, dtype=torch.int32, device="cuda"),
+                argmax_out=torch.empty(L, dtype=torch.int32, device="cuda"),
+                sample_out=torch.empty(L, dtype=torch.int32, device="cuda"),
+                accept_out=torch.empty(L, dtype=torch.uint8, device="cuda"),
+                entropy_out=torch.empty(L, device="cuda"),
+                n_accept_out=torch.empty(1, dtype=torch.int32, device="cuda"),
+                mean_entropy_out=torch.empty(1, device="cuda"),
+                stop_out=torch.empty(1, dtype=torch.uint8, device="cuda"))
+    ctx.dg_sampler_step(z, t, 0, seeds_tensor([0]), ctx.step_out(**bufs))
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in bufs.items()}
+    ref = O.step(host_values(z), np.float32(0.8), 0, 0)
+    compare_stats(host_values(z), np.float32(0.8), 0, np.arange(L), 0, g["entropy_out"],
+                  g["argmax_out"], g["sample_out"])
+    dh = float(np.max(np.abs(g["entropy_out"] - ref["entropy"])))
+    if not accept_near_tie(ref["entropy"], float(np.float32(0.1)), dh):
+        assert np.array_equal(g["accept_out"].astype(bool), ref["accept"])
+        assert g["n_accept_out"][0] == ref["n_accept"]
+    # decisions from the GPU's own statistics are exact
+    mask, k = O.accept(g["entropy_out"].astype(np.float64), np.float32(0.1))
+    assert np.array_equal(g["accept_out"].astype(bool), mask) and g["n_accept_out"][0] == k
+    ren = O.uniform_tokens(0, L, 0, V, OP.TAG_RENOISE)
+    assert np.array_equal(g["canvas_out"], np.where(mask, g["sample_out"], ren))
+    assert g["stop_out"][0] == 0
+    print("C1 step: n_accept", k, "max dH", dh)

@@ -1,0 +1,86 @@
+"""Host-side tests of the C-ABI library (no GPU needed): it loads, exports
+every symbol include/dg_canvas.h declares, validates parameters with messages
+that name the offending field, and computes the temperature schedule exactly
+as the oracle does."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from canvas_sampler_amd import binding as B
+from oracle import sampler as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "dg_canvas.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", text)) - {"dg_denoise_fn"})
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 13
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dg_\w+)", out))
+    assert set(names) <= exported
+    assert sorted(B.EXPORTS) == names
+
+
+def test_version_and_defaults():
+    assert "gfx950" in B.version()
+    p = B.params_default()
+    assert (p.canvas_len, p.vocab, p.temp_steps, p.max_steps) == (256, 262144, 48, 48)
+    assert p.entropy_bound == np.float32(0.1) and p.stop_mean_entropy == np.float32(0.005)
+    assert p.temp_start == np.float32(0.8) and p.temp_end == np.float32(0.4)
+    B.params_check(p)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("canvas_len", 0), ("canvas_len", 257), ("vocab", 1), ("entropy_bound", -0.01),
+    ("entropy_bound", float("nan")), ("temp_start", 0.0), ("temp_end", -1.0),
+    ("temp_start", float("inf")), ("temp_steps", 0), ("max_steps", 0),
+    ("stop_mean_entropy", 0.0)])
+def test_invalid_parameters_name_the_field(field, value):
+    # "DiffusionGemma Lab", side finding: an upstream validator's error path
+    # referred to the wrong attribute; here every message names the field.
+    p = B.params_default(**{field: value})
+    with pytest.raises(B.DgError) as ei:
+        B.params_check(p)
+    assert ei.value.status == B.DG_ERR_INVALID_ARG
+    assert f"params.{field}" in ei.value.message
+
+
+@pytest.mark.parametrize("steps", [1, 2, 16, 48])
+def test_temperature_schedule_matches_oracle(steps):
+    p = B.params_default(temp_steps=steps)
+    for s in range(0, 60):
+        got = np.float32(B.dg_temperature(p, s))
+        assert got == O.temperature(s, 0.8, 0.4, steps), (s, got)
+    with pytest.raises(B.DgError):
+        B.dg_temperature(p, -1)
+
+
+def test_create_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    h = ctypes.c_void_p(123)
+    p = B.params_default()
+    st = B.lib().dg_create(ctypes.byref(h), 0, 1, ctypes.byref(p))
+    assert st == B.DG_ERR_DEVICE and h.value is None
+    assert "device" in B.lib().dg_last_error(None).decode()
+
+
+def test_null_context_is_rejected():
+    st = B.lib().dg_canvas_init(None, 1, None, None, None)
+    assert st == B.DG_ERR_INVALID_ARG
+    assert "ctx" in B.lib().dg_last_error(None).decode()
