@@ -2,9 +2,10 @@
 // sampler step and the initial canvas.
 //
 // One 256-thread workgroup per canvas, one thread per position:
-//   - sort the L keys (entropy bits << 32 | position) ascending in LDS with a
-//     bitonic network (entropies are >= +0, so their fp32 bit patterns order
-//     like the values; equal entropies fall back to position order);
+//   - sort the L keys (entropy bits << 32 | position) ascending with a
+//     bitonic network, in-wave steps by lane shuffles and the cross-wave steps
+//     through LDS (entropies are >= +0, so their fp32 bit patterns order like
+//     the values; equal entropies fall back to position order);
 //   - inclusive fp64 scan C_i of the sorted entropies; position i of the
 //     order is acceptable while C_i - H_i <= b (H_i is the running maximum of
 //     an ascending order), and the accepted set is the longest acceptable
@@ -44,29 +45,35 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_renoise_kernel(AcceptAr
     am = a.argmax[base + tid];
     smp = a.sample[base + tid];
   }
-  s_key[tid] = valid ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(tid))
-                     : ~0ull;
-  __syncthreads();
-
-  // bitonic sort of 256 keys, ascending
+  // bitonic sort of 256 keys, ascending. Compare-exchange partners closer
+  // than a wave are reached with lane shuffles; only the three steps whose
+  // partner lies in another wave go through LDS.
+  uint64_t key = valid ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(tid))
+                       : ~0ull;
+#pragma unroll
   for (int k = 2; k <= kAcceptThreads; k <<= 1) {
+#pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const int partner = tid ^ j;
-      uint64_t mine = s_key[tid];
-      const uint64_t other = s_key[partner];
+      uint64_t other;
+      if (j >= kWave) {
+        s_key[tid] = key;
+        __syncthreads();
+        other = s_key[tid ^ j];
+        __syncthreads();
+      } else {
+        const uint32_t lo32 = __shfl_xor(static_cast<uint32_t>(key), j, kWave);
+        const uint32_t hi32 = __shfl_xor(static_cast<uint32_t>(key >> 32), j, kWave);
+        other = (static_cast<uint64_t>(hi32) << 32) | lo32;
+      }
       const bool ascending = (tid & k) == 0;
-      const bool lower = tid < partner;
-      const uint64_t lo = mine < other ? mine : other;
-      const uint64_t hi = mine < other ? other : mine;
-      mine = (lower == ascending) ? lo : hi;
-      __syncthreads();
-      s_key[tid] = mine;
-      __syncthreads();
+      const bool lower = (tid & j) == 0;
+      const uint64_t lo = key < other ? key : other;
+      const uint64_t hi = key < other ? other : key;
+      key = (lower == ascending) ? lo : hi;
     }
   }
 
   // inclusive fp64 scan of sorted entropies (wave scan + wave offsets)
-  const uint64_t key = s_key[tid];
   const double hs = valid ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(key >> 32))) : 0.0;
   double incl = hs;
 #pragma unroll

@@ -41,32 +41,39 @@ constexpr float kNegInf = -__builtin_inff();
 // a factor 256) before the sums are rescaled: 2^t <= 256 cannot overflow.
 constexpr float kRefSlack = 8.0f;
 
+// Offset used for prefetches past a wave's last batch: beyond every row
+// resource (rows hold fewer than 2^31 - 2^16 bytes) even with the largest
+// immediate offset added, so those loads return zero and read nothing.
+constexpr uint32_t kPastEnd = 0x7FFF0000u;
+
+// Cache policy of the streaming loads: non-temporal (each logit is read once).
+constexpr int kStreamPolicy = 2;
+
 template <bool kBf16>
 struct Geometry {
   static constexpr int kLoadsPerStripe = kBf16 ? 1 : 2;   // 16-byte loads per lane
   static constexpr int kElemBytes = kBf16 ? 2 : 4;
 };
 
-// Loads NB stripes of the lane's slot starting at vocabulary id `id0` (the
-// lane's first id in the first stripe of the batch). Chunks at or past V are
-// filled with -inf.
+// Loads NB stripes of the lane's slot with raw buffer loads on the row's
+// resource (base = row start, size = V elements): `byte0` is the byte offset of
+// the lane's chunk in the batch's first stripe. The loads are unconditional;
+// bytes past V read as zero (hardware range check) and are masked by the
+// caller, so no load sits behind a branch and the next batch stays in flight
+// while the current one is reduced.
 template <bool kBf16, int NB>
 __device__ __forceinline__ void load_batch(uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
-                                           const char* __restrict__ row, int64_t id0,
-                                           int32_t vocab) {
+                                           __amdgpu_buffer_rsrc_t rsrc, uint32_t byte0) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
-  constexpr uint32_t kNegInfBits = kBf16 ? 0xFF80FF80u : 0xFF800000u;
+  constexpr int kEB = Geometry<kBf16>::kElemBytes;
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
 #pragma unroll
     for (int h = 0; h < LPS; ++h) {
-      const int64_t id = id0 + static_cast<int64_t>(s) * kStripeIds + h * 4;
-      if (id < vocab) {
-        buf[s * LPS + h] =
-            *reinterpret_cast<const uint4*>(row + id * Geometry<kBf16>::kElemBytes);
-      } else {
-        buf[s * LPS + h] = make_uint4(kNegInfBits, kNegInfBits, kNegInfBits, kNegInfBits);
-      }
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc, static_cast<int>(byte0 + static_cast<uint32_t>((s * kStripeIds + h * 4) * kEB)), 0,
+          kStreamPolicy);
+      buf[s * LPS + h] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -146,11 +153,11 @@ __device__ __forceinline__ void batch_sums(const float (&z)[N], float c, float r
 template <bool kBf16, int NB>
 __device__ __forceinline__ void process_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
                                               int64_t id0, int64_t batch_first_id, int32_t vocab,
-                                              bool ragged, float c, LaneState& st) {
+                                              float c, LaneState& st) {
   float z[NB * kSlotIds];
   unpack_batch<kBf16, NB>(buf, z);
-  if (ragged) {
-    // ids past V inside the last chunk: mask to -inf
+  if (batch_first_id + NB * kStripeIds > vocab) {
+    // the batch holding id V-1: ids past V (read as zero) become -inf
 #pragma unroll
     for (int s = 0; s < NB; ++s)
 #pragma unroll
@@ -235,23 +242,17 @@ __device__ __forceinline__ RowPartial wave_partial(const LaneState& st) {
   return p;
 }
 
-template <bool kBf16>
-__device__ __forceinline__ float load_logit(const char* __restrict__ row, int64_t id) {
-  if constexpr (kBf16) {
-    const uint16_t b = *reinterpret_cast<const uint16_t*>(row + id * 2);
-    return __uint_as_float(static_cast<uint32_t>(b) << 16);
-  } else {
-    return *reinterpret_cast<const float*>(row + id * 4);
-  }
-}
-
 // Finishes a row from its merged partial: entropy, exact argmax (re-search of
-// one 8192-id unit), and the in-block resample of block j*. All threads of the
-// workgroup take part; thread 0 writes the results.
+// one 8192-id unit), and the in-block resample of block j*. Every thread of
+// the workgroup takes part with unconditional buffer loads (ids past V read
+// as zero and are excluded), so each phase costs one memory latency; thread 0
+// writes the results.
 template <bool kBf16>
-__device__ void finish_row(const StatsArgs& a, const char* __restrict__ row, int32_t r,
+__device__ void finish_row(const StatsArgs& a, __amdgpu_buffer_rsrc_t rsrc, int32_t r,
                            int32_t pos, float temp, uint32_t k0, uint32_t k1,
                            const RowPartial& p) {
+  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
+  constexpr int kChunksPerThread = kSearchIds / (kStatsThreads * kSlotIds);
   __shared__ int32_t s_min[kWaves];
   __shared__ float s_score[kWaves];
   __shared__ int32_t s_id[kWaves];
@@ -264,42 +265,57 @@ __device__ void finish_row(const StatsArgs& a, const char* __restrict__ row, int
   int32_t cand = 0x7FFFFFFF;
   {
     const int64_t base = static_cast<int64_t>(p.search) * kSearchIds;
+    float z[kChunksPerThread][kSlotIds];
 #pragma unroll
-    for (int i = 0; i < kSearchIds / (kStatsThreads * kSlotIds); ++i) {
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int64_t id0 = base + static_cast<int64_t>(i * kStatsThreads + tid) * kSlotIds;
+      const uint32_t off = id0 < vocab ? static_cast<uint32_t>(id0) * kEB : kPastEnd;
+      if constexpr (kBf16) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off), 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          z[i][2 * q] = __uint_as_float(v[q] << 16);
+          z[i][2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off + 16 * h), 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) z[i][4 * h + q] = __uint_as_float(v[q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = kChunksPerThread - 1; i >= 0; --i) {
       const int64_t id0 = base + static_cast<int64_t>(i * kStatsThreads + tid) * kSlotIds;
 #pragma unroll
-      for (int e = 0; e < kSlotIds; ++e) {
-        const int64_t id = id0 + e;
-        if (id < vocab && load_logit<kBf16>(row, id) == p.m && id < cand)
-          cand = static_cast<int32_t>(id);
-      }
+      for (int e = kSlotIds - 1; e >= 0; --e)
+        if (id0 + e < vocab && z[i][e] == p.m) cand = static_cast<int32_t>(id0 + e);
     }
   }
   cand = wave_min_int(cand);
 
-  // in-block resample: 512 members of block j*, two per thread
+  // in-block resample: the 512 members of block j*, one per thread
   float best = kNegInf;
   int32_t best_id = 0x7FFFFFFF;
   {
     const int32_t j = p.bestj;
-    const int64_t sg = j >> 6;
-    const int slot = j & 63;
-    const int stripe = tid >> 2;
-    const int pair = (tid & 3) * 2;
-    const int64_t v0 = sg * kSgIds + static_cast<int64_t>(stripe) * kStripeIds + slot * kSlotIds + pair;
-    const Words4 rw = philox4x32_10(static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(pos),
+    const int64_t v = static_cast<int64_t>(j >> 6) * kSgIds + static_cast<int64_t>(tid >> 3) * kStripeIds +
+                      (j & 63) * kSlotIds + (tid & 7);
+    const uint32_t off = v < vocab ? static_cast<uint32_t>(v) * kEB : kPastEnd;
+    float zv;
+    if constexpr (kBf16) {
+      const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(rsrc, static_cast<int>(off), 0, 0);
+      zv = __uint_as_float(static_cast<uint32_t>(bits) << 16);
+    } else {
+      zv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, static_cast<int>(off), 0, 0));
+    }
+    const Words4 rw = philox4x32_10(static_cast<uint32_t>(v >> 2), static_cast<uint32_t>(pos),
                                     static_cast<uint32_t>(a.step), kTagElem, k0, k1);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t v = v0 + i;
-      if (v < vocab) {
-        const float g = gumbel(rw.w[(v & 3)]);
-        const float score = load_logit<kBf16>(row, v) / temp + g;
-        if (score > best) {  // v increases with i: strict > keeps the lower id
-          best = score;
-          best_id = static_cast<int32_t>(v);
-        }
-      }
+    if (v < vocab) {
+      best = zv / temp + gumbel(rw.w[v & 3]);
+      best_id = static_cast<int32_t>(v);
     }
   }
   wave_argmax(best, best_id);
@@ -320,7 +336,7 @@ __device__ void finish_row(const StatsArgs& a, const char* __restrict__ row, int
         bid = s_id[w];
       }
     }
-    double h = kLn2 * (log2(p.s) - p.w / p.s);
+    const double h = kLn2 * (log2(p.s) - p.w / p.s);
     const float hf = static_cast<float>(h);
     a.entropy[r] = hf > 0.0f ? hf : 0.0f;
     a.argmax[r] = am;
@@ -343,16 +359,24 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave index as a scalar, so the batch loop below is uniform control flow
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const float temp = a.temperature[canvas];
   const float c = kLog2e / temp;
   const uint64_t seed = a.seeds[canvas];
   const uint32_t k0 = static_cast<uint32_t>(seed);
   const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
   const int32_t vocab = a.vocab;
-  const bool ragged = (vocab & (kSlotIds - 1)) != 0;
   const char* __restrict__ row =
       static_cast<const char*>(a.logits) + static_cast<int64_t>(r) * a.row_stride * Geometry<kBf16>::kElemBytes;
+
+  // The resource covers the row rounded up to 16 bytes (inside the row
+  // stride): the range check works per dword, and a dword holding the last
+  // bf16 id and one padding id must still be read. Ids past V are masked.
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(row), 0, ((vocab * Geometry<kBf16>::kElemBytes + 15) / 16) * 16, 0x00020000);
+  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
+  const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
 
   const int32_t nsg = (vocab + kSgIds - 1) / kSgIds;
   const int32_t sg_begin = static_cast<int32_t>((static_cast<int64_t>(split) * nsg) / a.nsplit);
@@ -395,16 +419,24 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   };
   auto block_ends = [&](int32_t b) { return (b + 1) % kBatchesPerSg == 0 || b + 1 == n; };
 
+  // Byte offset of batch b for this lane; batches past the end point beyond
+  // the resource, where buffer loads return zero without touching memory, so
+  // every prefetch can be issued unconditionally (a load behind a branch would
+  // make the compiler wait for it before reducing the current batch).
+  auto byte_of = [&](int32_t b) {
+    return b < n ? static_cast<uint32_t>(first_id(b)) * kEB + lane_bytes : kPastEnd;
+  };
   uint4 buf0[NB * LPS], buf1[NB * LPS];
-  if (n > 0) load_batch<kBf16, NB>(buf0, row, first_id(0) + lane * kSlotIds, vocab);
+  load_batch<kBf16, NB>(buf0, rsrc, byte_of(0));
   for (int32_t b = 0; b < n; b += 2) {
-    if (b + 1 < n) load_batch<kBf16, NB>(buf1, row, first_id(b + 1) + lane * kSlotIds, vocab);
-    process_batch<kBf16, NB>(buf0, first_id(b) + lane * kSlotIds, first_id(b), vocab, ragged, c, st);
+    load_batch<kBf16, NB>(buf1, rsrc, byte_of(b + 1));
+    process_batch<kBf16, NB>(buf0, first_id(b) + lane * kSlotIds, first_id(b), vocab, c, st);
     if (block_ends(b)) end_of_block(b);
-    if (b + 1 >= n) break;
-    if (b + 2 < n) load_batch<kBf16, NB>(buf0, row, first_id(b + 2) + lane * kSlotIds, vocab);
-    process_batch<kBf16, NB>(buf1, first_id(b + 1) + lane * kSlotIds, first_id(b + 1), vocab, ragged, c, st);
-    if (block_ends(b + 1)) end_of_block(b + 1);
+    load_batch<kBf16, NB>(buf0, rsrc, byte_of(b + 2));
+    if (b + 1 < n) {  // a single loop exit keeps the load counters exact
+      process_batch<kBf16, NB>(buf1, first_id(b + 1) + lane * kSlotIds, first_id(b + 1), vocab, c, st);
+      if (block_ends(b + 1)) end_of_block(b + 1);
+    }
   }
 
   RowPartial wp = wave_partial(st);
@@ -431,7 +463,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     p = parts[0];
     for (int sidx = 1; sidx < a.nsplit; ++sidx) merge_partial(p, parts[sidx]);
   }
-  finish_row<kBf16>(a, row, r, pos, temp, k0, k1, p);
+  finish_row<kBf16>(a, rsrc, r, pos, temp, k0, k1, p);
 }
 
 }  // namespace

@@ -39,6 +39,10 @@ struct dg_ctx {
 
 namespace {
 
+// Rows are read through 32-bit buffer offsets; prefetches past a wave's last
+// batch use offsets beyond this size.
+constexpr int64_t kMaxRowBytes = 0x7FFF0000LL - 0x10000LL;
+
 thread_local std::string g_err;
 
 dg_status set_err(dg_ctx* ctx, dg_status st, const char* fmt, ...) {
@@ -120,6 +124,11 @@ dg_status check_logits(dg_ctx* ctx, const void* logits, dg_dtype dtype, int64_t 
   if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0)
     return set_err(ctx, DG_ERR_UNSUPPORTED, "logits is not 16-byte aligned");
   const int64_t per16 = dtype == DG_DTYPE_BF16 ? 8 : 4;
+  const int64_t row_bytes = static_cast<int64_t>(ctx->p.vocab) * (16 / per16);
+  if (row_bytes > kMaxRowBytes)
+    return set_err(ctx, DG_ERR_UNSUPPORTED,
+                   "vocab = %d is too large for this dtype: a row must hold at most %lld bytes",
+                   ctx->p.vocab, static_cast<long long>(kMaxRowBytes));
   if (row_stride % per16 != 0)
     return set_err(ctx, DG_ERR_UNSUPPORTED,
                    "row_stride = %lld must be a multiple of %lld elements (16 bytes)",

@@ -65,7 +65,7 @@ struct AcceptArgs {
   uint8_t* stop_out;           // may be null
 };
 
-constexpr int kStatsThreads = 256;
+constexpr int kStatsThreads = 512;   // 8 waves: one workgroup streams a whole row
 constexpr int kAcceptThreads = 256;
 
 // Chooses the number of workgroups per row for `rows` rows of `vocab` ids.

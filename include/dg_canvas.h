@@ -154,7 +154,8 @@ dg_status dg_canvas_init(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t*
  * Rows of inactive canvases are not written. Arguments:
  *   logits       device, [B*L rows, row_stride elements] of `dtype`; base
  *                16-byte aligned; row_stride >= V and a multiple of 8 (bf16)
- *                or 4 (fp32), else DG_ERR_UNSUPPORTED
+ *                or 4 (fp32), and V * element size below 2^31 - 2^17 bytes,
+ *                else DG_ERR_UNSUPPORTED
  *   temperature  device, fp32 [B], each > 0 and finite
  *   step         >= 0 (enters the random counters)
  *   seeds        device, uint64 [B]
