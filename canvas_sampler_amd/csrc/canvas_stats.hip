@@ -16,16 +16,20 @@
 //     sample is the id of j* with the largest z/T + element Gumbel.
 //
 // Layout and schedule (gfx950, wave64): rows are V-contiguous. A workgroup of
-// four waves handles one split (a range of 32768-id supergroups) of one row;
-// its waves take supergroups round-robin. Each lane issues one 16-byte load
-// per 512-id stripe (bf16; two for fp32), so a wave's load covers 1 KiB (bf16)
-// or 2 KiB (fp32) of consecutive memory; loads of the next batch of stripes
-// are issued before the current batch is reduced (register double buffer).
+// eight waves handles a row (or one split of it); its waves take 32768-id
+// supergroups round-robin. Each lane issues one 16-byte load per 512-id stripe
+// (bf16; two for fp32), so a wave's load covers 1 KiB (bf16) or 2 KiB (fp32)
+// of consecutive memory. Loads are raw buffer loads on a per-row resource
+// (hardware range check, no branches), marked non-temporal, and a register
+// ring keeps two batches of 8 stripes in flight while a third is reduced.
 // Per element the loop costs one convert, half a max, one fma, one v_exp_f32,
-// one add and one fma; the per-block and per-batch work is amortised over 64
-// ids per lane. When a row is split over several workgroups, each writes a
-// 32-byte partial and the last one to finish (atomic ticket, release/acquire
-// at agent scope) merges them and finishes the row.
+// one add and one fma; per-block work is amortised over 512 ids per lane.
+// When its stream ends, each wave resolves its own exact argmax (the lanes
+// holding the wave maximum re-read the batch where they first saw it) and
+// resamples its own best block, overlapping other waves still streaming; the
+// workgroup then merges eight 32-byte partials. A row split over several
+// workgroups (for very short batches) is merged by the last workgroup to
+// finish (atomic ticket, release/acquire at agent scope).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,8 +41,8 @@ constexpr double kLn2 = 0.69314718055994530942;
 constexpr int kWaves = kStatsThreads / kWave;
 constexpr float kNegInf = -__builtin_inff();
 
-// Lets the running reference trail the true maximum by up to 8 (log2 units,
-// a factor 256) before the sums are rescaled: 2^t <= 256 cannot overflow.
+// The running reference trails the true maximum by up to 8 (log2 units, a
+// factor 256) before the sums are rescaled.
 constexpr float kRefSlack = 8.0f;
 
 // Offset used for prefetches past a wave's last batch: beyond every row
@@ -48,6 +52,7 @@ constexpr uint32_t kPastEnd = 0x7FFF0000u;
 
 // Cache policy of the streaming loads: non-temporal (each logit is read once).
 constexpr int kStreamPolicy = 2;
+
 
 template <bool kBf16>
 struct Geometry {
@@ -105,6 +110,16 @@ __device__ __forceinline__ void unpack_batch(const uint4 (&buf)[NB * Geometry<kB
   }
 }
 
+// active[canvas] read through the aligned 32-bit word that holds it, so that
+// the workgroup-uniform read is a scalar load and does not queue behind the
+// vector loads already in flight (the word lies in the same page as the byte).
+__device__ __forceinline__ bool active_flag(const uint8_t* active, int32_t canvas) {
+  const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(active) & 3);
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(active - mis);
+  const uint32_t at = static_cast<uint32_t>(canvas) + mis;
+  return ((words[at >> 2] >> (8 * (at & 3))) & 0xFFu) != 0;
+}
+
 // Per-lane running state of the pass.
 struct LaneState {
   double s = 0.0;        // sum 2^t relative to ref
@@ -112,7 +127,7 @@ struct LaneState {
   double sb = 0.0;       // current block's sum 2^t relative to ref
   float ref = kNegInf;   // reference, <= max z*c seen so far
   float m = kNegInf;     // max raw logit
-  int32_t search = 0x7FFFFFFF;
+  int32_t search = 0x7FFFFFFF;  // first id of the batch where m was first seen
   float best = kNegInf;  // best block score (log2 units)
   int32_t bestj = 0x7FFFFFFF;
 };
@@ -150,56 +165,151 @@ __device__ __forceinline__ void batch_sums(const float (&z)[N], float c, float r
   bs = e[0];
 }
 
+// 2^d for a reference shift d <= 0 (exact in double): the factor only scales
+// partial sums, so fp32 v_exp_f32 of the rounded shift is accurate enough
+// (relative error below 1e-6 wherever the factor is not negligible).
+__device__ __forceinline__ double scale_of(double d) {
+  return static_cast<double>(__builtin_amdgcn_exp2f(static_cast<float>(d)));
+}
+
+// Rescales a lane's sums from reference st.ref to the larger reference r.
+__device__ __forceinline__ void rebase(LaneState& st, float r) {
+  if (st.ref != kNegInf) {
+    const double d = static_cast<double>(st.ref) - static_cast<double>(r);
+    const double f = scale_of(d);
+    st.w = f * (st.w + d * st.s);
+    st.s *= f;
+    st.sb *= f;
+  }
+  st.ref = r;
+}
+
+// Chunk-ordered reduction of a batch against reference ref: for every
+// 8-id chunk, widen, 2^t with t = z*c - ref, the chunk's fma chain for t*2^t,
+// an 8-way tree for 2^t and a max. Written chunk by chunk so that each chunk's
+// work can start when its own load has landed. Returns the batch maximum;
+// bs, bw as in batch_sums (a -inf logit gives NaN in bw; see there).
+template <bool kBf16, int NB>
+__device__ __forceinline__ float chunked_sums(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
+                                              float c, float ref, float& bs, float& bw) {
+  float cs[NB];
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float bm = kNegInf;
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    float zz[kSlotIds];
+    if constexpr (kBf16) {
+      const uint4 q = buf[s];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zz[2 * i] = __uint_as_float(w[i] << 16);
+        zz[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 q = buf[2 * s + h];
+        zz[4 * h + 0] = __uint_as_float(q.x);
+        zz[4 * h + 1] = __uint_as_float(q.y);
+        zz[4 * h + 2] = __uint_as_float(q.z);
+        zz[4 * h + 3] = __uint_as_float(q.w);
+      }
+    }
+    float e[kSlotIds];
+#pragma unroll
+    for (int k = 0; k < kSlotIds; ++k) {
+      const float t = fmaf(zz[k], c, -ref);
+      e[k] = __builtin_amdgcn_exp2f(t);
+      acc[k & 3] = fmaf(t, e[k], acc[k & 3]);
+    }
+    bm = max3_raw(bm, max3_raw(zz[0], zz[1], zz[2]),
+                  max3_raw(max3_raw(zz[3], zz[4], zz[5]), zz[6], zz[7]));
+    cs[s] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  }
+#pragma unroll
+  for (int h = NB / 2; h >= 1; h >>= 1) {
+#pragma unroll
+    for (int i = 0; i < h; ++i) cs[i] = cs[i] + cs[i + h];
+  }
+  bs = cs[0];
+  bw = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  return bm;
+}
+
+// Reduces one batch into the lane state. The exponentials use the reference
+// of the batches before (it lags the running maximum), so each chunk is
+// reduced as soon as it arrives instead of after a batch-wide maximum; the
+// batch maximum is folded in afterwards. A lag of up to 2^64 cannot overflow
+// fp32; a batch whose maximum jumps further is reduced again (rare), and so
+// is the batch holding id V-1 (ids past V are masked to -inf first) and any
+// batch holding -inf logits.
 template <bool kBf16, int NB>
 __device__ __forceinline__ void process_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
                                               int64_t id0, int64_t batch_first_id, int32_t vocab,
                                               float c, LaneState& st) {
-  float z[NB * kSlotIds];
-  unpack_batch<kBf16, NB>(buf, z);
-  if (batch_first_id + NB * kStripeIds > vocab) {
-    // the batch holding id V-1: ids past V (read as zero) become -inf
+  constexpr float kMaxLag = 64.0f;
+  const bool tail = batch_first_id + NB * kStripeIds > vocab;             // wave-uniform
+  const bool fresh = __builtin_amdgcn_ballot_w64(st.ref == kNegInf) != 0;  // wave-uniform
+  // widened batch with ids past V masked to -inf (slow paths only)
+  auto widen = [&](float (&z)[NB * kSlotIds]) {
+    unpack_batch<kBf16, NB>(buf, z);
+    if (tail) {
 #pragma unroll
-    for (int s = 0; s < NB; ++s)
+      for (int s = 0; s < NB; ++s)
 #pragma unroll
-      for (int e = 0; e < kSlotIds; ++e)
-        if (id0 + s * kStripeIds + e >= vocab) z[s * 8 + e] = kNegInf;
+        for (int e = 0; e < kSlotIds; ++e)
+          if (id0 + s * kStripeIds + e >= vocab) z[s * 8 + e] = kNegInf;
+    }
+  };
+  float bs = 0.f, bw = 0.f, bm;
+  bool redo;
+  if (!tail && !fresh) {
+    bm = chunked_sums<kBf16, NB>(buf, c, st.ref, bs, bw);
+    redo = bw != bw;  // a -inf logit: 0 * -inf
+  } else {
+    float z[NB * kSlotIds];
+    widen(z);
+    bm = z[0];
+#pragma unroll
+    for (int k = 1; k + 1 < NB * kSlotIds; k += 2) bm = max3_raw(bm, z[k], z[k + 1]);
+    bm = max3_raw(bm, z[NB * kSlotIds - 1], z[NB * kSlotIds - 1]);
+    if (st.ref == kNegInf) rebase(st, __fmul_rn(bm, c));  // first finite values of this lane
+    redo = true;
   }
-  float bm = z[0];
-#pragma unroll
-  for (int k = 1; k < NB * kSlotIds; ++k) bm = fmaxf(bm, z[k]);
   // exact argmax bookkeeping: first batch that attains the lane's maximum
   if (bm > st.m) {
     st.m = bm;
-    st.search = static_cast<int32_t>(batch_first_id >> 13);
-  }
-  const float bref = __fmul_rn(bm, c);
-  if (bref > st.ref + kRefSlack) {
-    if (st.ref != kNegInf) {
-      const double d = static_cast<double>(st.ref) - static_cast<double>(bref);
-      const double f = exp2(d);
-      st.w = f * (st.w + d * st.s);
-      st.s *= f;
-      st.sb *= f;
-    }
-    st.ref = bref;
+    st.search = static_cast<int32_t>(batch_first_id);
   }
   if (st.ref == kNegInf) return;  // nothing finite seen by this lane yet
-  float bs, bw;
-  batch_sums<NB * kSlotIds>(z, c, st.ref, bs, bw);
+  const float bref = __fmul_rn(bm, c);
+  if (bref > st.ref + kMaxLag) {  // 2^t may have overflowed
+    rebase(st, bref);
+    redo = true;
+  }
+  if (redo) {
+    float z[NB * kSlotIds];
+    widen(z);
+    batch_sums<NB * kSlotIds>(z, c, st.ref, bs, bw);
+  }
   st.s += static_cast<double>(bs);
   st.w += static_cast<double>(bw);
   st.sb += static_cast<double>(bs);
+  if (bref > st.ref + kRefSlack) rebase(st, bref);
 }
 
-// Merges partial b into a (entropy sums, argmax, best block).
+// Merges partial b into a: entropy sums, argmax (lowest id among equal
+// maxima) and the sample of the best block (lowest block among equal scores).
 __device__ __forceinline__ void merge_partial(RowPartial& a, const RowPartial& b) {
-  if (b.m > a.m || (b.m == a.m && b.search < a.search)) {
+  if (b.m > a.m || (b.m == a.m && b.argmax < a.argmax)) {
     a.m = b.m;
-    a.search = b.search;
+    a.argmax = b.argmax;
   }
   if (b.best > a.best || (b.best == a.best && b.bestj < a.bestj)) {
     a.best = b.best;
     a.bestj = b.bestj;
+    a.sample = b.sample;
   }
   if (b.ref == kNegInf) return;
   if (a.ref == kNegInf) {
@@ -211,161 +321,146 @@ __device__ __forceinline__ void merge_partial(RowPartial& a, const RowPartial& b
   const float r = fmaxf(a.ref, b.ref);
   const double da = static_cast<double>(a.ref) - static_cast<double>(r);
   const double db = static_cast<double>(b.ref) - static_cast<double>(r);
-  const double fa = exp2(da), fb = exp2(db);
+  const double fa = scale_of(da), fb = scale_of(db);
   a.w = fa * (a.w + da * a.s) + fb * (b.w + db * b.s);
   a.s = fa * a.s + fb * b.s;
   a.ref = r;
 }
 
-// Reduces the lane states of a wave into one partial (valid in every lane).
-__device__ __forceinline__ RowPartial wave_partial(const LaneState& st) {
+// Finishes a wave once its stream ends, while other waves may still be
+// streaming: reduces the lane states to one partial, finds the exact first id
+// of the wave's maximum (the lanes holding it re-read the batch where they
+// first saw it), and draws the in-block sample of the wave's best block (lane
+// k reads the block's 8 ids in stripe k). Both re-reads are issued together,
+// before any dependent work. Returns the partial in every lane.
+template <bool kBf16, int NB>
+__device__ __forceinline__ RowPartial wave_finish(const LaneState& st, __amdgpu_buffer_rsrc_t rsrc,
+                                                  int32_t vocab, float temp, int32_t pos, int32_t step,
+                                                  uint32_t k0, uint32_t k1, int lane) {
+  constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
+  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
   RowPartial p;
+  p.m = wave_max(st.m);
+  float bscore = st.best;
+  int32_t bj = st.bestj;
+  wave_argmax(bscore, bj);
+  p.best = bscore;
+  p.bestj = bj;
+
+  // loads: this lane's batch if it holds the wave maximum, and stripe `lane`
+  // of the best block (offsets past the resource read nothing)
+  const bool holds_max = p.m != kNegInf && st.m == p.m;
+  uint4 mine[NB * LPS];
+  load_batch<kBf16, NB>(mine, rsrc,
+                        holds_max ? static_cast<uint32_t>(st.search + lane * kSlotIds) * kEB : kPastEnd);
+  const int64_t v0 = static_cast<int64_t>(bj >> 6) * kSgIds + static_cast<int64_t>(lane) * kStripeIds +
+                     (bj & 63) * kSlotIds;
+  const bool block_ok = bscore != kNegInf && v0 < vocab;
+  uint4 blk[LPS];
+#pragma unroll
+  for (int h = 0; h < LPS; ++h) {
+    const uint32_t off = block_ok ? static_cast<uint32_t>(v0 + 4 * h) * kEB : kPastEnd;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off), 0, 0);
+    blk[h] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+
+  // entropy sums (independent of the loads)
   const float r = wave_max(st.ref);
   double s = 0.0, w = 0.0;
   if (st.ref != kNegInf) {
     const double d = static_cast<double>(st.ref) - static_cast<double>(r);
-    const double f = exp2(d);
+    const double f = scale_of(d);
     s = f * st.s;
     w = f * (st.w + d * st.s);
   }
   p.s = wave_sum(s);
   p.w = wave_sum(w);
   p.ref = r;
-  p.m = wave_max(st.m);
-  p.search = wave_min_int(st.m == p.m ? st.search : 0x7FFFFFFF);
-  float best = st.best;
-  int bestj = st.bestj;
-  wave_argmax(best, bestj);
-  p.best = best;
-  p.bestj = bestj;
-  p.pad = 0;
-  return p;
-}
+  // element Gumbel noise of this lane's 8 block ids: words of (v0>>2) and (v0>>2)+1
+  const Words4 g0 = philox4x32_10(static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(pos),
+                                  static_cast<uint32_t>(step), kTagElem, k0, k1);
+  const Words4 g1 = philox4x32_10(static_cast<uint32_t>(v0 >> 2) + 1u, static_cast<uint32_t>(pos),
+                                  static_cast<uint32_t>(step), kTagElem, k0, k1);
 
-// Finishes a row from its merged partial: entropy, exact argmax (re-search of
-// one 8192-id unit), and the in-block resample of block j*. Every thread of
-// the workgroup takes part with unconditional buffer loads (ids past V read
-// as zero and are excluded), so each phase costs one memory latency; thread 0
-// writes the results.
-template <bool kBf16>
-__device__ void finish_row(const StatsArgs& a, __amdgpu_buffer_rsrc_t rsrc, int32_t r,
-                           int32_t pos, float temp, uint32_t k0, uint32_t k1,
-                           const RowPartial& p) {
-  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
-  constexpr int kChunksPerThread = kSearchIds / (kStatsThreads * kSlotIds);
-  __shared__ int32_t s_min[kWaves];
-  __shared__ float s_score[kWaves];
-  __shared__ int32_t s_id[kWaves];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int32_t vocab = a.vocab;
-
-  // exact argmax: lowest id of the unit whose value equals the maximum
+  // exact argmax of the wave: lowest id equal to the maximum
   int32_t cand = 0x7FFFFFFF;
-  {
-    const int64_t base = static_cast<int64_t>(p.search) * kSearchIds;
-    float z[kChunksPerThread][kSlotIds];
+  if (holds_max) {
+    float z[NB * kSlotIds];
+    unpack_batch<kBf16, NB>(mine, z);
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int64_t id0 = base + static_cast<int64_t>(i * kStatsThreads + tid) * kSlotIds;
-      const uint32_t off = id0 < vocab ? static_cast<uint32_t>(id0) * kEB : kPastEnd;
-      if constexpr (kBf16) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off), 0, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          z[i][2 * q] = __uint_as_float(v[q] << 16);
-          z[i][2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off + 16 * h), 0, 0);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) z[i][4 * h + q] = __uint_as_float(v[q]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = kChunksPerThread - 1; i >= 0; --i) {
-      const int64_t id0 = base + static_cast<int64_t>(i * kStatsThreads + tid) * kSlotIds;
-#pragma unroll
-      for (int e = kSlotIds - 1; e >= 0; --e)
-        if (id0 + e < vocab && z[i][e] == p.m) cand = static_cast<int32_t>(id0 + e);
+    for (int k = NB * kSlotIds - 1; k >= 0; --k) {  // ids increase with k
+      const int64_t id = static_cast<int64_t>(st.search) + lane * kSlotIds + (k >> 3) * kStripeIds + (k & 7);
+      if (id < vocab && z[k] == p.m) cand = static_cast<int32_t>(id);
     }
   }
-  cand = wave_min_int(cand);
+  p.argmax = wave_min_int(cand);
 
-  // in-block resample: the 512 members of block j*, one per thread
+  // in-block resample of the wave's best block: z/T as z * (1/T), within an
+  // ulp of the quotient
+  const float inv_t = 1.0f / temp;
   float best = kNegInf;
   int32_t best_id = 0x7FFFFFFF;
-  {
-    const int32_t j = p.bestj;
-    const int64_t v = static_cast<int64_t>(j >> 6) * kSgIds + static_cast<int64_t>(tid >> 3) * kStripeIds +
-                      (j & 63) * kSlotIds + (tid & 7);
-    const uint32_t off = v < vocab ? static_cast<uint32_t>(v) * kEB : kPastEnd;
-    float zv;
+  if (block_ok) {
+    float zb[kSlotIds];
     if constexpr (kBf16) {
-      const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(rsrc, static_cast<int>(off), 0, 0);
-      zv = __uint_as_float(static_cast<uint32_t>(bits) << 16);
+      const uint32_t w4[4] = {blk[0].x, blk[0].y, blk[0].z, blk[0].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        zb[2 * q] = __uint_as_float(w4[q] << 16);
+        zb[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
+      }
     } else {
-      zv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, static_cast<int>(off), 0, 0));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        zb[4 * h + 0] = __uint_as_float(blk[h].x);
+        zb[4 * h + 1] = __uint_as_float(blk[h].y);
+        zb[4 * h + 2] = __uint_as_float(blk[h].z);
+        zb[4 * h + 3] = __uint_as_float(blk[h].w);
+      }
     }
-    const Words4 rw = philox4x32_10(static_cast<uint32_t>(v >> 2), static_cast<uint32_t>(pos),
-                                    static_cast<uint32_t>(a.step), kTagElem, k0, k1);
-    if (v < vocab) {
-      best = zv / temp + gumbel(rw.w[v & 3]);
-      best_id = static_cast<int32_t>(v);
+    const uint32_t words[8] = {g0.w[0], g0.w[1], g0.w[2], g0.w[3], g1.w[0], g1.w[1], g1.w[2], g1.w[3]};
+#pragma unroll
+    for (int e = 0; e < kSlotIds; ++e) {  // v0 is a multiple of 8: word e belongs to id v0 + e
+      if (v0 + e < vocab) {
+        const float score = zb[e] * inv_t + gumbel(words[e]);
+        if (score > best) {  // ids increase with e: strict > keeps the lower
+          best = score;
+          best_id = static_cast<int32_t>(v0 + e);
+        }
+      }
     }
   }
   wave_argmax(best, best_id);
-  if (lane == 0) {
-    s_min[wave] = cand;
-    s_score[wave] = best;
-    s_id[wave] = best_id;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int32_t am = s_min[0];
-    float bs = s_score[0];
-    int32_t bid = s_id[0];
-    for (int w = 1; w < kWaves; ++w) {
-      am = min(am, s_min[w]);
-      if (s_score[w] > bs || (s_score[w] == bs && s_id[w] < bid)) {
-        bs = s_score[w];
-        bid = s_id[w];
-      }
-    }
-    const double h = kLn2 * (log2(p.s) - p.w / p.s);
-    const float hf = static_cast<float>(h);
-    a.entropy[r] = hf > 0.0f ? hf : 0.0f;
-    a.argmax[r] = am;
-    a.sample[r] = bid;
-  }
+  p.sample = best_id;
+  return p;
 }
 
-template <bool kBf16, int NB>
+// Writes a row's outputs from its merged partial: H = ln 2 (log2 S - W/S).
+__device__ __forceinline__ void row_output(const StatsArgs& a, int32_t r, const RowPartial& p) {
+  const double h = kLn2 * (log2(p.s) - p.w / p.s);
+  const float hf = static_cast<float>(h);
+  a.entropy[r] = hf > 0.0f ? hf : 0.0f;
+  a.argmax[r] = p.argmax;
+  a.sample[r] = p.sample;
+}
+
+// NB stripes per batch; DEPTH batches in the register ring (DEPTH - 1 in
+// flight while one is reduced).
+template <bool kBf16, int NB, int DEPTH>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
   constexpr int kBatchesPerSg = kStripesPerSg / NB;
   __shared__ RowPartial s_part[kWaves];
-  __shared__ int s_last;
 
   const int32_t r = static_cast<int32_t>(blockIdx.x) / a.nsplit;
   const int32_t split = static_cast<int32_t>(blockIdx.x) % a.nsplit;
   const int32_t canvas = r / a.canvas_len;
   const int32_t pos = r % a.canvas_len;
-  if (a.active != nullptr && a.active[canvas] == 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   // wave index as a scalar, so the batch loop below is uniform control flow
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const float temp = a.temperature[canvas];
-  const float c = kLog2e / temp;
-  const uint64_t seed = a.seeds[canvas];
-  const uint32_t k0 = static_cast<uint32_t>(seed);
-  const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
   const int32_t vocab = a.vocab;
   const char* __restrict__ row =
       static_cast<const char*>(a.logits) + static_cast<int64_t>(r) * a.row_stride * Geometry<kBf16>::kElemBytes;
@@ -382,7 +477,6 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const int32_t sg_begin = static_cast<int32_t>((static_cast<int64_t>(split) * nsg) / a.nsplit);
   const int32_t sg_end = static_cast<int32_t>((static_cast<int64_t>(split + 1) * nsg) / a.nsplit);
 
-  LaneState st;
   // This wave streams supergroups sg_begin + wave, + kWaves, ... in batches of
   // NB stripes. Only the row's last supergroup can be partial, and it is the
   // last one of whichever wave owns it, so the wave's live batches form a
@@ -403,6 +497,27 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     n = (my_sgs - 1) * kBatchesPerSg +
         static_cast<int32_t>(live_last < kBatchesPerSg ? live_last : kBatchesPerSg);
   }
+  // Byte offset of batch b for this lane; batches past the end point beyond
+  // the resource, where buffer loads return zero without touching memory, so
+  // every prefetch can be issued unconditionally (a load behind a branch would
+  // make the compiler wait for it before reducing the current batch).
+  auto byte_of = [&](int32_t b) {
+    return b < n ? static_cast<uint32_t>(first_id(b)) * kEB + lane_bytes : kPastEnd;
+  };
+
+  // Register ring of DEPTH batches. The first loads go out before the per-canvas scalars are read.
+  uint4 buf[DEPTH][NB * LPS];
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) load_batch<kBf16, NB>(buf[d], rsrc, byte_of(d));
+
+  if (a.active != nullptr && !active_flag(a.active, canvas)) return;
+  const float temp = a.temperature[canvas];
+  const float c = kLog2e / temp;
+  const uint64_t seed = a.seeds[canvas];
+  const uint32_t k0 = static_cast<uint32_t>(seed);
+  const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
+
+  LaneState st;
   auto end_of_block = [&](int32_t b) {
     const int32_t j = sg_of(b) * kSlots + lane;
     float score = kNegInf;
@@ -419,51 +534,39 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   };
   auto block_ends = [&](int32_t b) { return (b + 1) % kBatchesPerSg == 0 || b + 1 == n; };
 
-  // Byte offset of batch b for this lane; batches past the end point beyond
-  // the resource, where buffer loads return zero without touching memory, so
-  // every prefetch can be issued unconditionally (a load behind a branch would
-  // make the compiler wait for it before reducing the current batch).
-  auto byte_of = [&](int32_t b) {
-    return b < n ? static_cast<uint32_t>(first_id(b)) * kEB + lane_bytes : kPastEnd;
-  };
-  uint4 buf0[NB * LPS], buf1[NB * LPS];
-  load_batch<kBf16, NB>(buf0, rsrc, byte_of(0));
-  for (int32_t b = 0; b < n; b += 2) {
-    load_batch<kBf16, NB>(buf1, rsrc, byte_of(b + 1));
-    process_batch<kBf16, NB>(buf0, first_id(b) + lane * kSlotIds, first_id(b), vocab, c, st);
-    if (block_ends(b)) end_of_block(b);
-    load_batch<kBf16, NB>(buf0, rsrc, byte_of(b + 2));
-    if (b + 1 < n) {  // a single loop exit keeps the load counters exact
-      process_batch<kBf16, NB>(buf1, first_id(b + 1) + lane * kSlotIds, first_id(b + 1), vocab, c, st);
-      if (block_ends(b + 1)) end_of_block(b + 1);
+  for (int32_t b = 0; b < n; b += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load_batch<kBf16, NB>(buf[(d + DEPTH - 1) % DEPTH], rsrc, byte_of(b + d + DEPTH - 1));
+      if (b + d < n) {  // the loop has one exit, so load counters stay exact
+        process_batch<kBf16, NB>(buf[d], first_id(b + d) + lane * kSlotIds, first_id(b + d), vocab, c, st);
+        if (block_ends(b + d)) end_of_block(b + d);
+      }
     }
   }
 
-  RowPartial wp = wave_partial(st);
+  const RowPartial wp = wave_finish<kBf16, NB>(st, rsrc, vocab, temp, pos, a.step, k0, k1, lane);
   if (lane == 0) s_part[wave] = wp;
   __syncthreads();
+  if (tid != 0) return;
   RowPartial p = s_part[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) merge_partial(p, s_part[w]);
 
   if (a.nsplit > 1) {
-    if (tid == 0) {
-      a.partials[static_cast<int64_t>(r) * a.nsplit + split] = p;
-      __threadfence();
-      const uint32_t prev = __hip_atomic_fetch_add(&a.tickets[r], 1u, __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      const int last = (prev == static_cast<uint32_t>(a.nsplit - 1));
-      if (last) __hip_atomic_store(&a.tickets[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
+    // the last workgroup of the row (atomic ticket, release/acquire at agent
+    // scope) merges every split's partial
+    a.partials[static_cast<int64_t>(r) * a.nsplit + split] = p;
+    __threadfence();
+    const uint32_t prev = __hip_atomic_fetch_add(&a.tickets[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev != static_cast<uint32_t>(a.nsplit - 1)) return;
+    __hip_atomic_store(&a.tickets[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __threadfence();
     const RowPartial* parts = a.partials + static_cast<int64_t>(r) * a.nsplit;
     p = parts[0];
     for (int sidx = 1; sidx < a.nsplit; ++sidx) merge_partial(p, parts[sidx]);
   }
-  finish_row<kBf16>(a, rsrc, r, pos, temp, k0, k1, p);
+  row_output(a, r, p);
 }
 
 }  // namespace
@@ -484,9 +587,9 @@ hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream
   const dim3 grid(static_cast<unsigned>(a.rows) * static_cast<unsigned>(a.nsplit));
   const dim3 block(kStatsThreads);
   if (bf16)
-    hipLaunchKernelGGL((canvas_stats_kernel<true, 8>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((canvas_stats_kernel<true, 2, 6>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((canvas_stats_kernel<false, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((canvas_stats_kernel<false, 2, 4>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

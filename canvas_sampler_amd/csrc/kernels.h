@@ -6,23 +6,23 @@
 
 namespace dg {
 
-// Per-(row, split) partial result of the statistics pass (32 bytes).
-//   s, w   sums of 2^t and t*2^t over the split's ids, t = z*c - ref with
-//          c = log2(e)/T and ref an fp32 value at most the split's max z*c
-//          (ref = -inf when the split saw no finite logit)
-//   ref    that reference
-//   m      largest raw logit; search = index of the 8192-id unit holding its
-//          first occurrence
-//   best   largest block score (log2 units) and bestj its block
+// Partial result of the statistics pass over part of a row (32 bytes): of a
+// wave, of a workgroup, or of a split of a row over several workgroups.
+//   s, w     sums of 2^t and t*2^t, t = z*c - ref with c = log2(e)/T and ref
+//            an fp32 value at most the part's max z*c (-inf: nothing finite)
+//   ref      that reference
+//   m        largest raw logit; argmax = lowest id attaining it
+//   best     largest block score (log2 units), bestj its block, and sample
+//            the in-block Gumbel-max draw of that block
 struct RowPartial {
   double s;
   double w;
   float ref;
   float m;
-  int32_t search;
+  int32_t argmax;
   float best;
   int32_t bestj;
-  int32_t pad;
+  int32_t sample;
 };
 
 struct StatsArgs {
