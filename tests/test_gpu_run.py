@@ -1,0 +1,262 @@
+"""GPU tests of the whole denoising loop (dg_run_canvas) and of multi-step
+trajectories, against the oracle and against the properties the method has."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from canvas_sampler_amd import binding as B
+from canvas_sampler_amd import synth
+from oracle import philox as OP
+from oracle import sampler as O
+
+from gpu_util import compare_stats, gpu, host_values, require_gpu, seeds_tensor
+
+pytestmark = gpu
+
+
+def _sharpening_denoiser(gen_seeds, L, V, m0_max, dtype):
+    def denoise(step, canvas_ptr, active_ptr, logits, stream):
+        for c, g in enumerate(gen_seeds):
+            synth.sharpening_logits(g, step, L, V, m0_max=m0_max, dtype=dtype, device="cuda",
+                                    out=logits[c * L:(c + 1) * L])
+    return denoise
+
+
+def _run_gpu(ctx, seeds, denoise, dtype, record_canvas=False):
+    Bn, L, V = len(seeds), ctx.L, ctx.V
+    logits = torch.empty(Bn * L, V, dtype=dtype, device="cuda")
+    final = torch.full((Bn, L), -1, dtype=torch.int32, device="cuda")
+    canvases = []
+
+    def wrapped(step, canvas_ptr, active_ptr, lg, stream):
+        if record_canvas:
+            buf = torch.empty(Bn, L, dtype=torch.int32, device="cuda")
+            B.copy_from_device(buf, canvas_ptr)
+            canvases.append(buf)
+        denoise(step, canvas_ptr, active_ptr, lg, stream)
+
+    steps, stopped = ctx.dg_run_canvas(seeds, wrapped, logits, final)
+    torch.cuda.synchronize()
+    return final.cpu().numpy(), steps, stopped, [c.cpu().numpy() for c in canvases]
+
+
+def test_run_matches_oracle_trajectory_reduced_vocab():
+    # sharpening denoiser (N(0,1) + m0 + 1.5*step at a fixed target, m0 ~ U[0,6]),
+    # T 0.8 -> 0.4 over 16 steps, b = 0.1, cap 48; three canvases; V reduced so
+    # that the oracle reruns every step in seconds
+    L, V = 256, 16384
+    gens = [1002, 2002, 3002]
+    seeds = [0, 7, 2**63 + 5]
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16), max_batch=3)
+    final, steps, stopped, canvases = _run_gpu(
+        ctx, seeds, _sharpening_denoiser(gens, L, V, 6.0, torch.bfloat16), torch.bfloat16,
+        record_canvas=True)
+    for c in range(3):
+        zs = {}
+
+        def den(s, canvas, g=gens[c]):
+            z = synth.sharpening_logits(g, s, L, V, m0_max=6.0, dtype=torch.bfloat16,
+                                        device="cuda")
+            zs[s] = z
+            return host_values(z)
+
+        ofinal, osteps, ostopped, rec = O.run(den, seeds[c], L, V, n_sched=16, record=True)
+        # canvases handed to the denoiser: init canvas, then the renoised ones
+        n = min(osteps, steps[c])
+        diverged = None
+        for s in range(n):
+            if not np.array_equal(canvases[s][c], rec[s]["canvas_in"]):
+                diverged = s
+                break
+        if diverged is None:
+            assert steps[c] == osteps and stopped[c] == ostopped
+            assert np.array_equal(final[c], ofinal)
+            assert 2 <= osteps < 48
+            print(f"canvas {c}: stopped after {osteps} steps, trajectory identical")
+            continue
+        # the trajectories may part only at a near-tie of the step before
+        s = diverged - 1
+        why = _explain_divergence(zs[s], rec[s], seeds[c], s, L, V, canvases[diverged][c])
+        print(f"canvas {c}: trajectories part at step {diverged} through a near-tie ({why})")
+
+
+def _explain_divergence(z, orec, seed, step, L, V, gpu_next_canvas):
+    """Reruns step `step` on the GPU for one canvas and returns the near-tie
+    that makes its next canvas differ from the oracle's; fails otherwise."""
+    from gpu_util import accept_near_tie, near_tie
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16), max_batch=1)
+    t = np.float32(O.temperature(step, 0.8, 0.4, 16))
+    h = torch.empty(L, device="cuda")
+    am = torch.empty(L, dtype=torch.int32, device="cuda")
+    smp = torch.empty(L, dtype=torch.int32, device="cuda")
+    ctx.dg_canvas_stats(z, torch.tensor([t], device="cuda"), step, seeds_tensor([seed]), h, am, smp)
+    torch.cuda.synchronize()
+    h, smp = h.cpu().numpy(), smp.cpu().numpy()
+    zh = host_values(z)
+    _, bbest, bgap, ebest, egap = O.sample_two_level_detail(zh, t, seed, np.arange(L), step)
+    dh = float(np.max(np.abs(h - orec["entropy"])))
+    mask, _ = O.accept(h.astype(np.float64), np.float32(0.1))
+    ren = O.uniform_tokens(seed, L, step, V, OP.TAG_RENOISE)
+    assert np.array_equal(gpu_next_canvas, np.where(mask, smp, ren)), "GPU canvas is not its own decision"
+    reasons = []
+    bad = np.flatnonzero(smp != orec["sample"])
+    ties = near_tie(bbest, bgap) | near_tie(ebest, egap)
+    if np.any(mask[bad] | orec["accept"][bad]):
+        hard = [i for i in bad if (mask[i] or orec["accept"][i]) and not ties[i]]
+        assert not hard, f"sample differs at committed positions {hard} without a near-tie"
+        reasons.append(f"sample near-tie at {list(bad)}")
+    if not np.array_equal(mask, orec["accept"]):
+        assert accept_near_tie(orec["entropy"], float(np.float32(0.1)), dh), \
+            f"acceptance differs without a near-tie (max |dH| {dh:.2e})"
+        reasons.append(f"acceptance boundary near-tie, max |dH| {dh:.2e}")
+    assert reasons, "trajectories part without any difference at the step before"
+    return "; ".join(reasons)
+
+
+def test_full_vocab_steps_sampled_rows_and_exact_decisions():
+    # the benchmark's single-canvas shape (B=1, 256 x 262144 bf16, nsplit auto),
+    # stepped from Python so every step's outputs are visible: oracle statistics
+    # on sampled rows, decisions checked exactly from the GPU's own entropies
+    L, V = 256, 262144
+    require_gpu()
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=16)
+    ctx = B.Context(params, max_batch=1)
+    rows = np.array([0, 5, 64, 127, 200, 255])
+    seeds = seeds_tensor([0])
+    prev = None
+    outs = {k: torch.empty(L, dtype=d, device="cuda") for k, d in
+            (("canvas_out", torch.int32), ("sample_out", torch.int32), ("accept_out", torch.uint8),
+             ("entropy_out", torch.float32))}
+    am = [torch.empty(L, dtype=torch.int32, device="cuda") for _ in range(2)]
+    nacc = torch.empty(1, dtype=torch.int32, device="cuda")
+    meanh = torch.empty(1, device="cuda")
+    stop = torch.empty(1, dtype=torch.uint8, device="cuda")
+    stopped_at = None
+    for s in range(48):
+        z = synth.sharpening_logits(1002, s, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda")
+        t = B.dg_temperature(params, s)
+        out = ctx.step_out(argmax_out=am[s & 1], n_accept_out=nacc, mean_entropy_out=meanh,
+                           stop_out=stop, **outs)
+        ctx.dg_sampler_step(z, torch.tensor([t], device="cuda"), s, seeds, out,
+                            prev_argmax=None if s == 0 else am[(s + 1) & 1])
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy() for k, v in outs.items()}
+        gam = am[s & 1].cpu().numpy()
+        zh = host_values(z[torch.as_tensor(rows, device="cuda")])
+        compare_stats(zh, np.float32(t), 0, rows, s, g["entropy_out"][rows], gam[rows],
+                      g["sample_out"][rows])
+        mask, k = O.accept(g["entropy_out"].astype(np.float64), np.float32(0.1))
+        assert np.array_equal(g["accept_out"].astype(bool), mask) and nacc.item() == k
+        ren = O.uniform_tokens(0, L, s, V, OP.TAG_RENOISE)
+        assert np.array_equal(g["canvas_out"], np.where(mask, g["sample_out"], ren))
+        mh = float(np.mean(g["entropy_out"].astype(np.float64)))
+        assert abs(meanh.item() - mh) < 1e-6
+        want_stop = O.stop_test(gam, prev, mh, np.float32(0.005))
+        assert bool(stop.item()) == want_stop
+        prev = gam
+        if want_stop:
+            stopped_at = s + 1
+            break
+    assert stopped_at is not None and stopped_at >= 2
+    print("full-vocab sharpening canvas stopped after", stopped_at, "steps")
+
+
+def test_batch_invariance_sixteen_canvases():
+    # a canvas's trajectory depends only on its own seed and logits, not on the
+    # batch it runs in: B=16 run vs single-canvas runs (full vocabulary, bf16)
+    L, V, Bn = 256, 262144, 16
+    require_gpu()
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=48)
+    gens = [(1003 << 32) | c for c in range(Bn)]
+    seeds = list(range(Bn))
+    ctx = B.Context(params, max_batch=Bn)
+    final, steps, stopped, _ = _run_gpu(ctx, seeds,
+                                        _sharpening_denoiser(gens, L, V, 8.0, torch.bfloat16),
+                                        torch.bfloat16)
+    assert all(stopped) and len(set(steps)) >= 1
+    ctx1 = B.Context(params, max_batch=1)
+    for c in (0, 5, 15):
+        f1, s1, st1, _ = _run_gpu(ctx1, [seeds[c]],
+                                  _sharpening_denoiser([gens[c]], L, V, 8.0, torch.bfloat16),
+                                  torch.bfloat16)
+        assert s1[0] == steps[c] and st1[0] == stopped[c]
+        assert np.array_equal(f1[0], final[c])
+    print("B=16 steps to stop:", steps)
+
+
+def test_run_is_deterministic():
+    L, V = 256, 32768
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16), max_batch=2)
+    den = _sharpening_denoiser([11, 12], L, V, 6.0, torch.bfloat16)
+    a = _run_gpu(ctx, [3, 4], den, torch.bfloat16)
+    b = _run_gpu(ctx, [3, 4], den, torch.bfloat16)
+    assert np.array_equal(a[0], b[0]) and a[1] == b[1] and a[2] == b[2]
+
+
+def test_low_confidence_fp32_commits_one_per_step_to_cap():
+    # untrained-model stand-in: iid N(0, 0.05) fp32 logits at V = 262144,
+    # default schedule; exactly one commit per step, no stop before the cap
+    L, V = 256, 262144
+    require_gpu()
+    params = B.params_default(canvas_len=L, vocab=V)
+    ctx = B.Context(params, max_batch=1)
+    seeds = seeds_tensor([0])
+    canvas = torch.empty(L, dtype=torch.int32, device="cuda")
+    ent = torch.empty(L, device="cuda")
+    smp = torch.empty(L, dtype=torch.int32, device="cuda")
+    am = [torch.empty(L, dtype=torch.int32, device="cuda") for _ in range(2)]
+    nacc = torch.empty(1, dtype=torch.int32, device="cuda")
+    stop = torch.empty(1, dtype=torch.uint8, device="cuda")
+    rows = np.array([0, 99, 255])
+    for s in range(48):
+        z = synth.iid_normal_logits(1004, s, L, V, variance=0.05, dtype=torch.float32, device="cuda")
+        t = B.dg_temperature(params, s)
+        out = ctx.step_out(canvas, argmax_out=am[s & 1], sample_out=smp, entropy_out=ent,
+                           n_accept_out=nacc, stop_out=stop)
+        ctx.dg_sampler_step(z, torch.tensor([t], device="cuda"), s, seeds, out,
+                            prev_argmax=None if s == 0 else am[(s + 1) & 1])
+        torch.cuda.synchronize()
+        assert nacc.item() == 1 and stop.item() == 0
+        h = ent.cpu().numpy()
+        assert abs(h.mean() - (math.log(V) - 0.05 / (2 * t * t))) < 0.03
+        if s in (0, 23, 47):
+            zh = host_values(z[torch.as_tensor(rows, device="cuda")])
+            compare_stats(zh, np.float32(t), 0, rows, s, h[rows],
+                          am[s & 1].cpu().numpy()[rows], smp.cpu().numpy()[rows])
+    # and through the library loop: runs to the cap without stopping
+    logits = torch.empty(L, V, device="cuda")
+    final = torch.empty(1, L, dtype=torch.int32, device="cuda")
+
+    def den(step, cp, ap, lg, stream):
+        synth.iid_normal_logits(1004, step, L, V, variance=0.05, device="cuda", out=lg)
+
+    steps, stopped = ctx.dg_run_canvas([0], den, logits, final)
+    assert steps == [48] and stopped == [False]
+
+
+def test_callback_failure_reports_and_keeps_steps():
+    L, V = 64, 4096
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=1)
+    logits = torch.empty(L, V, device="cuda")
+    final = torch.empty(1, L, dtype=torch.int32, device="cuda")
+
+    class Boom(RuntimeError):
+        pass
+
+    def den(step, cp, ap, lg, stream):
+        if step == 3:
+            raise Boom("denoiser failed")
+        synth.iid_normal_logits(5, step, L, V, device="cuda", out=lg)
+
+    with pytest.raises(Boom):
+        ctx.dg_run_canvas([1], den, logits, final)
+    # the library reported DG_ERR_CALLBACK; the context stays usable
+    steps, stopped = ctx.dg_run_canvas(
+        [1], lambda s, cp, ap, lg, st: synth.iid_normal_logits(5, s, L, V, device="cuda", out=lg),
+        logits, final)
+    assert steps == [48] and stopped == [False]
