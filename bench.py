@@ -69,6 +69,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="logits buffers (>= 4 beats the LLC)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 20 plain 128 MiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the sampler has no multi-GPU path (independent "
@@ -82,6 +84,15 @@ def main():
     from canvas_sampler_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": src.numel() * 2,
+                          "bytes_written": dst.numel() * 2, "launches": 20}))
+        return
     L, V, Bn = 256, 262144, 1
     R = max(1, args.rotate)
     params = B.params_default(canvas_len=L, vocab=V, temp_steps=16)
