@@ -23,7 +23,12 @@ Pins (tests/test_oracle_*.py, run with -m "not gpu"):
                          canvas (H = 0, all commit, stops at the 2nd step);
                          low-confidence canvas (1 commit/step, 48-step cap);
                          trend directions of "DiffusionGemma Lab" EXP B.
+  lmhead.logits          pure-Python dot products; exact rational sums within
+                         K * 2^-53; one-hot weight columns select hidden
+                         columns exactly; power-of-two scaling is exact
+  lmhead.step            zero hidden states give uniform logits: H = ln V at
+                         every position and exactly one commit
 No function is parity-unpinned; the bit-level choice of random protocol is
 pinned only by agreement of the two independent implementations.
 """
-from . import philox, sampler  # noqa: F401
+from . import lmhead, philox, sampler  # noqa: F401
