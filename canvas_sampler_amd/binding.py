@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_INVALID_ARG", 2: "DG_ERR_UNSUPPORTED",
 EXPORTS = ["dg_params_default", "dg_params_check", "dg_create", "dg_destroy", "dg_last_error",
            "dg_get_params", "dg_temperature", "dg_set_stats_split", "dg_canvas_init",
            "dg_canvas_stats", "dg_accept_renoise", "dg_sampler_step", "dg_run_canvas",
-           "dg_version"]
+           "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_version"]
 
 
 class DgParams(ctypes.Structure):
@@ -81,6 +81,9 @@ def lib():
             "dg_sampler_step": [vp, i32, vp, ctypes.c_int, i64, vp, i32, vp, vp, vp,
                                 ctypes.POINTER(DgStepOut), vp],
             "dg_run_canvas": [vp, i32, vp, DENOISE_FN, vp, ctypes.c_int, vp, vp, vp, vp, vp],
+            "dg_lmhead_logits": [vp, i32, vp, vp, i32, vp, i64, vp],
+            "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp,
+                                       ctypes.POINTER(DgStepOut), vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -215,6 +218,20 @@ class Context:
         self._chk(lib().dg_sampler_step(self.handle, B, _ptr(logits), _dtype_code(logits), stride,
                                         _ptr(temperature), step, _ptr(seeds), _ptr(prev_argmax),
                                         _ptr(active), ctypes.byref(out), _stream(stream)))
+
+    def dg_lmhead_logits(self, hidden, weight, logits, stream=None):
+        """logits[:rows, :V] = hidden @ weight (bf16 operands, fp32 result)."""
+        rows, k = hidden.shape
+        self._chk(lib().dg_lmhead_logits(self.handle, rows, _ptr(hidden), _ptr(weight), k,
+                                         _ptr(logits), logits.stride(0), _stream(stream)))
+
+    def dg_lmhead_sampler_step(self, hidden, weight, logits, temperature, step, seeds, out,
+                               steps=None, prev_argmax=None, active=None, stream=None):
+        B = seeds.shape[0]
+        self._chk(lib().dg_lmhead_sampler_step(self.handle, B, _ptr(hidden), _ptr(weight),
+                                               hidden.shape[1], _ptr(logits), _ptr(temperature),
+                                               step, _ptr(steps), _ptr(seeds), _ptr(prev_argmax),
+                                               _ptr(active), ctypes.byref(out), _stream(stream)))
 
     def dg_run_canvas(self, seeds, denoise, logits_scratch, final_argmax, stream=None):
         """seeds: list of ints (host). denoise(step, canvas_ptr, active_ptr, logits, stream)

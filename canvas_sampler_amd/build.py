@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdgcanvas.so")
-SOURCES = ["dg_canvas.hip", "canvas_stats.hip", "accept_renoise.hip"]
+SOURCES = ["dg_canvas.hip", "canvas_stats.hip", "accept_renoise.hip", "lmhead_gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_renoise_kernel(AcceptAr
     int32_t tok = smp;
     if (!accepted) {
       const uint64_t seed = a.seeds[canvas];
-      const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(a.step),
+      const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
+      const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(step),
                                       kTagRenoise, static_cast<uint32_t>(seed),
                                       static_cast<uint32_t>(seed >> 32));
       tok = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));

@@ -512,6 +512,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
 
   if (a.active != nullptr && !active_flag(a.active, canvas)) return;
   const float temp = a.temperature[canvas];
+  const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
   const float c = kLog2e / temp;
   const uint64_t seed = a.seeds[canvas];
   const uint32_t k0 = static_cast<uint32_t>(seed);
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     float score = kNegInf;
     if (st.sb > 0.0) {
       const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
-                                      static_cast<uint32_t>(a.step), kTagBlock, k0, k1);
+                                      static_cast<uint32_t>(step), kTagBlock, k0, k1);
       score = st.ref + __log2f(static_cast<float>(st.sb)) + kLog2e * gumbel(rw.w[0]);
     }
     if (score > st.best) {  // blocks arrive in increasing j: ties keep the lower
@@ -545,7 +546,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     }
   }
 
-  const RowPartial wp = wave_finish<kBf16, NB>(st, rsrc, vocab, temp, pos, a.step, k0, k1, lane);
+  const RowPartial wp = wave_finish<kBf16, NB>(st, rsrc, vocab, temp, pos, step, k0, k1, lane);
   if (lane == 0) s_part[wave] = wp;
   __syncthreads();
   if (tid != 0) return;

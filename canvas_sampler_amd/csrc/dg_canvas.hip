@@ -144,8 +144,8 @@ int32_t effective_nsplit(const dg_ctx* ctx, int32_t rows) {
 
 dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
                         int64_t row_stride, const float* temperature, int32_t step,
-                        const uint64_t* seeds, const uint8_t* active, float* entropy,
-                        int32_t* argmax, int32_t* sample, hipStream_t stream) {
+                        const int32_t* steps, const uint64_t* seeds, const uint8_t* active,
+                        float* entropy, int32_t* argmax, int32_t* sample, hipStream_t stream) {
   dg::StatsArgs a{};
   a.logits = logits;
   a.row_stride = row_stride;
@@ -156,6 +156,7 @@ dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dty
   a.temperature = temperature;
   a.seeds = seeds;
   a.step = step;
+  a.steps = steps;
   a.active = active;
   a.entropy = entropy;
   a.argmax = argmax;
@@ -167,9 +168,9 @@ dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dty
 }
 
 dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
-                         const int32_t* sample, int32_t step, const uint64_t* seeds,
-                         const int32_t* prev_argmax, const uint8_t* active, const dg_step_out* out,
-                         bool copy_stats, hipStream_t stream) {
+                         const int32_t* sample, int32_t step, const int32_t* steps,
+                         const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                         const dg_step_out* out, bool copy_stats, hipStream_t stream) {
   dg::AcceptArgs a{};
   a.entropy = entropy;
   a.argmax = argmax;
@@ -178,6 +179,7 @@ dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int
   a.prev_argmax = prev_argmax;
   a.active = active;
   a.step = step;
+  a.steps = steps;
   a.canvas_len = ctx->p.canvas_len;
   a.vocab = ctx->p.vocab;
   a.bound = ctx->p.entropy_bound;
@@ -193,6 +195,53 @@ dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int
   a.mean_entropy_out = out->mean_entropy_out;
   a.stop_out = out->stop_out;
   DG_CHECK_HIP(ctx, dg::launch_accept_renoise(a, B, stream));
+  return DG_OK;
+}
+
+// Operands of the LM-head product are read through 32-bit buffer offsets.
+constexpr int64_t kMaxOperandBytes = 0x7FFF0000LL;
+
+dg_status check_lmhead(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
+                       int32_t hidden_dim, const float* logits, int64_t ld_logits) {
+  if (!hidden) return set_err(ctx, DG_ERR_INVALID_ARG, "hidden is NULL");
+  if (!weight) return set_err(ctx, DG_ERR_INVALID_ARG, "weight is NULL");
+  if (!logits) return set_err(ctx, DG_ERR_INVALID_ARG, "logits is NULL");
+  if (hidden_dim < 1) return set_err(ctx, DG_ERR_INVALID_ARG, "hidden_dim = %d must be >= 1", hidden_dim);
+  if (ld_logits < ctx->p.vocab)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "ld_logits = %lld is below vocab (%d)",
+                   static_cast<long long>(ld_logits), ctx->p.vocab);
+  if (hidden_dim % 64 != 0)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "hidden_dim = %d must be a multiple of 64", hidden_dim);
+  if (ctx->p.vocab % 8 != 0)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "vocab = %d must be a multiple of 8 for the LM head", ctx->p.vocab);
+  if (ld_logits % 4 != 0)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "ld_logits = %lld must be a multiple of 4",
+                   static_cast<long long>(ld_logits));
+  if ((reinterpret_cast<uintptr_t>(hidden) & 15u) || (reinterpret_cast<uintptr_t>(weight) & 15u) ||
+      (reinterpret_cast<uintptr_t>(logits) & 15u))
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "hidden, weight and logits must be 16-byte aligned");
+  if (static_cast<int64_t>(rows) * hidden_dim * 2 > kMaxOperandBytes)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "hidden is too large: rows * hidden_dim * 2 = %lld bytes > %lld",
+                   static_cast<long long>(static_cast<int64_t>(rows) * hidden_dim * 2),
+                   static_cast<long long>(kMaxOperandBytes));
+  if (static_cast<int64_t>(hidden_dim) * ctx->p.vocab * 2 > kMaxOperandBytes)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "weight is too large: hidden_dim * vocab * 2 = %lld bytes > %lld",
+                   static_cast<long long>(static_cast<int64_t>(hidden_dim) * ctx->p.vocab * 2),
+                   static_cast<long long>(kMaxOperandBytes));
+  return DG_OK;
+}
+
+dg_status enqueue_lmhead(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
+                         int32_t hidden_dim, float* logits, int64_t ld_logits, hipStream_t stream) {
+  dg::GemmArgs g{};
+  g.hidden = hidden;
+  g.weight = weight;
+  g.logits = logits;
+  g.ld_logits = ld_logits;
+  g.rows = rows;
+  g.hidden_dim = hidden_dim;
+  g.vocab = ctx->p.vocab;
+  DG_CHECK_HIP(ctx, dg::launch_lmhead_gemm(g, stream));
   return DG_OK;
 }
 
@@ -352,8 +401,8 @@ dg_status dg_canvas_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype d
   if (!argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "argmax is NULL");
   if (!sample) return set_err(ctx, DG_ERR_INVALID_ARG, "sample is NULL");
   DeviceGuard guard(ctx->device);
-  return enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, seeds, active, entropy,
-                       argmax, sample, static_cast<hipStream_t>(stream));
+  return enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, nullptr, seeds, active,
+                       entropy, argmax, sample, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_accept_renoise(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
@@ -371,8 +420,8 @@ dg_status dg_accept_renoise(dg_ctx* ctx, int32_t B, const float* entropy, const 
   if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
   if (!out->canvas_out) return set_err(ctx, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
   DeviceGuard guard(ctx->device);
-  return enqueue_accept(ctx, B, entropy, argmax, sample, step, seeds, prev_argmax, active, out,
-                        true, static_cast<hipStream_t>(stream));
+  return enqueue_accept(ctx, B, entropy, argmax, sample, step, nullptr, seeds, prev_argmax, active,
+                        out, true, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_sampler_step(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
@@ -394,9 +443,49 @@ dg_status dg_sampler_step(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype d
   float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;
   int32_t* am = out->argmax_out ? out->argmax_out : ctx->argmax[0];
   int32_t* smp = out->sample_out ? out->sample_out : ctx->sample;
-  st = enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, seeds, active, ent, am, smp, s);
+  st = enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, nullptr, seeds, active, ent,
+                     am, smp, s);
   if (st != DG_OK) return st;
-  return enqueue_accept(ctx, B, ent, am, smp, step, seeds, prev_argmax, active, out, false, s);
+  return enqueue_accept(ctx, B, ent, am, smp, step, nullptr, seeds, prev_argmax, active, out, false, s);
+}
+
+dg_status dg_lmhead_logits(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
+                           int32_t hidden_dim, float* logits, int64_t ld_logits, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  if (rows < 1) return set_err(ctx, DG_ERR_INVALID_ARG, "rows = %d must be >= 1", rows);
+  dg_status st = check_lmhead(ctx, rows, hidden, weight, hidden_dim, logits, ld_logits);
+  if (st != DG_OK) return st;
+  DeviceGuard guard(ctx->device);
+  return enqueue_lmhead(ctx, rows, hidden, weight, hidden_dim, logits, ld_logits,
+                        static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, const void* weight,
+                                 int32_t hidden_dim, float* logits, const float* temperature,
+                                 int32_t step, const int32_t* steps, const uint64_t* seeds,
+                                 const int32_t* prev_argmax, const uint8_t* active,
+                                 const dg_step_out* out, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  const int32_t rows = B * ctx->p.canvas_len;
+  if ((st = check_lmhead(ctx, rows, hidden, weight, hidden_dim, logits, ctx->p.vocab)) != DG_OK) return st;
+  if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
+  if (step < 0) return set_err(ctx, DG_ERR_INVALID_ARG, "step = %d is negative", step);
+  if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
+  if (!out->canvas_out) return set_err(ctx, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
+  DeviceGuard guard(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = enqueue_lmhead(ctx, rows, hidden, weight, hidden_dim, logits, ctx->p.vocab, s);
+  if (st != DG_OK) return st;
+  float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;
+  int32_t* am = out->argmax_out ? out->argmax_out : ctx->argmax[0];
+  int32_t* smp = out->sample_out ? out->sample_out : ctx->sample;
+  st = enqueue_stats(ctx, B, logits, DG_DTYPE_F32, ctx->p.vocab, temperature, step, steps, seeds, active,
+                     ent, am, smp, s);
+  if (st != DG_OK) return st;
+  return enqueue_accept(ctx, B, ent, am, smp, step, steps, seeds, prev_argmax, active, out, false, s);
 }
 
 dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
@@ -444,14 +533,14 @@ dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denois
                                      hipMemcpyHostToDevice, s));
     int32_t* am_cur = ctx->argmax[step & 1];
     const int32_t* am_prev = step > 0 ? ctx->argmax[(step - 1) & 1] : nullptr;
-    st = enqueue_stats(ctx, B, logits_scratch, dtype, V, ctx->temperature, step, ctx->seeds,
+    st = enqueue_stats(ctx, B, logits_scratch, dtype, V, ctx->temperature, step, nullptr, ctx->seeds,
                        ctx->active, ctx->entropy, am_cur, ctx->sample, s);
     if (st != DG_OK) return st;
     dg_step_out o{};
     o.canvas_out = ctx->canvas;           // the denoiser has consumed the old canvas
     o.argmax_out = final_argmax;          // holds each canvas's latest argmax canvas
     o.stop_out = ctx->stop;
-    st = enqueue_accept(ctx, B, ctx->entropy, am_cur, ctx->sample, step, ctx->seeds, am_prev,
+    st = enqueue_accept(ctx, B, ctx->entropy, am_cur, ctx->sample, step, nullptr, ctx->seeds, am_prev,
                         ctx->active, &o, true, s);
     if (st != DG_OK) return st;
     DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->stop_host, ctx->stop, B, hipMemcpyDeviceToHost, s));

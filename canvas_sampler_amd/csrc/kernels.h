@@ -35,6 +35,7 @@ struct StatsArgs {
   const float* temperature;
   const uint64_t* seeds;
   int32_t step;
+  const int32_t* steps;    // may be null: per-canvas step, else `step`
   const uint8_t* active;   // may be null
   float* entropy;
   int32_t* argmax;
@@ -51,6 +52,7 @@ struct AcceptArgs {
   const int32_t* prev_argmax;  // may be null
   const uint8_t* active;       // may be null
   int32_t step;
+  const int32_t* steps;        // may be null: per-canvas step, else `step`
   int32_t canvas_len;
   int32_t vocab;
   float bound;
@@ -65,6 +67,19 @@ struct AcceptArgs {
   uint8_t* stop_out;           // may be null
 };
 
+// LM-head projection: logits[r, v] = sum_k hidden[r, k] * weight[k, v].
+struct GemmArgs {
+  const void* hidden;      // bf16 [rows, hidden_dim]
+  const void* weight;      // bf16 [hidden_dim, vocab]
+  float* logits;           // fp32 [rows, ld_logits]
+  int64_t ld_logits;
+  int32_t rows;
+  int32_t hidden_dim;      // multiple of 64
+  int32_t vocab;           // multiple of 8
+};
+
+constexpr int kGemmThreads = 512;
+
 constexpr int kStatsThreads = 512;   // 8 waves: one workgroup streams a whole row
 constexpr int kAcceptThreads = 256;
 
@@ -73,6 +88,7 @@ int32_t choose_nsplit(int32_t rows, int32_t vocab);
 
 hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_renoise(const AcceptArgs& a, int32_t batch, hipStream_t stream);
+hipError_t launch_lmhead_gemm(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_canvas_init(const uint64_t* seeds, int32_t batch, int32_t canvas_len,
                               int32_t vocab, int32_t* canvas, hipStream_t stream);
 

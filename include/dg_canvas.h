@@ -230,6 +230,42 @@ dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denois
                         void* user, dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
                         int32_t* steps_used, uint8_t* stopped, void* stream);
 
+/* LM-head projection feeding the sampler: the pages' sampling stage runs a
+ * full-vocabulary softmax over the 256 canvas positions (boxwrench.dev,
+ * "DiffusionGemma: Parallel Denoising From an Autoregressive Checkpoint", the
+ * hardware breakdown of one denoising step); its logits are the product of the
+ * decoder's last hidden states with the LM-head weights:
+ *   logits[r, v] = sum_k hidden[r, k] * weight[k, v]
+ * computed from bf16 operands with fp32 accumulation on the matrix cores
+ * (summation order unspecified) and stored as fp32.
+ *   rows        >= 1
+ *   hidden      device bf16 [rows, hidden_dim], row-major (K contiguous)
+ *   weight      device bf16 [hidden_dim, V], row-major (V contiguous), V the
+ *               context's vocab
+ *   hidden_dim  K: a positive multiple of 64      (else DG_ERR_UNSUPPORTED)
+ *   logits      device fp32 [rows, ld_logits], written in columns [0, V)
+ *   ld_logits   >= V, a multiple of 4
+ * V must be a multiple of 8 and each of rows*K*2 and K*V*2 bytes at most
+ * 0x7FFF0000 (DG_ERR_UNSUPPORTED otherwise); the three arrays must be 16-byte
+ * aligned. Asynchronous on `stream`. */
+dg_status dg_lmhead_logits(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
+                           int32_t hidden_dim, float* logits, int64_t ld_logits, void* stream);
+
+/* One sampler step of B canvases whose logits come from the LM head:
+ * dg_lmhead_logits into `logits` ([B*L, V] fp32, row stride V, caller-owned
+ * workspace that holds the logits afterwards), then dg_sampler_step on them.
+ *   temperature  device float [B]
+ *   step         the step index of every canvas when `steps` is NULL
+ *   steps        device int32 [B] or NULL: canvas c draws its random numbers
+ *                for step steps[c] (values >= 0, not checked), so canvases at
+ *                different points of their schedules share one call
+ * The other arguments are those of dg_lmhead_logits and dg_sampler_step. */
+dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, const void* weight,
+                                 int32_t hidden_dim, float* logits, const float* temperature,
+                                 int32_t step, const int32_t* steps, const uint64_t* seeds,
+                                 const int32_t* prev_argmax, const uint8_t* active,
+                                 const dg_step_out* out, void* stream);
+
 /* Library version string. */
 const char* dg_version(void);
 

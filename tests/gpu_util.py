@@ -8,10 +8,14 @@ Comparison policy:
   - sample: bit-exact except near-ties, i.e. rows where the oracle's two best
     Gumbel-perturbed scores (block level or in-block level) differ by less
     than 1e-6 * max(1, |score|); such rows are counted and reported;
-  - acceptance/stop from the GPU's own entropies: exact (the decision rule is
-    checked in isolation); from the oracle's entropies: exact except when an
-    entropy gap or the bound slack at the acceptance boundary is below the
-    measured entropy error.
+  - acceptance/stop against the oracle's: exact except when an entropy gap or
+    the bound slack at the acceptance boundary is below the measured entropy
+    error; in addition the GPU's decisions must obey the rules as properties
+    of the GPU's own outputs (check_decision_rules, which uses no oracle code);
+  - logits from the LM head (fp32 accumulation) differ from the oracle's
+    exact products by a measured per-row error e; an argmax or sample mismatch
+    is then a near-tie when the oracle's competing scores are within 2e/T of
+    each other (compare_stats's logit_err).
 """
 import numpy as np
 import pytest
@@ -45,9 +49,11 @@ def near_tie(best, gap):
     return gap < NEAR_TIE_REL * np.maximum(1.0, np.abs(best))
 
 
-def compare_stats(z_host, temp, seed, positions, step, h_gpu, am_gpu, smp_gpu, report=None):
+def compare_stats(z_host, temp, seed, positions, step, h_gpu, am_gpu, smp_gpu, report=None,
+                  logit_err=None):
     """Compares one canvas's GPU statistics (rows `positions` of z_host) with
-    the oracle. Returns a dict of measured errors and counts."""
+    the oracle. logit_err (per row, optional): how far the logits the GPU
+    consumed may be from z_host. Returns a dict of measured errors and counts."""
     z = np.asarray(z_host, dtype=np.float64)
     oh = O.entropy(z, temp)
     oam = O.argmax_raw(z)
@@ -55,10 +61,20 @@ def compare_stats(z_host, temp, seed, positions, step, h_gpu, am_gpu, smp_gpu, r
     dh = np.abs(np.asarray(h_gpu, dtype=np.float64) - oh)
     out = dict(max_dh=float(dh.max()) if dh.size else 0.0, rows=len(positions))
     assert out["max_dh"] <= H_TOL, f"entropy error {out['max_dh']:.3g} > {H_TOL}"
-    bad_am = np.flatnonzero(np.asarray(am_gpu) != oam)
-    assert bad_am.size == 0, f"argmax differs at rows {bad_am[:10]} (gpu {np.asarray(am_gpu)[bad_am[:5]]}, oracle {oam[bad_am[:5]]})"
+    am_gpu = np.asarray(am_gpu)
+    bad_am = np.flatnonzero(am_gpu != oam)
+    if logit_err is not None and bad_am.size:
+        err = np.broadcast_to(np.asarray(logit_err, dtype=np.float64), (len(positions),))
+        gap = z[bad_am, oam[bad_am]] - z[bad_am, am_gpu[bad_am]]
+        excused = gap <= 2 * err[bad_am]
+        out["argmax_near_ties"] = int(excused.sum())
+        bad_am = bad_am[~excused]
+    assert bad_am.size == 0, f"argmax differs at rows {bad_am[:10]} (gpu {am_gpu[bad_am[:5]]}, oracle {oam[bad_am[:5]]})"
     mism = np.asarray(smp_gpu) != osmp
     ties = near_tie(bbest, bgap) | near_tie(ebest, egap)
+    if logit_err is not None:
+        slack = 2 * np.asarray(logit_err, dtype=np.float64) / float(temp)
+        ties = ties | (bgap < slack) | (egap < slack)
     hard = np.flatnonzero(mism & ~ties)
     assert hard.size == 0, (f"sample differs at rows {hard[:10]} that are not near-ties: gpu "
                             f"{np.asarray(smp_gpu)[hard[:5]]}, oracle {osmp[hard[:5]]}, block gaps "
@@ -85,3 +101,35 @@ def accept_near_tie(h_oracle, bound, tol):
         near |= abs(ex[k] - bound) < slack_tol or abs(hs[k] - hs[k - 1]) < max(1e-6, 4 * tol)
     near |= abs(ex[k - 1] - bound) < slack_tol
     return near
+
+
+def check_decision_rules(h, accept, n_accept, sample, canvas, renoise, mean_h, stop, prev_argmax,
+                         argmax, bound, threshold):
+    """The acceptance, renoise and stop rules as properties of one canvas's
+    GPU outputs (no oracle code): the accepted positions are the n_accept
+    lowest by (entropy, position); the entropy of the accepted prefix without
+    its last element stays within the bound and one more position would break
+    it (fp64 sums; boundary cases closer than 1e-12 are not judged); accepted
+    positions take the sample, the others the given renoise tokens; the mean
+    entropy is the fp64 mean; the stop needs a previous argmax canvas equal to
+    this one and a mean entropy below the threshold."""
+    h = np.asarray(h, dtype=np.float64)
+    L = len(h)
+    order = np.lexsort((np.arange(L), h))
+    k = int(n_accept)
+    assert 1 <= k <= L, f"n_accept {k} outside 1..{L}"
+    want = np.zeros(L, dtype=bool)
+    want[order[:k]] = True
+    assert np.array_equal(np.asarray(accept).astype(bool), want), "accepted set is not the lowest-entropy prefix"
+    hs = h[order]
+    ex = np.concatenate([[0.0], np.cumsum(hs)])
+    assert ex[k - 1] <= bound + 1e-12, f"accepted prefix exceeds the bound: {ex[k - 1]} > {bound}"
+    if k < L:
+        assert ex[k] > bound - 1e-12, f"one more position fits the bound: {ex[k]} <= {bound}"
+    assert np.array_equal(np.asarray(canvas), np.where(want, np.asarray(sample), np.asarray(renoise)))
+    mh = float(np.mean(h))
+    assert abs(float(mean_h) - mh) <= 1e-6 * max(1.0, mh)
+    stable = prev_argmax is not None and np.array_equal(np.asarray(argmax), np.asarray(prev_argmax))
+    if abs(mh - float(threshold)) > 1e-6:
+        assert bool(stop) == (stable and mh < float(threshold))
+    return k

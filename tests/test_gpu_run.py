@@ -11,7 +11,7 @@ from canvas_sampler_amd import synth
 from oracle import philox as OP
 from oracle import sampler as O
 
-from gpu_util import compare_stats, gpu, host_values, require_gpu, seeds_tensor
+from gpu_util import check_decision_rules, compare_stats, gpu, host_values, require_gpu, seeds_tensor
 
 pytestmark = gpu
 
@@ -89,18 +89,27 @@ def _explain_divergence(z, orec, seed, step, L, V, gpu_next_canvas):
     from gpu_util import accept_near_tie, near_tie
     ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16), max_batch=1)
     t = np.float32(O.temperature(step, 0.8, 0.4, 16))
-    h = torch.empty(L, device="cuda")
-    am = torch.empty(L, dtype=torch.int32, device="cuda")
-    smp = torch.empty(L, dtype=torch.int32, device="cuda")
-    ctx.dg_canvas_stats(z, torch.tensor([t], device="cuda"), step, seeds_tensor([seed]), h, am, smp)
+    bufs = dict(canvas_out=torch.empty(L, dtype=torch.int32, device="cuda"),
+                argmax_out=torch.empty(L, dtype=torch.int32, device="cuda"),
+                sample_out=torch.empty(L, dtype=torch.int32, device="cuda"),
+                accept_out=torch.empty(L, dtype=torch.uint8, device="cuda"),
+                entropy_out=torch.empty(L, device="cuda"),
+                n_accept_out=torch.empty(1, dtype=torch.int32, device="cuda"),
+                mean_entropy_out=torch.empty(1, device="cuda"),
+                stop_out=torch.empty(1, dtype=torch.uint8, device="cuda"))
+    ctx.dg_sampler_step(z, torch.tensor([t], device="cuda"), step, seeds_tensor([seed]),
+                        ctx.step_out(**bufs))
     torch.cuda.synchronize()
-    h, smp = h.cpu().numpy(), smp.cpu().numpy()
+    g = {k: v.cpu().numpy() for k, v in bufs.items()}
+    h, smp, mask = g["entropy_out"], g["sample_out"], g["accept_out"].astype(bool)
     zh = host_values(z)
     _, bbest, bgap, ebest, egap = O.sample_two_level_detail(zh, t, seed, np.arange(L), step)
     dh = float(np.max(np.abs(h - orec["entropy"])))
-    mask, _ = O.accept(h.astype(np.float64), np.float32(0.1))
     ren = O.uniform_tokens(seed, L, step, V, OP.TAG_RENOISE)
-    assert np.array_equal(gpu_next_canvas, np.where(mask, smp, ren)), "GPU canvas is not its own decision"
+    check_decision_rules(h, mask, g["n_accept_out"][0], smp, g["canvas_out"], ren,
+                         g["mean_entropy_out"][0], g["stop_out"][0], None, g["argmax_out"],
+                         float(np.float32(0.1)), float(np.float32(0.005)))
+    assert np.array_equal(gpu_next_canvas, g["canvas_out"]), "rerun step differs from the run's"
     reasons = []
     bad = np.flatnonzero(smp != orec["sample"])
     ties = near_tie(bbest, bgap) | near_tie(ebest, egap)
@@ -148,16 +157,12 @@ def test_full_vocab_steps_sampled_rows_and_exact_decisions():
         zh = host_values(z[torch.as_tensor(rows, device="cuda")])
         compare_stats(zh, np.float32(t), 0, rows, s, g["entropy_out"][rows], gam[rows],
                       g["sample_out"][rows])
-        mask, k = O.accept(g["entropy_out"].astype(np.float64), np.float32(0.1))
-        assert np.array_equal(g["accept_out"].astype(bool), mask) and nacc.item() == k
         ren = O.uniform_tokens(0, L, s, V, OP.TAG_RENOISE)
-        assert np.array_equal(g["canvas_out"], np.where(mask, g["sample_out"], ren))
-        mh = float(np.mean(g["entropy_out"].astype(np.float64)))
-        assert abs(meanh.item() - mh) < 1e-6
-        want_stop = O.stop_test(gam, prev, mh, np.float32(0.005))
-        assert bool(stop.item()) == want_stop
+        check_decision_rules(g["entropy_out"], g["accept_out"], nacc.item(), g["sample_out"],
+                             g["canvas_out"], ren, meanh.item(), stop.item(), prev, gam,
+                             float(np.float32(0.1)), float(np.float32(0.005)))
         prev = gam
-        if want_stop:
+        if stop.item():
             stopped_at = s + 1
             break
     assert stopped_at is not None and stopped_at >= 2
