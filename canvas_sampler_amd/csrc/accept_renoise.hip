@@ -3,8 +3,8 @@
 //
 // One 256-thread workgroup per canvas, one thread per position:
 //   - sort the L keys (entropy bits << 32 | position) ascending with a
-//     bitonic network, in-wave steps by lane shuffles and the cross-wave steps
-//     through LDS (entropies are >= +0, so their fp32 bit patterns order like
+//     bitonic network, in-wave steps by DPP and permlane swaps (no LDS round
+//     trip) and the cross-wave steps through LDS (entropies are >= +0, so their fp32 bit patterns order like
 //     the values; equal entropies fall back to position order);
 //   - inclusive fp64 scan C_i of the sorted entropies; position i of the
 //     order is acceptable while C_i - H_i <= b (H_i is the running maximum of
@@ -22,6 +22,36 @@ namespace dg {
 namespace {
 
 constexpr int kWaves = kAcceptThreads / kWave;
+
+// The 64-bit key of lane (lane ^ j), j a power of two below the wave size
+// (a constant once the sorting network is unrolled).
+__device__ __forceinline__ uint64_t key_xor(uint64_t v, int j) {
+  switch (j) {
+    case 1: return lane_xor64<1>(v);
+    case 2: return lane_xor64<2>(v);
+    case 4: return lane_xor64<4>(v);
+    case 8: return lane_xor64<8>(v);
+    case 16: return lane_xor64<16>(v);
+    default: return lane_xor64<32>(v);
+  }
+}
+
+// v of lane i - s within its row of 16 lanes (row_shr:s, CTRL = 0x110 + s),
+// or 0 where that lane lies before the row.
+template <int CTRL>
+__device__ __forceinline__ double shifted_in_row(double v) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ double read_lane_f64(double v, int lane) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), lane));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
 
 __global__ __launch_bounds__(kAcceptThreads) void accept_renoise_kernel(AcceptArgs a) {
   __shared__ uint64_t s_key[kAcceptThreads];
@@ -61,9 +91,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_renoise_kernel(AcceptAr
         other = s_key[tid ^ j];
         __syncthreads();
       } else {
-        const uint32_t lo32 = __shfl_xor(static_cast<uint32_t>(key), j, kWave);
-        const uint32_t hi32 = __shfl_xor(static_cast<uint32_t>(key >> 32), j, kWave);
-        other = (static_cast<uint64_t>(hi32) << 32) | lo32;
+        other = key_xor(key, j);
       }
       const bool ascending = (tid & k) == 0;
       const bool lower = (tid & j) == 0;
@@ -73,13 +101,18 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_renoise_kernel(AcceptAr
     }
   }
 
-  // inclusive fp64 scan of sorted entropies (wave scan + wave offsets)
+  // inclusive fp64 scan of sorted entropies: rows of 16 lanes by DPP shifts,
+  // then row offsets, then wave offsets
   const double hs = valid ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(key >> 32))) : 0.0;
   double incl = hs;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double v = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += v;
+  incl += shifted_in_row<0x111>(incl);
+  incl += shifted_in_row<0x112>(incl);
+  incl += shifted_in_row<0x114>(incl);
+  incl += shifted_in_row<0x118>(incl);
+  {
+    const double t0 = read_lane_f64(incl, 15), t1 = read_lane_f64(incl, 31), t2 = read_lane_f64(incl, 47);
+    const int row = lane >> 4;
+    incl += row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
   }
   if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();

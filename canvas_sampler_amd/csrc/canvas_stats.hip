@@ -120,11 +120,14 @@ __device__ __forceinline__ bool active_flag(const uint8_t* active, int32_t canva
   return ((words[at >> 2] >> (8 * (at & 3))) & 0xFFu) != 0;
 }
 
-// Per-lane running state of the pass.
+// Per-lane running state of the pass. The current block's sums stay in fp32
+// (at most 512 ids per lane, each term below 2^8 relative to ref) and are
+// folded into the fp64 row sums when the block ends.
 struct LaneState {
-  double s = 0.0;        // sum 2^t relative to ref
-  double w = 0.0;        // sum t*2^t relative to ref
-  double sb = 0.0;       // current block's sum 2^t relative to ref
+  double s = 0.0;        // sum 2^t over finished blocks, relative to ref
+  double w = 0.0;        // sum t*2^t over finished blocks, relative to ref
+  float sb = 0.f;        // current block's sum 2^t, relative to ref
+  float wb = 0.f;        // current block's sum t*2^t, relative to ref
   float ref = kNegInf;   // reference, <= max z*c seen so far
   float m = kNegInf;     // max raw logit
   int32_t search = 0x7FFFFFFF;  // first id of the batch where m was first seen
@@ -179,7 +182,9 @@ __device__ __forceinline__ void rebase(LaneState& st, float r) {
     const double f = scale_of(d);
     st.w = f * (st.w + d * st.s);
     st.s *= f;
-    st.sb *= f;
+    const float ff = static_cast<float>(f), df = static_cast<float>(d);
+    st.wb = ff * (st.wb + df * st.sb);
+    st.sb *= ff;
   }
   st.ref = r;
 }
@@ -237,66 +242,65 @@ __device__ __forceinline__ float chunked_sums(const uint4 (&buf)[NB * Geometry<k
   return bm;
 }
 
-// Reduces one batch into the lane state. The exponentials use the reference
-// of the batches before (it lags the running maximum), so each chunk is
-// reduced as soon as it arrives instead of after a batch-wide maximum; the
-// batch maximum is folded in afterwards. A lag of up to 2^64 cannot overflow
-// fp32; a batch whose maximum jumps further is reduced again (rare), and so
-// is the batch holding id V-1 (ids past V are masked to -inf first) and any
-// batch holding -inf logits.
+// Reduces one batch on the slow path: for a lane that has seen no finite
+// logit yet, whose batch holds -inf logits (2^t = 0 but t*2^t = 0 * -inf =
+// NaN), whose maximum jumped past the lag bound, or for the batch that
+// crosses V (ids past V masked to -inf). The widened batch gives the batch
+// maximum first, the reference moves up if needed, and the sums are formed
+// against it.
 template <bool kBf16, int NB>
-__device__ __forceinline__ void process_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
-                                              int64_t id0, int64_t batch_first_id, int32_t vocab,
-                                              float c, LaneState& st) {
-  constexpr float kMaxLag = 64.0f;
-  const bool tail = batch_first_id + NB * kStripeIds > vocab;             // wave-uniform
-  const bool fresh = __builtin_amdgcn_ballot_w64(st.ref == kNegInf) != 0;  // wave-uniform
-  // widened batch with ids past V masked to -inf (slow paths only)
-  auto widen = [&](float (&z)[NB * kSlotIds]) {
-    unpack_batch<kBf16, NB>(buf, z);
-    if (tail) {
+__device__ __forceinline__ void slow_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
+                                           int64_t id0, int32_t vocab, float c, bool tail,
+                                           LaneState& st) {
+  float z[NB * kSlotIds];
+  unpack_batch<kBf16, NB>(buf, z);
+  if (tail) {
 #pragma unroll
-      for (int s = 0; s < NB; ++s)
+    for (int s = 0; s < NB; ++s)
 #pragma unroll
-        for (int e = 0; e < kSlotIds; ++e)
-          if (id0 + s * kStripeIds + e >= vocab) z[s * 8 + e] = kNegInf;
-    }
-  };
-  float bs = 0.f, bw = 0.f, bm;
-  bool redo;
-  if (!tail && !fresh) {
-    bm = chunked_sums<kBf16, NB>(buf, c, st.ref, bs, bw);
-    redo = bw != bw;  // a -inf logit: 0 * -inf
-  } else {
-    float z[NB * kSlotIds];
-    widen(z);
-    bm = z[0];
-#pragma unroll
-    for (int k = 1; k + 1 < NB * kSlotIds; k += 2) bm = max3_raw(bm, z[k], z[k + 1]);
-    bm = max3_raw(bm, z[NB * kSlotIds - 1], z[NB * kSlotIds - 1]);
-    if (st.ref == kNegInf) rebase(st, __fmul_rn(bm, c));  // first finite values of this lane
-    redo = true;
+      for (int e = 0; e < kSlotIds; ++e)
+        if (id0 + s * kStripeIds + e >= vocab) z[s * 8 + e] = kNegInf;
   }
+  float bm = z[0];
+#pragma unroll
+  for (int k = 1; k < NB * kSlotIds; ++k) bm = fmaxf(bm, z[k]);
+  if (bm == kNegInf) return;
+  const float bref = __fmul_rn(bm, c);
+  if (st.ref == kNegInf || bref > st.ref + kRefSlack) rebase(st, bref);
+  float bs, bw;
+  batch_sums<NB * kSlotIds>(z, c, st.ref, bs, bw);
+  st.sb += bs;
+  st.wb += bw;
+}
+
+// Reduces one complete batch (every id below V) into the lane state. The
+// exponentials use the reference of the batches before (it lags the running
+// maximum), so each chunk is reduced as soon as its load lands instead of
+// after a batch-wide maximum; the batch maximum is folded in afterwards. A
+// lag of up to 2^64 cannot overflow fp32; the rare batches that need more go
+// to the slow path, behind a wave-uniform branch.
+template <bool kBf16, int NB>
+__device__ __forceinline__ void fast_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
+                                           int64_t batch_first_id, int64_t id0, int32_t vocab, float c,
+                                           LaneState& st) {
+  constexpr float kMaxLag = 64.0f;
+  float bs, bw;
+  const float bm = chunked_sums<kBf16, NB>(buf, c, st.ref, bs, bw);
   // exact argmax bookkeeping: first batch that attains the lane's maximum
   if (bm > st.m) {
     st.m = bm;
     st.search = static_cast<int32_t>(batch_first_id);
   }
-  if (st.ref == kNegInf) return;  // nothing finite seen by this lane yet
   const float bref = __fmul_rn(bm, c);
-  if (bref > st.ref + kMaxLag) {  // 2^t may have overflowed
-    rebase(st, bref);
-    redo = true;
+  const bool bad = !(bw == bw) || !(bref <= st.ref + kMaxLag);  // NaN, fresh lane, or a big jump
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && bad) {
+    slow_batch<kBf16, NB>(buf, id0, vocab, c, false, st);
+  } else {
+    st.sb += bs;
+    st.wb += bw;
   }
-  if (redo) {
-    float z[NB * kSlotIds];
-    widen(z);
-    batch_sums<NB * kSlotIds>(z, c, st.ref, bs, bw);
-  }
-  st.s += static_cast<double>(bs);
-  st.w += static_cast<double>(bw);
-  st.sb += static_cast<double>(bs);
-  if (bref > st.ref + kRefSlack) rebase(st, bref);
+  const bool lift = bref > st.ref + kRefSlack;
+  if (__builtin_amdgcn_ballot_w64(lift) != 0 && lift) rebase(st, bref);
 }
 
 // Merges partial b into a: entropy sums, argmax (lowest id among equal
@@ -325,6 +329,21 @@ __device__ __forceinline__ void merge_partial(RowPartial& a, const RowPartial& b
   a.w = fa * (a.w + da * a.s) + fb * (b.w + db * b.s);
   a.s = fa * a.s + fb * b.s;
   a.ref = r;
+}
+
+// The partial held by lane (lane ^ J).
+template <int J>
+__device__ __forceinline__ RowPartial partial_xor(const RowPartial& p) {
+  RowPartial q;
+  q.s = __longlong_as_double(static_cast<long long>(lane_xor64<J>(static_cast<uint64_t>(__double_as_longlong(p.s)))));
+  q.w = __longlong_as_double(static_cast<long long>(lane_xor64<J>(static_cast<uint64_t>(__double_as_longlong(p.w)))));
+  q.ref = __uint_as_float(lane_xor<J>(__float_as_uint(p.ref)));
+  q.m = __uint_as_float(lane_xor<J>(__float_as_uint(p.m)));
+  q.argmax = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(p.argmax)));
+  q.best = __uint_as_float(lane_xor<J>(__float_as_uint(p.best)));
+  q.bestj = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(p.bestj)));
+  q.sample = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(p.sample)));
+  return q;
 }
 
 // Finishes a wave once its stream ends, while other waves may still be
@@ -364,7 +383,7 @@ __device__ __forceinline__ RowPartial wave_finish(const LaneState& st, __amdgpu_
     blk[h] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 
-  // entropy sums (independent of the loads)
+  // entropy sums (independent of the loads); every block has been folded
   const float r = wave_max(st.ref);
   double s = 0.0, w = 0.0;
   if (st.ref != kNegInf) {
@@ -450,6 +469,7 @@ template <bool kBf16, int NB, int DEPTH>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
   constexpr int kBatchesPerSg = kStripesPerSg / NB;
+  static_assert(kBatchesPerSg % DEPTH == 0, "the ring must divide a supergroup's batches");
   __shared__ RowPartial s_part[kWaves];
 
   const int32_t r = static_cast<int32_t>(blockIdx.x) / a.nsplit;
@@ -481,8 +501,8 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   // NB stripes. Only the row's last supergroup can be partial, and it is the
   // last one of whichever wave owns it, so the wave's live batches form a
   // flat range [0, n): batch b lies in supergroup sg_of(b) at stripe
-  // (b % kBatchesPerSg) * NB, and a block ends after every kBatchesPerSg-th
-  // batch and after the last one.
+  // (b % kBatchesPerSg) * NB. Batches [0, n_fast) lie wholly below V; the
+  // batch that crosses V, if any, is the last one.
   const int32_t my_sgs = (sg_end - sg_begin - wave + kWaves - 1) / kWaves;
   auto sg_of = [&](int32_t b) { return sg_begin + wave + (b / kBatchesPerSg) * kWaves; };
   auto first_id = [&](int32_t b) {
@@ -497,12 +517,13 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     n = (my_sgs - 1) * kBatchesPerSg +
         static_cast<int32_t>(live_last < kBatchesPerSg ? live_last : kBatchesPerSg);
   }
-  // Byte offset of batch b for this lane; batches past the end point beyond
+  const int32_t n_fast = (n > 0 && first_id(n - 1) + NB * kStripeIds > vocab) ? n - 1 : n;
+  // Byte offset of batch b for this lane; batches from n_fast on point beyond
   // the resource, where buffer loads return zero without touching memory, so
   // every prefetch can be issued unconditionally (a load behind a branch would
   // make the compiler wait for it before reducing the current batch).
   auto byte_of = [&](int32_t b) {
-    return b < n ? static_cast<uint32_t>(first_id(b)) * kEB + lane_bytes : kPastEnd;
+    return b < n_fast ? static_cast<uint32_t>(first_id(b)) * kEB + lane_bytes : kPastEnd;
   };
 
   // Register ring of DEPTH batches. The first loads go out before the per-canvas scalars are read.
@@ -519,40 +540,70 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
 
   LaneState st;
+  // A block (this lane's slot across the 64 stripes of a supergroup) ends:
+  // its score is its log-sum-exp plus its Gumbel, and its sums join the row's.
   auto end_of_block = [&](int32_t b) {
     const int32_t j = sg_of(b) * kSlots + lane;
     float score = kNegInf;
-    if (st.sb > 0.0) {
+    if (st.sb > 0.f) {
       const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
                                       static_cast<uint32_t>(step), kTagBlock, k0, k1);
-      score = st.ref + __log2f(static_cast<float>(st.sb)) + kLog2e * gumbel(rw.w[0]);
+      score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
     }
     if (score > st.best) {  // blocks arrive in increasing j: ties keep the lower
       st.best = score;
       st.bestj = j;
     }
-    st.sb = 0.0;
+    st.s += static_cast<double>(st.sb);
+    st.w += static_cast<double>(st.wb);
+    st.sb = 0.f;
+    st.wb = 0.f;
   };
-  auto block_ends = [&](int32_t b) { return (b + 1) % kBatchesPerSg == 0 || b + 1 == n; };
 
-  for (int32_t b = 0; b < n; b += DEPTH) {
+  // DEPTH divides a supergroup's batch count, so blocks end only after the
+  // last batch of a ring turn.
+  for (int32_t b = 0; b < n_fast; b += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       load_batch<kBf16, NB>(buf[(d + DEPTH - 1) % DEPTH], rsrc, byte_of(b + d + DEPTH - 1));
-      if (b + d < n) {  // the loop has one exit, so load counters stay exact
-        process_batch<kBf16, NB>(buf[d], first_id(b + d) + lane * kSlotIds, first_id(b + d), vocab, c, st);
-        if (block_ends(b + d)) end_of_block(b + d);
-      }
+      if (b + d < n_fast)  // the loop has one exit, so load counters stay exact
+        fast_batch<kBf16, NB>(buf[d], first_id(b + d), first_id(b + d) + lane * kSlotIds, vocab, c, st);
     }
+    if ((b + DEPTH) % kBatchesPerSg == 0 && b + DEPTH <= n_fast) end_of_block(b);
   }
+  if (n_fast < n) {
+    // the batch that crosses V: loaded again here (ids past V read as zero and
+    // are masked) and reduced on the slow path
+    uint4 tb[NB * LPS];
+    const int64_t bfirst = first_id(n - 1);
+    load_batch<kBf16, NB>(tb, rsrc, static_cast<uint32_t>(bfirst) * kEB + lane_bytes);
+    float z[NB * kSlotIds];
+    unpack_batch<kBf16, NB>(tb, z);
+    float bm = kNegInf;
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int e = 0; e < kSlotIds; ++e)
+        if (bfirst + lane * kSlotIds + q * kStripeIds + e < vocab) bm = fmaxf(bm, z[q * 8 + e]);
+    if (bm > st.m) {
+      st.m = bm;
+      st.search = static_cast<int32_t>(bfirst);
+    }
+    slow_batch<kBf16, NB>(tb, bfirst + lane * kSlotIds, vocab, c, true, st);
+  }
+  if (n > 0 && (n % kBatchesPerSg != 0 || n_fast < n)) end_of_block(n - 1);
 
   const RowPartial wp = wave_finish<kBf16, NB>(st, rsrc, vocab, temp, pos, step, k0, k1, lane);
   if (lane == 0) s_part[wave] = wp;
   __syncthreads();
-  if (tid != 0) return;
-  RowPartial p = s_part[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) merge_partial(p, s_part[w]);
+  if (wave != 0) return;
+  // merge the eight wave partials in a three-level tree across lanes 0..7 of
+  // wave 0 (lane l starts from partial l mod 8); lane 0 ends with all eight
+  RowPartial p = s_part[lane & (kWaves - 1)];
+  merge_partial(p, partial_xor<4>(p));
+  merge_partial(p, partial_xor<2>(p));
+  merge_partial(p, partial_xor<1>(p));
+  if (lane != 0) return;
 
   if (a.nsplit > 1) {
     // the last workgroup of the row (atomic ticket, release/acquire at agent
@@ -588,7 +639,7 @@ hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream
   const dim3 grid(static_cast<unsigned>(a.rows) * static_cast<unsigned>(a.nsplit));
   const dim3 block(kStatsThreads);
   if (bf16)
-    hipLaunchKernelGGL((canvas_stats_kernel<true, 2, 6>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((canvas_stats_kernel<true, 2, 4>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((canvas_stats_kernel<false, 2, 4>), grid, block, 0, stream, a);
   return hipGetLastError();

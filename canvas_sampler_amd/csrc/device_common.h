@@ -90,36 +90,133 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
   return r;
 }
 
-// ---- wave64 reductions (butterfly over all 64 lanes) ----
+// ---- cross-lane moves and wave64 reductions ----
+// All moves stay in the VALU: DPP within rows of 16 lanes, and gfx950's
+// v_permlane16_swap / v_permlane32_swap across rows and halves. Neither goes
+// through the LDS crossbar, whose round trip (ds_bpermute) would dominate the
+// short reductions that end a pass.
+
+// DPP move of v with control CTRL over all rows and banks; lanes whose source
+// lies outside their row keep v.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppShl4 = 0x104;   // row_shl:4, lane i <- lane i+4 of its row
+constexpr int kDppShr4 = 0x114;   // row_shr:4, lane i <- lane i-4 of its row
+constexpr int kDppRor4 = 0x124;   // row_ror:4, lane i <- lane (i-4) mod 16 of its row
+constexpr int kDppXor8 = 0x128;   // row_ror:8, lane i <- lane i^8
+
+// The value of lane (lane ^ J), J a power of two below 64.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) {
+    return dpp_mov<kDppXor1>(v);
+  } else if constexpr (J == 2) {
+    return dpp_mov<kDppXor2>(v);
+  } else if constexpr (J == 4) {
+    const uint32_t up = dpp_mov<kDppShl4>(v), down = dpp_mov<kDppShr4>(v);
+    return (__lane_id() & 4) ? down : up;
+  } else if constexpr (J == 8) {
+    return dpp_mov<kDppXor8>(v);
+  } else if constexpr (J == 16) {
+    // [0] holds rows (0,0,2,2) of v, [1] rows (1,1,3,3)
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & 16) ? p[0] : p[1];
+  } else {
+    static_assert(J == 32, "lane_xor: J must be a power of two below 64");
+    // [0] holds the low half of v in both halves, [1] the high half
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() & 32) ? p[0] : p[1];
+  }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+  const uint32_t lo = lane_xor<J>(static_cast<uint32_t>(v));
+  const uint32_t hi = lane_xor<J>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ float f32_of(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t u32_of(float f) { return __float_as_uint(f); }
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+#define DG_STEP(C) v = fmaxf(v, f32_of(dpp_mov<C>(u32_of(v))))
+  DG_STEP(kDppXor8); DG_STEP(kDppRor4); DG_STEP(kDppXor2); DG_STEP(kDppXor1);
+#undef DG_STEP
+  const auto p = __builtin_amdgcn_permlane16_swap(u32_of(v), u32_of(v), false, false);
+  v = fmaxf(f32_of(p[0]), f32_of(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(u32_of(v), u32_of(v), false, false);
+  return fmaxf(f32_of(q[0]), f32_of(q[1]));
 }
 
 __device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+#define DG_STEP(C) v = min(v, static_cast<int>(dpp_mov<C>(static_cast<uint32_t>(v))))
+  DG_STEP(kDppXor8); DG_STEP(kDppRor4); DG_STEP(kDppXor2); DG_STEP(kDppXor1);
+#undef DG_STEP
+  const auto p = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  v = min(static_cast<int>(p[0]), static_cast<int>(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  return min(static_cast<int>(q[0]), static_cast<int>(q[1]));
 }
 
+template <int C>
+__device__ __forceinline__ double dpp_mov_f64(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = dpp_mov<C>(static_cast<uint32_t>(b));
+  const uint32_t hi = dpp_mov<C>(static_cast<uint32_t>(b >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Sum over the wave; every lane returns the same bits.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_mov_f64<kDppXor8>(v);
+  v += dpp_mov_f64<kDppRor4>(v);
+  v += dpp_mov_f64<kDppXor2>(v);
+  v += dpp_mov_f64<kDppXor1>(v);
+  uint64_t b = __double_as_longlong(v);
+  const auto plo = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(b), static_cast<uint32_t>(b), false, false);
+  const auto phi = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(b >> 32), static_cast<uint32_t>(b >> 32),
+                                                    false, false);
+  v = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(phi[0]) << 32) | plo[0])) +
+      __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(phi[1]) << 32) | plo[1]));
+  b = __double_as_longlong(v);
+  const auto qlo = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(b), static_cast<uint32_t>(b), false, false);
+  const auto qhi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(b >> 32), static_cast<uint32_t>(b >> 32),
+                                                    false, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(qhi[0]) << 32) | qlo[0])) +
+         __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(qhi[1]) << 32) | qlo[1]));
 }
 
-// (score, index) arg-max with the lowest index winning exact ties.
-__device__ __forceinline__ void wave_argmax(float& score, int& idx) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float s2 = __shfl_xor(score, o, kWave);
-    const int i2 = __shfl_xor(idx, o, kWave);
-    if (s2 > score || (s2 == score && i2 < idx)) {
-      score = s2;
-      idx = i2;
-    }
+// (score, index) arg-max over the wave, the lowest index winning exact ties;
+// every lane returns the winner.
+__device__ __forceinline__ void argmax_combine(float& score, int& idx, float s2, int i2) {
+  if (s2 > score || (s2 == score && i2 < idx)) {
+    score = s2;
+    idx = i2;
   }
+}
+
+__device__ __forceinline__ void wave_argmax(float& score, int& idx) {
+#define DG_STEP(C) argmax_combine(score, idx, f32_of(dpp_mov<C>(u32_of(score))), \
+                                  static_cast<int>(dpp_mov<C>(static_cast<uint32_t>(idx))))
+  DG_STEP(kDppXor8); DG_STEP(kDppRor4); DG_STEP(kDppXor2); DG_STEP(kDppXor1);
+#undef DG_STEP
+  const auto ps = __builtin_amdgcn_permlane16_swap(u32_of(score), u32_of(score), false, false);
+  const auto pi = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(idx), static_cast<uint32_t>(idx), false, false);
+  score = f32_of(ps[0]);
+  idx = static_cast<int>(pi[0]);
+  argmax_combine(score, idx, f32_of(ps[1]), static_cast<int>(pi[1]));
+  const auto qs = __builtin_amdgcn_permlane32_swap(u32_of(score), u32_of(score), false, false);
+  const auto qi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(idx), static_cast<uint32_t>(idx), false, false);
+  score = f32_of(qs[0]);
+  idx = static_cast<int>(qi[0]);
+  argmax_combine(score, idx, f32_of(qs[1]), static_cast<int>(qi[1]));
 }
 
 }  // namespace dg
