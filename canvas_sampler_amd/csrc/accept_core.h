@@ -1,0 +1,175 @@
+// Acceptance, renoise and stop of one canvas (the per-canvas half of a
+// sampler step), shared by accept_renoise_kernel and by the statistics kernel
+// when the last workgroup of a canvas finishes the step itself.
+//
+// One thread per position, kAcceptThreads (256) positions at most:
+//   - sort the L keys (entropy bits << 32 | position) ascending with a
+//     bitonic network, in-wave steps by DPP and permlane swaps (no LDS round
+//     trip) and the cross-wave steps through LDS (entropies are >= +0, so
+//     their fp32 bit patterns order like the values; equal entropies fall
+//     back to position order);
+//   - inclusive fp64 scan C_i of the sorted entropies; position i of the
+//     order is acceptable while C_i - H_i <= b (H_i is the running maximum of
+//     an ascending order), and the accepted set is the longest acceptable
+//     prefix ("DiffusionGemma Lab", §2 item 2; boxwrench.dev, Algorithm 1,
+//     entropy-bounded acceptance); it is never empty since C_0 - H_0 = 0;
+//   - next canvas: the sample where accepted, else a fresh uniform token
+//     (boxwrench.dev, Algorithm 1: the remainder is renoised uniformly);
+//   - stop = previous argmax given, equal at all positions, and mean entropy
+//     below the threshold ("DiffusionGemma Lab", §2 item 3).
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dg {
+namespace accept_detail {
+
+constexpr int kWaves = kAcceptThreads / kWave;
+
+// The 64-bit key of lane (lane ^ j), j a power of two below the wave size
+// (a constant once the sorting network is unrolled).
+__device__ __forceinline__ uint64_t key_xor(uint64_t v, int j) {
+  switch (j) {
+    case 1: return lane_xor64<1>(v);
+    case 2: return lane_xor64<2>(v);
+    case 4: return lane_xor64<4>(v);
+    case 8: return lane_xor64<8>(v);
+    case 16: return lane_xor64<16>(v);
+    default: return lane_xor64<32>(v);
+  }
+}
+
+// v of lane i - s within its row of 16 lanes (row_shr:s, CTRL = 0x110 + s),
+// or 0 where that lane lies before the row.
+template <int CTRL>
+__device__ __forceinline__ double shifted_in_row(double v) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ double read_lane_f64(double v, int lane) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), lane));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+
+}  // namespace accept_detail
+
+// Runs the acceptance of `canvas` on a workgroup of NT threads (NT a multiple
+// of 64, at least kAcceptThreads); threads from kAcceptThreads on only join
+// the barriers. Every thread of the workgroup must call it; thread t < L
+// passes position t's entropy h, argmax am and sample smp.
+template <int NT>
+__device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canvas, float h, int32_t am,
+                                              int32_t smp) {
+  using namespace accept_detail;
+  static_assert(NT % kWave == 0 && NT >= kAcceptThreads, "accept_canvas: bad workgroup size");
+  __shared__ uint64_t s_key[kAcceptThreads];
+  __shared__ double s_wsum[kWaves];
+  __shared__ int32_t s_wmin[kWaves];
+  __shared__ uint8_t s_acc[kAcceptThreads];
+
+  const int tid = threadIdx.x;
+  const bool part = tid < kAcceptThreads;   // owns a key slot
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int32_t L = a.canvas_len;
+  const int64_t base = static_cast<int64_t>(canvas) * L;
+  const bool valid = tid < L;
+  // bitonic sort of 256 keys, ascending. Compare-exchange partners closer
+  // than a wave are reached with lane shuffles; only the three steps whose
+  // partner lies in another wave go through LDS.
+  uint64_t key = valid ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(tid))
+                       : ~0ull;
+#pragma unroll
+  for (int k = 2; k <= kAcceptThreads; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t other;
+      if (j >= kWave) {
+        if (part) s_key[tid] = key;
+        __syncthreads();
+        other = part ? s_key[tid ^ j] : key;
+        __syncthreads();
+      } else {
+        other = key_xor(key, j);
+      }
+      const bool ascending = (tid & k) == 0;
+      const bool lower = (tid & j) == 0;
+      const uint64_t lo = key < other ? key : other;
+      const uint64_t hi = key < other ? other : key;
+      key = (lower == ascending) ? lo : hi;
+    }
+  }
+
+  // inclusive fp64 scan of sorted entropies: rows of 16 lanes by DPP shifts,
+  // then row offsets, then wave offsets
+  const double hs = valid ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(key >> 32))) : 0.0;
+  double incl = hs;
+  incl += shifted_in_row<0x111>(incl);
+  incl += shifted_in_row<0x112>(incl);
+  incl += shifted_in_row<0x114>(incl);
+  incl += shifted_in_row<0x118>(incl);
+  {
+    const double t0 = read_lane_f64(incl, 15), t1 = read_lane_f64(incl, 31), t2 = read_lane_f64(incl, 47);
+    const int row = lane >> 4;
+    incl += row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+  }
+  if (part && lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave && w < kWaves; ++w) incl += s_wsum[w];
+
+  // first sorted index that is not acceptable; k* = that index (or L)
+  const bool ok = valid && (incl - hs) <= static_cast<double>(a.bound);
+  int32_t first_bad = (valid && !ok) ? tid : L;
+  first_bad = wave_min_int(first_bad);
+  __syncthreads();
+  if (part && lane == 0) s_wmin[wave] = first_bad;
+  __syncthreads();
+  int32_t kstar = s_wmin[0];
+  for (int w = 1; w < kWaves; ++w) kstar = min(kstar, s_wmin[w]);
+  if (valid) s_acc[static_cast<uint32_t>(key)] = static_cast<uint8_t>(tid < kstar);
+
+  // mean entropy (fp64, in position order) and argmax stability
+  double hsum = valid ? static_cast<double>(h) : 0.0;
+  hsum = wave_sum(hsum);
+  const bool same = !valid || (a.prev_argmax != nullptr && a.prev_argmax[base + tid] == am);
+  __syncthreads();
+  if (part && lane == 0) s_wsum[wave] = hsum;
+  const int all_same = __syncthreads_and(same ? 1 : 0);
+  double total = 0.0;
+  for (int w = 0; w < kWaves; ++w) total += s_wsum[w];
+  const double mean_h = total / static_cast<double>(L);
+
+  if (valid) {
+    const bool accepted = s_acc[tid] != 0;
+    int32_t tok = smp;
+    if (!accepted) {
+      const uint64_t seed = a.seeds[canvas];
+      const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
+      const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(step),
+                                      kTagRenoise, static_cast<uint32_t>(seed),
+                                      static_cast<uint32_t>(seed >> 32));
+      tok = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
+    }
+    a.canvas_out[base + tid] = tok;
+    if (a.accept_out) a.accept_out[base + tid] = accepted ? 1 : 0;
+    if (a.argmax_out) a.argmax_out[base + tid] = am;
+    if (a.sample_out) a.sample_out[base + tid] = smp;
+    if (a.entropy_out) a.entropy_out[base + tid] = h;
+  }
+  if (tid == 0) {
+    const bool stop = a.prev_argmax != nullptr && all_same &&
+                      mean_h < static_cast<double>(a.stop_mean_entropy);
+    if (a.n_accept_out) a.n_accept_out[canvas] = kstar;
+    if (a.mean_entropy_out) a.mean_entropy_out[canvas] = static_cast<float>(mean_h);
+    if (a.stop_out) a.stop_out[canvas] = stop ? 1 : 0;
+  }
+}
+
+}  // namespace dg

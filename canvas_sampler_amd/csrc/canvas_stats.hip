@@ -463,6 +463,16 @@ __device__ __forceinline__ void row_output(const StatsArgs& a, int32_t r, const 
   a.sample[r] = p.sample;
 }
 
+// Merges the eight wave partials in a three-level tree across lanes 0..7 of
+// wave 0 (lane l starts from partial l mod 8); lane 0 returns all eight.
+__device__ __forceinline__ RowPartial merge_waves(const RowPartial* s_part, int lane) {
+  RowPartial p = s_part[lane & (kWaves - 1)];
+  merge_partial(p, partial_xor<4>(p));
+  merge_partial(p, partial_xor<2>(p));
+  merge_partial(p, partial_xor<1>(p));
+  return p;
+}
+
 // NB stripes per batch; DEPTH batches in the register ring (DEPTH - 1 in
 // flight while one is reduced).
 template <bool kBf16, int NB, int DEPTH>
@@ -597,12 +607,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   if (lane == 0) s_part[wave] = wp;
   __syncthreads();
   if (wave != 0) return;
-  // merge the eight wave partials in a three-level tree across lanes 0..7 of
-  // wave 0 (lane l starts from partial l mod 8); lane 0 ends with all eight
-  RowPartial p = s_part[lane & (kWaves - 1)];
-  merge_partial(p, partial_xor<4>(p));
-  merge_partial(p, partial_xor<2>(p));
-  merge_partial(p, partial_xor<1>(p));
+  RowPartial p = merge_waves(s_part, lane);
   if (lane != 0) return;
 
   if (a.nsplit > 1) {

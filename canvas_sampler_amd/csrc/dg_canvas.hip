@@ -142,10 +142,10 @@ int32_t effective_nsplit(const dg_ctx* ctx, int32_t rows) {
   return n < 1 ? 1 : n;
 }
 
-dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
-                        int64_t row_stride, const float* temperature, int32_t step,
-                        const int32_t* steps, const uint64_t* seeds, const uint8_t* active,
-                        float* entropy, int32_t* argmax, int32_t* sample, hipStream_t stream) {
+dg::StatsArgs stats_args(const dg_ctx* ctx, int32_t B, const void* logits, int64_t row_stride,
+                         const float* temperature, int32_t step, const int32_t* steps,
+                         const uint64_t* seeds, const uint8_t* active, float* entropy, int32_t* argmax,
+                         int32_t* sample) {
   dg::StatsArgs a{};
   a.logits = logits;
   a.row_stride = row_stride;
@@ -163,14 +163,23 @@ dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dty
   a.sample = sample;
   a.partials = ctx->partials;
   a.tickets = ctx->tickets;
+  return a;
+}
+
+dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                        int64_t row_stride, const float* temperature, int32_t step,
+                        const int32_t* steps, const uint64_t* seeds, const uint8_t* active,
+                        float* entropy, int32_t* argmax, int32_t* sample, hipStream_t stream) {
+  const dg::StatsArgs a = stats_args(ctx, B, logits, row_stride, temperature, step, steps, seeds, active,
+                                     entropy, argmax, sample);
   DG_CHECK_HIP(ctx, dg::launch_canvas_stats(a, dtype == DG_DTYPE_BF16, stream));
   return DG_OK;
 }
 
-dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
-                         const int32_t* sample, int32_t step, const int32_t* steps,
-                         const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
-                         const dg_step_out* out, bool copy_stats, hipStream_t stream) {
+dg::AcceptArgs accept_args(const dg_ctx* ctx, const float* entropy, const int32_t* argmax,
+                           const int32_t* sample, int32_t step, const int32_t* steps,
+                           const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                           const dg_step_out* out, bool copy_stats) {
   dg::AcceptArgs a{};
   a.entropy = entropy;
   a.argmax = argmax;
@@ -194,8 +203,31 @@ dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int
   a.n_accept_out = out->n_accept_out;
   a.mean_entropy_out = out->mean_entropy_out;
   a.stop_out = out->stop_out;
+  return a;
+}
+
+dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
+                         const int32_t* sample, int32_t step, const int32_t* steps,
+                         const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                         const dg_step_out* out, bool copy_stats, hipStream_t stream) {
+  const dg::AcceptArgs a = accept_args(ctx, entropy, argmax, sample, step, steps, seeds, prev_argmax,
+                                       active, out, copy_stats);
   DG_CHECK_HIP(ctx, dg::launch_accept_renoise(a, B, stream));
   return DG_OK;
+}
+
+// One whole step: the statistics pass into (entropy, argmax, sample), then the
+// per-canvas acceptance.
+dg_status enqueue_step(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype, int64_t row_stride,
+                       const float* temperature, int32_t step, const int32_t* steps,
+                       const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                       float* entropy, int32_t* argmax, int32_t* sample, const dg_step_out* out,
+                       bool copy_stats, hipStream_t stream) {
+  const dg_status st = enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, steps, seeds,
+                                     active, entropy, argmax, sample, stream);
+  if (st != DG_OK) return st;
+  return enqueue_accept(ctx, B, entropy, argmax, sample, step, steps, seeds, prev_argmax, active, out,
+                        copy_stats, stream);
 }
 
 // Operands of the LM-head product are read through 32-bit buffer offsets.
@@ -336,6 +368,7 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
   const size_t rows = static_cast<size_t>(max_batch) * params->canvas_len;
   bool ok = dev_alloc(&c->partials, rows * c->nsplit_max) == hipSuccess &&
             dev_alloc(&c->tickets, rows) == hipSuccess && dev_alloc(&c->entropy, rows) == hipSuccess &&
+
             dev_alloc(&c->argmax[0], rows) == hipSuccess && dev_alloc(&c->argmax[1], rows) == hipSuccess &&
             dev_alloc(&c->sample, rows) == hipSuccess && dev_alloc(&c->canvas, rows) == hipSuccess &&
             dev_alloc(&c->seeds, max_batch) == hipSuccess &&
@@ -350,6 +383,7 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
     return set_err(nullptr, DG_ERR_OUT_OF_MEMORY, "could not allocate scratch for max_batch = %d", max_batch);
   }
   if (hipMemset(c->tickets, 0, rows * sizeof(uint32_t)) != hipSuccess ||
+
       hipDeviceSynchronize() != hipSuccess) {
     free_ctx(c);
     return set_err(nullptr, DG_ERR_DEVICE, "could not clear the ticket scratch");
@@ -443,10 +477,8 @@ dg_status dg_sampler_step(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype d
   float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;
   int32_t* am = out->argmax_out ? out->argmax_out : ctx->argmax[0];
   int32_t* smp = out->sample_out ? out->sample_out : ctx->sample;
-  st = enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, nullptr, seeds, active, ent,
-                     am, smp, s);
-  if (st != DG_OK) return st;
-  return enqueue_accept(ctx, B, ent, am, smp, step, nullptr, seeds, prev_argmax, active, out, false, s);
+  return enqueue_step(ctx, B, logits, dtype, row_stride, temperature, step, nullptr, seeds, prev_argmax,
+                      active, ent, am, smp, out, false, s);
 }
 
 dg_status dg_lmhead_logits(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
@@ -482,10 +514,8 @@ dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, con
   float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;
   int32_t* am = out->argmax_out ? out->argmax_out : ctx->argmax[0];
   int32_t* smp = out->sample_out ? out->sample_out : ctx->sample;
-  st = enqueue_stats(ctx, B, logits, DG_DTYPE_F32, ctx->p.vocab, temperature, step, steps, seeds, active,
-                     ent, am, smp, s);
-  if (st != DG_OK) return st;
-  return enqueue_accept(ctx, B, ent, am, smp, step, steps, seeds, prev_argmax, active, out, false, s);
+  return enqueue_step(ctx, B, logits, DG_DTYPE_F32, ctx->p.vocab, temperature, step, steps, seeds,
+                      prev_argmax, active, ent, am, smp, out, false, s);
 }
 
 dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
@@ -533,15 +563,12 @@ dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denois
                                      hipMemcpyHostToDevice, s));
     int32_t* am_cur = ctx->argmax[step & 1];
     const int32_t* am_prev = step > 0 ? ctx->argmax[(step - 1) & 1] : nullptr;
-    st = enqueue_stats(ctx, B, logits_scratch, dtype, V, ctx->temperature, step, nullptr, ctx->seeds,
-                       ctx->active, ctx->entropy, am_cur, ctx->sample, s);
-    if (st != DG_OK) return st;
     dg_step_out o{};
     o.canvas_out = ctx->canvas;           // the denoiser has consumed the old canvas
     o.argmax_out = final_argmax;          // holds each canvas's latest argmax canvas
     o.stop_out = ctx->stop;
-    st = enqueue_accept(ctx, B, ctx->entropy, am_cur, ctx->sample, step, nullptr, ctx->seeds, am_prev,
-                        ctx->active, &o, true, s);
+    st = enqueue_step(ctx, B, logits_scratch, dtype, V, ctx->temperature, step, nullptr, ctx->seeds,
+                      am_prev, ctx->active, ctx->entropy, am_cur, ctx->sample, &o, true, s);
     if (st != DG_OK) return st;
     DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->stop_host, ctx->stop, B, hipMemcpyDeviceToHost, s));
     DG_CHECK_HIP(ctx, hipStreamSynchronize(s));

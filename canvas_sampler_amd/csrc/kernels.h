@@ -25,25 +25,6 @@ struct RowPartial {
   int32_t sample;
 };
 
-struct StatsArgs {
-  const void* logits;
-  int64_t row_stride;      // elements
-  int32_t vocab;
-  int32_t canvas_len;
-  int32_t rows;            // B * L
-  int32_t nsplit;          // workgroups per row
-  const float* temperature;
-  const uint64_t* seeds;
-  int32_t step;
-  const int32_t* steps;    // may be null: per-canvas step, else `step`
-  const uint8_t* active;   // may be null
-  float* entropy;
-  int32_t* argmax;
-  int32_t* sample;
-  RowPartial* partials;    // [rows * nsplit] when nsplit > 1
-  uint32_t* tickets;       // [rows], zero between launches
-};
-
 struct AcceptArgs {
   const float* entropy;
   const int32_t* argmax;
@@ -65,6 +46,25 @@ struct AcceptArgs {
   int32_t* n_accept_out;       // may be null
   float* mean_entropy_out;     // may be null
   uint8_t* stop_out;           // may be null
+};
+
+struct StatsArgs {
+  const void* logits;
+  int64_t row_stride;      // elements
+  int32_t vocab;
+  int32_t canvas_len;
+  int32_t rows;            // B * L
+  int32_t nsplit;          // workgroups per row
+  const float* temperature;
+  const uint64_t* seeds;
+  int32_t step;
+  const int32_t* steps;    // may be null: per-canvas step, else `step`
+  const uint8_t* active;   // may be null
+  float* entropy;
+  int32_t* argmax;
+  int32_t* sample;
+  RowPartial* partials;    // [rows * nsplit] when nsplit > 1
+  uint32_t* tickets;       // [rows], zero between launches
 };
 
 // LM-head projection: logits[r, v] = sum_k hidden[r, k] * weight[k, v].
