@@ -13,7 +13,10 @@ hidden); the same steps replayed from captured HIP graphs are reported too.
 
 Prints one JSON line: steps/s (value), positions/s, the statistics kernel's
 achieved HBM bandwidth against the 8 TB/s peak (HIP events on the launch
-stream), and the oracle's rate on the host cores.
+stream), the oracle's rate on the host cores, and (under "lmhead") the step of
+64 canvases whose logits come from the bf16 LM-head product, hidden
+[16384, 2048] x weight [2048, 262144]: the product's time and matrix-core
+throughput against the 2.5 PFLOP/s dense bf16 peak, and the whole step's time.
 """
 import argparse
 import hashlib
@@ -27,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sampler steps/sec & canvas-positions/sec at 256xV=262144 bf16; % HBM peak"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "canvas_stats_traffic.json")
 STATS_SRC = os.path.join(ROOT, "canvas_sampler_amd", "csrc", "canvas_stats.hip")
 
@@ -61,6 +65,51 @@ def _time_graphs(graphs, k, torch):
     return start.elapsed_time(stop) / 1e3
 
 
+def lmhead_leg(args, torch, B, synth):
+    """The 64-canvas step whose logits come from the LM head: hidden bf16
+    [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
+    at step c mod 48 of the default schedule, seed c."""
+    L, K, V, Bn = 256, 2048, 262144, 64
+    params = B.params_default(canvas_len=L, vocab=V)
+    ctx = B.Context(params, max_batch=Bn)
+    hidden, weight = synth.lmhead_operands(1005, Bn * L, K, V, device="cuda")
+    logits = torch.empty(Bn * L, V, device="cuda")
+    steps = torch.tensor([c % 48 for c in range(Bn)], dtype=torch.int32, device="cuda")
+    temps = torch.tensor([B.dg_temperature(params, c % 48) for c in range(Bn)], device="cuda")
+    seeds = torch.arange(Bn, dtype=torch.int64, device="cuda")
+    canvas = torch.empty(Bn * L, dtype=torch.int32, device="cuda")
+    out = ctx.step_out(canvas)
+    stream = torch.cuda.Stream()
+    k = max(1, args.lmhead_steps)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            start.record()
+            for _ in range(k):
+                fn()
+            stop.record()
+            torch.cuda.synchronize()
+        return start.elapsed_time(stop) / 1e3 / k
+
+    gemm_s = timed(lambda: ctx.dg_lmhead_logits(hidden, weight, logits))
+    step_s = timed(lambda: ctx.dg_lmhead_sampler_step(hidden, weight, logits, temps, 0, seeds, out,
+                                                      steps=steps))
+    flops = 2.0 * Bn * L * V * K
+    tflops = flops / gemm_s / 1e12
+    ctx.close()
+    return {"workload": "64 canvases x 256 positions, LM head bf16 [16384,2048] x [2048,262144] "
+                        "-> fp32 logits -> statistics -> acceptance; per-canvas steps c mod 48",
+            "gemm_kernel": "lmhead_gemm_kernel", "gemm_ms": gemm_s * 1e3, "gemm_tflops": tflops,
+            "mfma_peak_tflops": PEAK_BF16_TFLOPS, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+            "flops_per_launch": flops, "step_ms": step_s * 1e3,
+            "stats_and_accept_ms": (step_s - gemm_s) * 1e3,
+            "positions_per_s": Bn * L / step_s, "steps_per_s": 1.0 / step_s, "timed_launches": k}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,6 +118,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="logits buffers (>= 4 beats the LLC)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head step")
+    ap.add_argument("--lmhead-only", action="store_true",
+                    help="only run the LM-head product and step (for counter runs)")
+    ap.add_argument("--lmhead-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 20 plain 128 MiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -92,6 +145,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes_read": src.numel() * 2,
                           "bytes_written": dst.numel() * 2, "launches": 20}))
+        return
+    if args.lmhead_only:
+        print(json.dumps({"lmhead": lmhead_leg(args, torch, B, synth)}), flush=True)
         return
     L, V, Bn = 256, 262144, 1
     R = max(1, args.rotate)
@@ -190,6 +246,7 @@ def main():
                      "traffic": traffic, "avg_kernel_us": stats_s * 1e6,
                      "algorithmic_bytes_per_launch": bytes_per_launch},
         "cpu_baseline": cpu,
+        "lmhead": None if args.no_lmhead else lmhead_leg(args, torch, B, synth),
     }
     print(json.dumps(rec), flush=True)
     ctx.close()

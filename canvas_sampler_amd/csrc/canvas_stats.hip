@@ -395,11 +395,18 @@ __device__ __forceinline__ RowPartial wave_finish(const LaneState& st, __amdgpu_
   p.s = wave_sum(s);
   p.w = wave_sum(w);
   p.ref = r;
-  // element Gumbel noise of this lane's 8 block ids: words of (v0>>2) and (v0>>2)+1
+  // element Gumbel noise of this lane's 8 block ids: words of (v0>>2) and
+  // (v0>>2)+1 (v0 is a multiple of 8: word e belongs to id v0 + e); it needs
+  // only the block index, so it is formed while the re-reads are in flight
   const Words4 g0 = philox4x32_10(static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(pos),
                                   static_cast<uint32_t>(step), kTagElem, k0, k1);
   const Words4 g1 = philox4x32_10(static_cast<uint32_t>(v0 >> 2) + 1u, static_cast<uint32_t>(pos),
                                   static_cast<uint32_t>(step), kTagElem, k0, k1);
+  const uint32_t words[8] = {g0.w[0], g0.w[1], g0.w[2], g0.w[3], g1.w[0], g1.w[1], g1.w[2], g1.w[3]};
+  float gum[kSlotIds];
+#pragma unroll
+  for (int e = 0; e < kSlotIds; ++e) gum[e] = gumbel(words[e]);
+  __builtin_amdgcn_sched_barrier(0);
 
   // exact argmax of the wave: lowest id equal to the maximum
   int32_t cand = 0x7FFFFFFF;
@@ -437,11 +444,10 @@ __device__ __forceinline__ RowPartial wave_finish(const LaneState& st, __amdgpu_
         zb[4 * h + 3] = __uint_as_float(blk[h].w);
       }
     }
-    const uint32_t words[8] = {g0.w[0], g0.w[1], g0.w[2], g0.w[3], g1.w[0], g1.w[1], g1.w[2], g1.w[3]};
 #pragma unroll
-    for (int e = 0; e < kSlotIds; ++e) {  // v0 is a multiple of 8: word e belongs to id v0 + e
+    for (int e = 0; e < kSlotIds; ++e) {
       if (v0 + e < vocab) {
-        const float score = zb[e] * inv_t + gumbel(words[e]);
+        const float score = zb[e] * inv_t + gum[e];
         if (score > best) {  // ids increase with e: strict > keeps the lower
           best = score;
           best_id = static_cast<int32_t>(v0 + e);
