@@ -127,9 +127,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[i][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Stage kt + 1 is written to LDS at the top of iteration kt from registers
-  // loaded during iteration kt - 1, and the loads of stage kt + 2 go out right
-  // after, so each load has a whole iteration of MFMAs to arrive.
+  // Stage kt + 1 is written to LDS in the middle of iteration kt, between the
+  // two K halves of stage kt, from registers loaded one iteration before; the
+  // loads of stage kt + 2 go out right after. The writes then overlap the
+  // matrix cores instead of stalling every wave at the top of the iteration
+  // (the written buffer is read only after the barrier that ends kt). The
+  // MFMA groups run at raised issue priority.
   load_stage(0);
   store_stage(0);
   load_stage(1);
@@ -139,11 +142,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
   const int frag_k = 8 * (lane >> 4);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    store_stage(cur ^ 1);
-    load_stage(kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
+      if (kk == 1) {
+        store_stage(cur ^ 1);
+        load_stage(kt + 2);
+      }
       bf16x8_t af[4];
       bf16x8_t bfr[8];
 #pragma unroll
@@ -154,11 +158,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
       for (int t = 0; t < 8; ++t)
         bfr[t] = *reinterpret_cast<const bf16x8_t*>(
             &lds.b[cur][(wn * 128 + t * 16 + frag_row) * kPitch + kk * 32 + frag_k]);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[t], acc[i][t], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
   }
