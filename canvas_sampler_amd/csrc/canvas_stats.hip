@@ -132,7 +132,7 @@ struct LaneState {
   float m = kNegInf;     // max raw logit
   int32_t search = 0x7FFFFFFF;  // first id of the batch where m was first seen
   float best = kNegInf;  // best block score (log2 units)
-  int32_t bestj = 0x7FFFFFFF;
+  int32_t bestj = 0x7FFFFFFF;  // its block; the lowest one among equal scores
 };
 
 // Sums of 2^t and t*2^t over a batch held in z: four interleaved fma chains
@@ -513,27 +513,40 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const int32_t sg_begin = static_cast<int32_t>((static_cast<int64_t>(split) * nsg) / a.nsplit);
   const int32_t sg_end = static_cast<int32_t>((static_cast<int64_t>(split + 1) * nsg) / a.nsplit);
 
-  // This wave streams supergroups sg_begin + wave, + kWaves, ... in batches of
-  // NB stripes. Only the row's last supergroup can be partial, and it is the
-  // last one of whichever wave owns it, so the wave's live batches form a
-  // flat range [0, n): batch b lies in supergroup sg_of(b) at stripe
-  // (b % kBatchesPerSg) * NB. Batches [0, n_fast) lie wholly below V; the
-  // batch that crosses V, if any, is the last one.
-  const int32_t my_sgs = (sg_end - sg_begin - wave + kWaves - 1) / kWaves;
-  auto sg_of = [&](int32_t b) { return sg_begin + wave + (b / kBatchesPerSg) * kWaves; };
+  // The two waves sharing a SIMD (w and w + 4) form a pair that streams
+  // supergroups sg_begin + w, + 4, ... in batches of NB stripes. Only the
+  // row's last supergroup can be partial, and it is the pair's last, so the
+  // pair's live batches form a flat range [0, npair): batch b lies in
+  // supergroup sg_of(b) at stripe (b % kBatchesPerSg) * NB. The older wave
+  // takes the first kFirstShare/16 of that range and the younger one the
+  // rest: the SIMD arbiter favours the older wave, and with equal halves the
+  // younger one would stream on alone for the last fifth. A supergroup cut
+  // by the split is closed in two pieces that the pair combines in LDS.
+  // Batches [b_lo, n_fast) of a wave lie wholly below V; the batch that
+  // crosses V, if any, is the pair's last.
+  constexpr int32_t kFirstShare = 10;
+  const int pair = wave & 3;
+  const int second = wave >> 2;
+  const int32_t pair_sgs = (sg_end - sg_begin - pair + 3) / 4;
+  auto sg_of = [&](int32_t b) { return sg_begin + pair + (b / kBatchesPerSg) * 4; };
   auto first_id = [&](int32_t b) {
     return static_cast<int64_t>(sg_of(b)) * kSgIds +
            static_cast<int64_t>(b % kBatchesPerSg) * NB * kStripeIds;
   };
-  int32_t n = 0;
-  if (my_sgs > 0) {
-    const int64_t last_sg_first = static_cast<int64_t>(sg_begin + wave + (my_sgs - 1) * kWaves) * kSgIds;
+  int32_t npair = 0;
+  if (pair_sgs > 0) {
+    const int64_t last_sg_first = static_cast<int64_t>(sg_begin + pair + (pair_sgs - 1) * 4) * kSgIds;
     const int64_t left = static_cast<int64_t>(vocab) - last_sg_first;  // > 0
     const int64_t live_last = (left + NB * kStripeIds - 1) / (NB * kStripeIds);
-    n = (my_sgs - 1) * kBatchesPerSg +
-        static_cast<int32_t>(live_last < kBatchesPerSg ? live_last : kBatchesPerSg);
+    npair = (pair_sgs - 1) * kBatchesPerSg +
+            static_cast<int32_t>(live_last < kBatchesPerSg ? live_last : kBatchesPerSg);
   }
-  const int32_t n_fast = (n > 0 && first_id(n - 1) + NB * kStripeIds > vocab) ? n - 1 : n;
+  const int32_t psplit = (npair * kFirstShare / 16) / DEPTH * DEPTH;
+  const int32_t b_lo = second ? psplit : 0;
+  const int32_t n = second ? npair : psplit;
+  const int32_t n_fast = (n > b_lo && first_id(n - 1) + NB * kStripeIds > vocab) ? n - 1 : n;
+  const bool cut = psplit % kBatchesPerSg != 0;  // a supergroup is shared by the pair
+  const int32_t sg_cut = cut ? sg_of(psplit) : -1;
   // Byte offset of batch b for this lane; batches from n_fast on point beyond
   // the resource, where buffer loads return zero without touching memory, so
   // every prefetch can be issued unconditionally (a load behind a branch would
@@ -545,7 +558,14 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   // Register ring of DEPTH batches. The first loads go out before the per-canvas scalars are read.
   uint4 buf[DEPTH][NB * LPS];
 #pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d) load_batch<kBf16, NB>(buf[d], rsrc, byte_of(d));
+  for (int d = 0; d < DEPTH - 1; ++d) load_batch<kBf16, NB>(buf[d], rsrc, byte_of(b_lo + d));
+
+  // pieces of the supergroup each pair cuts, and the pair's arrival counts
+  __shared__ float s_piece_ref[4][2][kWave];
+  __shared__ float s_piece_sb[4][2][kWave];
+  __shared__ uint32_t s_pair_arrivals[4];
+  if (tid < 4) s_pair_arrivals[tid] = 0;
+  __syncthreads();
 
   if (a.active != nullptr && !active_flag(a.active, canvas)) return;
   const float temp = a.temperature[canvas];
@@ -556,19 +576,44 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
 
   LaneState st;
-  // A block (this lane's slot across the 64 stripes of a supergroup) ends:
-  // its score is its log-sum-exp plus its Gumbel, and its sums join the row's.
-  auto end_of_block = [&](int32_t b) {
-    const int32_t j = sg_of(b) * kSlots + lane;
-    float score = kNegInf;
-    if (st.sb > 0.f) {
-      const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
-                                      static_cast<uint32_t>(step), kTagBlock, k0, k1);
-      score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
-    }
-    if (score > st.best) {  // blocks arrive in increasing j: ties keep the lower
+  auto consider = [&](float score, int32_t j) {
+    if (score > st.best || (score == st.best && j < st.bestj)) {
       st.best = score;
       st.bestj = j;
+    }
+  };
+  auto block_score = [&](int32_t j, float ref, float sb) {
+    const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
+                                    static_cast<uint32_t>(step), kTagBlock, k0, k1);
+    return ref + __log2f(sb) + kLog2e * gumbel(rw.w[0]);
+  };
+  // A block (this lane's slot across the 64 stripes of a supergroup) ends:
+  // its score is its log-sum-exp plus its Gumbel, and its sums join the row's.
+  // For the supergroup the pair cuts, this wave's piece goes to LDS instead;
+  // the wave of the pair that closes its piece second combines both pieces.
+  auto close_block = [&](int32_t b) {
+    const int32_t sg = sg_of(b);
+    const int32_t j = sg * kSlots + lane;
+    if (sg == sg_cut) {
+      s_piece_ref[pair][second][lane] = st.sb > 0.f ? st.ref : kNegInf;
+      s_piece_sb[pair][second][lane] = st.sb;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      uint32_t prev = 0;
+      if (lane == 0) prev = __hip_atomic_fetch_add(&s_pair_arrivals[pair], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (__builtin_amdgcn_readfirstlane(prev) == 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const float r0 = s_piece_ref[pair][0][lane], r1 = s_piece_ref[pair][1][lane];
+        const float q0 = s_piece_sb[pair][0][lane], q1 = s_piece_sb[pair][1][lane];
+        const float rm = fmaxf(r0, r1);
+        if (rm != kNegInf) {
+          const float sum = (r0 == kNegInf ? 0.f : q0 * __builtin_amdgcn_exp2f(r0 - rm)) +
+                            (r1 == kNegInf ? 0.f : q1 * __builtin_amdgcn_exp2f(r1 - rm));
+          consider(block_score(j, rm, sum), j);
+        }
+      }
+    } else if (st.sb > 0.f) {
+      consider(block_score(j, st.ref, st.sb), j);
     }
     st.s += static_cast<double>(st.sb);
     st.w += static_cast<double>(st.wb);
@@ -578,14 +623,14 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
 
   // DEPTH divides a supergroup's batch count, so blocks end only after the
   // last batch of a ring turn.
-  for (int32_t b = 0; b < n_fast; b += DEPTH) {
+  for (int32_t b = b_lo; b < n_fast; b += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       load_batch<kBf16, NB>(buf[(d + DEPTH - 1) % DEPTH], rsrc, byte_of(b + d + DEPTH - 1));
       if (b + d < n_fast)  // the loop has one exit, so load counters stay exact
         fast_batch<kBf16, NB>(buf[d], first_id(b + d), first_id(b + d) + lane * kSlotIds, vocab, c, st);
     }
-    if ((b + DEPTH) % kBatchesPerSg == 0 && b + DEPTH <= n_fast) end_of_block(b);
+    if ((b + DEPTH) % kBatchesPerSg == 0 && b + DEPTH <= n_fast) close_block(b);
   }
   if (n_fast < n) {
     // the batch that crosses V: loaded again here (ids past V read as zero and
@@ -607,7 +652,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     }
     slow_batch<kBf16, NB>(tb, bfirst + lane * kSlotIds, vocab, c, true, st);
   }
-  if (n > 0 && (n % kBatchesPerSg != 0 || n_fast < n)) end_of_block(n - 1);
+  if (n > b_lo && (n % kBatchesPerSg != 0 || n_fast < n)) close_block(n - 1);
 
   const RowPartial wp = wave_finish<kBf16, NB>(st, rsrc, vocab, temp, pos, step, k0, k1, lane);
   if (lane == 0) s_part[wave] = wp;
