@@ -71,6 +71,8 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   static_assert(NT % kWave == 0 && NT >= kAcceptThreads, "accept_canvas: bad workgroup size");
   __shared__ uint64_t s_key[kAcceptThreads];
   __shared__ double s_wsum[kWaves];
+  __shared__ double s_hsum[kWaves];
+  __shared__ int32_t s_same[kWaves];
   __shared__ int32_t s_wmin[kWaves];
   __shared__ uint8_t s_acc[kAcceptThreads];
 
@@ -81,6 +83,27 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   const int32_t L = a.canvas_len;
   const int64_t base = static_cast<int64_t>(canvas) * L;
   const bool valid = tid < L;
+
+  // Independent of the order: mean entropy (fp64, in position order), argmax
+  // stability and the renoise token. Formed before the sort so that they
+  // overlap it; the per-wave parts are published by the sort's LDS barriers.
+  double hsum = valid ? static_cast<double>(h) : 0.0;
+  hsum = wave_sum(hsum);
+  const bool same = !valid || (a.prev_argmax != nullptr && a.prev_argmax[base + tid] == am);
+  const bool wave_same = __builtin_amdgcn_ballot_w64(!same) == 0;
+  if (part && lane == 0) {
+    s_hsum[wave] = hsum;
+    s_same[wave] = wave_same ? 1 : 0;
+  }
+  int32_t renoise = 0;
+  if (valid) {
+    const uint64_t seed = a.seeds[canvas];
+    const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
+    const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(step),
+                                    kTagRenoise, static_cast<uint32_t>(seed),
+                                    static_cast<uint32_t>(seed >> 32));
+    renoise = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
+  }
   // bitonic sort of 256 keys, ascending. Compare-exchange partners closer
   // than a wave are reached with lane shuffles; only the three steps whose
   // partner lies in another wave go through LDS.
@@ -135,29 +158,18 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   for (int w = 1; w < kWaves; ++w) kstar = min(kstar, s_wmin[w]);
   if (valid) s_acc[static_cast<uint32_t>(key)] = static_cast<uint8_t>(tid < kstar);
 
-  // mean entropy (fp64, in position order) and argmax stability
-  double hsum = valid ? static_cast<double>(h) : 0.0;
-  hsum = wave_sum(hsum);
-  const bool same = !valid || (a.prev_argmax != nullptr && a.prev_argmax[base + tid] == am);
-  __syncthreads();
-  if (part && lane == 0) s_wsum[wave] = hsum;
-  const int all_same = __syncthreads_and(same ? 1 : 0);
   double total = 0.0;
-  for (int w = 0; w < kWaves; ++w) total += s_wsum[w];
+  int all_same = 1;
+  for (int w = 0; w < kWaves; ++w) {
+    total += s_hsum[w];
+    all_same &= s_same[w];
+  }
   const double mean_h = total / static_cast<double>(L);
+  __syncthreads();  // accept flags scattered by position
 
   if (valid) {
     const bool accepted = s_acc[tid] != 0;
-    int32_t tok = smp;
-    if (!accepted) {
-      const uint64_t seed = a.seeds[canvas];
-      const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
-      const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(step),
-                                      kTagRenoise, static_cast<uint32_t>(seed),
-                                      static_cast<uint32_t>(seed >> 32));
-      tok = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
-    }
-    a.canvas_out[base + tid] = tok;
+    a.canvas_out[base + tid] = accepted ? smp : renoise;
     if (a.accept_out) a.accept_out[base + tid] = accepted ? 1 : 0;
     if (a.argmax_out) a.argmax_out[base + tid] = am;
     if (a.sample_out) a.sample_out[base + tid] = smp;
