@@ -174,3 +174,44 @@ def test_fused_lmhead_workload_matches_oracle():
                       g["argmax_out"][r:r + 1], g["sample_out"][r:r + 1], report,
                       logit_err=err.max(axis=1))
     print("fused LM-head workload:", report)
+
+
+def test_lmhead_validation_rejects_before_launch():
+    # every argument is checked before anything is enqueued: the logits
+    # buffer keeps its sentinel after each rejected call
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=4, vocab=1024), max_batch=2)
+    h, w = synth.lmhead_operands(3, 8, 64, 1024, device="cuda")
+    z = torch.full((8, 1024), -7.0, device="cuda")
+    L = B.lib()
+    cases = [
+        (lambda: L.dg_lmhead_logits(ctx.handle, 0, B._ptr(h), B._ptr(w), 64, B._ptr(z), 1024, None),
+         B.DG_ERR_INVALID_ARG, "rows"),
+        (lambda: L.dg_lmhead_logits(ctx.handle, 8, None, B._ptr(w), 64, B._ptr(z), 1024, None),
+         B.DG_ERR_INVALID_ARG, "hidden"),
+        (lambda: L.dg_lmhead_logits(ctx.handle, 8, B._ptr(h), None, 64, B._ptr(z), 1024, None),
+         B.DG_ERR_INVALID_ARG, "weight"),
+        (lambda: L.dg_lmhead_logits(ctx.handle, 8, B._ptr(h), B._ptr(w), 64, None, 1024, None),
+         B.DG_ERR_INVALID_ARG, "logits"),
+        (lambda: L.dg_lmhead_logits(ctx.handle, 8, B._ptr(h), B._ptr(w), 64, B._ptr(z), 1000, None),
+         B.DG_ERR_INVALID_ARG, "ld_logits"),
+        (lambda: L.dg_lmhead_logits(ctx.handle, 8, B._ptr(h[:, 1:]), B._ptr(w), 64, B._ptr(z), 1024, None),
+         B.DG_ERR_UNSUPPORTED, "aligned"),
+        (lambda: L.dg_lmhead_logits(ctx.handle, 8, B._ptr(h), B._ptr(w), 64, B._ptr(z), 1026, None),
+         B.DG_ERR_UNSUPPORTED, "ld_logits"),
+    ]
+    for call, status, word in cases:
+        assert call() == status
+        assert word in L.dg_last_error(ctx.handle).decode()
+    # the fused step checks its batch and step too
+    seeds = seeds_tensor([1, 2])
+    temps = torch.tensor([0.8, 0.8], device="cuda")
+    canvas = torch.empty(8, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.DgError) as e:
+        ctx.dg_lmhead_sampler_step(h, w, z, temps, -1, seeds, ctx.step_out(canvas))
+    assert e.value.status == B.DG_ERR_INVALID_ARG and "step" in str(e.value)
+    with pytest.raises(B.DgError) as e:
+        ctx.dg_lmhead_sampler_step(h, w, z, temps, 0, seeds_tensor([1, 2, 3]), ctx.step_out(canvas))
+    assert e.value.status == B.DG_ERR_INVALID_ARG and "B = 3" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.all(z == -7.0)
