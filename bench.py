@@ -65,6 +65,57 @@ def _time_graphs(graphs, k, torch):
     return start.elapsed_time(stop) / 1e3
 
 
+def sweep_leg(torch, B, synth):
+    """Whole steps at other batch sizes (bf16, V = 262144) and the fp32
+    single canvas: steps/s, positions/s and the statistics kernel's achieved
+    HBM bandwidth (algorithmic bytes over its own time, HIP events)."""
+    L, V = 256, 262144
+    out = []
+    for Bn, dtype, R, k in ((4, torch.bfloat16, 2, 200), (16, torch.bfloat16, 2, 60),
+                            (64, torch.bfloat16, 2, 20), (1, torch.float32, 2, 400)):
+        params = B.params_default(canvas_len=L, vocab=V)
+        ctx = B.Context(params, max_batch=Bn)
+        z = [torch.empty(Bn * L, V, dtype=dtype, device="cuda") for _ in range(R)]
+        for r in range(R):
+            for c in range(Bn):
+                synth.sharpening_logits(1003 + c, r, L, V, m0_max=6.0, dtype=dtype, device="cuda",
+                                        out=z[r][c * L:(c + 1) * L])
+        temps = torch.full((Bn,), 0.6, device="cuda")
+        seeds = torch.arange(Bn, dtype=torch.int64, device="cuda")
+        canvas = torch.empty(Bn * L, dtype=torch.int32, device="cuda")
+        ent = torch.empty(Bn * L, device="cuda")
+        am = torch.empty(Bn * L, dtype=torch.int32, device="cuda")
+        smp = torch.empty(Bn * L, dtype=torch.int32, device="cuda")
+        o = ctx.step_out(canvas)
+        stream = torch.cuda.Stream()
+
+        def timed(fn):
+            with torch.cuda.stream(stream):
+                for i in range(3):
+                    fn(i)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(k):
+                    fn(i)
+                e1.record()
+                torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 1e3 / k
+
+        step_s = timed(lambda i: ctx.dg_sampler_step(z[i % R], temps, 1, seeds, o))
+        stats_s = timed(lambda i: ctx.dg_canvas_stats(z[i % R], temps, 1, seeds, ent, am, smp))
+        nbytes = Bn * L * V * z[0].element_size()
+        out.append({"batch": Bn, "dtype": "bf16" if dtype == torch.bfloat16 else "f32",
+                    "steps_per_s": 1.0 / step_s, "positions_per_s": Bn * L / step_s,
+                    "stats_us": stats_s * 1e6, "stats_gbs": nbytes / stats_s / 1e9,
+                    "stats_frac_of_8tbs": nbytes / stats_s / 1e9 / PEAK_HBM_GBS})
+        ctx.close()
+        del z
+        torch.cuda.empty_cache()
+    return out
+
+
 def lmhead_leg(args, torch, B, synth):
     """The 64-canvas step whose logits come from the LM head: hidden bf16
     [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
@@ -119,6 +170,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head step")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batch and dtype sweep")
     ap.add_argument("--lmhead-only", action="store_true",
                     help="only run the LM-head product and step (for counter runs)")
     ap.add_argument("--lmhead-steps", type=int, default=10)
@@ -246,6 +298,7 @@ def main():
                      "traffic": traffic, "avg_kernel_us": stats_s * 1e6,
                      "algorithmic_bytes_per_launch": bytes_per_launch},
         "cpu_baseline": cpu,
+        "sweep": None if args.no_sweep else sweep_leg(torch, B, synth),
         "lmhead": None if args.no_lmhead else lmhead_leg(args, torch, B, synth),
     }
     print(json.dumps(rec), flush=True)
