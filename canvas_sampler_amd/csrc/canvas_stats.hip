@@ -10,26 +10,29 @@
 //   - the argmax of the raw logits, lowest id on ties (§2 item 5: the argmax
 //     canvas is the output);
 //   - one multinomial sample (§2 item 5) by the two-level Gumbel-max protocol:
-//     each lane owns one block per supergroup (one 8-id slot across 64
-//     stripes), forms that block's log-sum-exp on the fly and adds its block
-//     Gumbel; the best block j* is re-read (512 ids, 0.2% of the row) and the
-//     sample is the id of j* with the largest z/T + element Gumbel.
+//     a block is one 8-id slot across the 8 stripes of a 4096-id chunk; each
+//     lane forms its block's log-sum-exp on the fly and adds the block's
+//     Gumbel, and the sample is the id of the best block j* with the largest
+//     z/T + element Gumbel.
 //
 // Layout and schedule (gfx950, wave64): rows are V-contiguous. A workgroup of
-// eight waves handles a row (or one split of it); its waves take 32768-id
-// supergroups round-robin. Each lane issues one 16-byte load per 512-id stripe
-// (bf16; two for fp32), so a wave's load covers 1 KiB (bf16) or 2 KiB (fp32)
-// of consecutive memory. Loads are raw buffer loads on a per-row resource
-// (hardware range check, no branches), marked non-temporal, and a register
-// ring keeps two batches of 8 stripes in flight while a third is reduced.
-// Per element the loop costs one convert, half a max, one fma, one v_exp_f32,
-// one add and one fma; per-block work is amortised over 512 ids per lane.
-// When its stream ends, each wave resolves its own exact argmax (the lanes
-// holding the wave maximum re-read the batch where they first saw it) and
-// resamples its own best block, overlapping other waves still streaming; the
-// workgroup then merges eight 32-byte partials. A row split over several
-// workgroups (for very short batches) is merged by the last workgroup to
-// finish (atomic ticket, release/acquire at agent scope).
+// eight waves handles a row (or one split of it); wave w takes the split's
+// chunks w, w + 8, ..., so that the workgroup streams 32 KiB (bf16) of
+// consecutive memory at a time. Each lane issues one 16-byte load per 512-id
+// stripe (bf16; two for fp32); a batch is 4 stripes and a block 2 batches,
+// and a register ring holds two blocks: one is reduced while the other is in
+// flight. Loads are raw buffer loads on a per-row resource (hardware range
+// check, no branches), marked non-temporal. Per element the loop costs one
+// convert, half a max, one fma, one v_exp_f32, one add and one fma; per block
+// (64 ids per lane) one Philox draw. When a block ends its logits are still
+// in registers, so nothing is read twice: if the block beats the wave's best
+// block, the wave resamples it on the spot (the winning lane hands its 64
+// logits to the wave through LDS), and if a lane's block holds a new wave
+// maximum, the lane finds its first id on the spot. After the stream each
+// wave folds its sums, and the workgroup merges eight 40-byte partials. A
+// row split over several workgroups (for very short batches) is merged by
+// the last workgroup to finish (atomic ticket, release/acquire at agent
+// scope).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -120,19 +123,15 @@ __device__ __forceinline__ bool active_flag(const uint8_t* active, int32_t canva
   return ((words[at >> 2] >> (8 * (at & 3))) & 0xFFu) != 0;
 }
 
-// Per-lane running state of the pass. The current block's sums stay in fp32
-// (at most 512 ids per lane, each term below 2^8 relative to ref) and are
-// folded into the fp64 row sums when the block ends.
+// Per-lane running state of the sums. The current block's sums stay in fp32
+// (64 ids per lane, each term below 2^8 relative to ref) and are folded into
+// the fp64 row sums when the block ends.
 struct LaneState {
   double s = 0.0;        // sum 2^t over finished blocks, relative to ref
   double w = 0.0;        // sum t*2^t over finished blocks, relative to ref
   float sb = 0.f;        // current block's sum 2^t, relative to ref
   float wb = 0.f;        // current block's sum t*2^t, relative to ref
   float ref = kNegInf;   // reference, <= max z*c seen so far
-  float m = kNegInf;     // max raw logit
-  int32_t search = 0x7FFFFFFF;  // first id of the batch where m was first seen
-  float best = kNegInf;  // best block score (log2 units)
-  int32_t bestj = 0x7FFFFFFF;  // its block; the lowest one among equal scores
 };
 
 // Sums of 2^t and t*2^t over a batch held in z: four interleaved fma chains
@@ -273,24 +272,19 @@ __device__ __forceinline__ void slow_batch(const uint4 (&buf)[NB * Geometry<kBf1
   st.wb += bw;
 }
 
-// Reduces one complete batch (every id below V) into the lane state. The
-// exponentials use the reference of the batches before (it lags the running
-// maximum), so each chunk is reduced as soon as its load lands instead of
-// after a batch-wide maximum; the batch maximum is folded in afterwards. A
-// lag of up to 2^64 cannot overflow fp32; the rare batches that need more go
-// to the slow path, behind a wave-uniform branch.
+// Reduces one complete batch (every id below V) into the lane state and
+// returns its maximum raw logit. The exponentials use the reference of the
+// batches before (it lags the running maximum), so each chunk is reduced as
+// soon as its load lands instead of after a batch-wide maximum; the batch
+// maximum is folded in afterwards. A lag of up to 2^64 cannot overflow fp32;
+// the rare batches that need more go to the slow path, behind a wave-uniform
+// branch.
 template <bool kBf16, int NB>
-__device__ __forceinline__ void fast_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
-                                           int64_t batch_first_id, int64_t id0, int32_t vocab, float c,
-                                           LaneState& st) {
+__device__ __forceinline__ float fast_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
+                                            int64_t id0, int32_t vocab, float c, LaneState& st) {
   constexpr float kMaxLag = 64.0f;
   float bs, bw;
   const float bm = chunked_sums<kBf16, NB>(buf, c, st.ref, bs, bw);
-  // exact argmax bookkeeping: first batch that attains the lane's maximum
-  if (bm > st.m) {
-    st.m = bm;
-    st.search = static_cast<int32_t>(batch_first_id);
-  }
   const float bref = __fmul_rn(bm, c);
   const bool bad = !(bw == bw) || !(bref <= st.ref + kMaxLag);  // NaN, fresh lane, or a big jump
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && bad) {
@@ -301,6 +295,39 @@ __device__ __forceinline__ void fast_batch(const uint4 (&buf)[NB * Geometry<kBf1
   }
   const bool lift = bref > st.ref + kRefSlack;
   if (__builtin_amdgcn_ballot_w64(lift) != 0 && lift) rebase(st, bref);
+  return bm;
+}
+
+// Reduces the batch that crosses V (ids past V masked) and returns its
+// maximum raw logit below V.
+template <bool kBf16, int NB>
+__device__ __forceinline__ float tail_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
+                                            int64_t id0, int32_t vocab, float c, LaneState& st) {
+  float z[NB * kSlotIds];
+  unpack_batch<kBf16, NB>(buf, z);
+  float bm = kNegInf;
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int e = 0; e < kSlotIds; ++e)
+      if (id0 + q * kStripeIds + e < vocab) bm = fmaxf(bm, z[q * 8 + e]);
+  slow_batch<kBf16, NB>(buf, id0, vocab, c, true, st);
+  return bm;
+}
+
+// Logit e (0..7) of stripe s of a batch, as loaded.
+template <bool kBf16, int NB>
+__device__ __forceinline__ float batch_logit(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe], int s,
+                                             int e) {
+  if constexpr (kBf16) {
+    const uint4 q = buf[s];
+    const uint32_t w = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    const uint4 q = buf[2 * s + (e >> 2)];
+    const uint32_t w = (e & 3) == 0 ? q.x : (e & 3) == 1 ? q.y : (e & 3) == 2 ? q.z : q.w;
+    return __uint_as_float(w);
+  }
 }
 
 // Merges partial b into a: entropy sums, argmax (lowest id among equal
@@ -331,135 +358,6 @@ __device__ __forceinline__ void merge_partial(RowPartial& a, const RowPartial& b
   a.ref = r;
 }
 
-// The partial held by lane (lane ^ J).
-template <int J>
-__device__ __forceinline__ RowPartial partial_xor(const RowPartial& p) {
-  RowPartial q;
-  q.s = __longlong_as_double(static_cast<long long>(lane_xor64<J>(static_cast<uint64_t>(__double_as_longlong(p.s)))));
-  q.w = __longlong_as_double(static_cast<long long>(lane_xor64<J>(static_cast<uint64_t>(__double_as_longlong(p.w)))));
-  q.ref = __uint_as_float(lane_xor<J>(__float_as_uint(p.ref)));
-  q.m = __uint_as_float(lane_xor<J>(__float_as_uint(p.m)));
-  q.argmax = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(p.argmax)));
-  q.best = __uint_as_float(lane_xor<J>(__float_as_uint(p.best)));
-  q.bestj = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(p.bestj)));
-  q.sample = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(p.sample)));
-  return q;
-}
-
-// Finishes a wave once its stream ends, while other waves may still be
-// streaming: reduces the lane states to one partial, finds the exact first id
-// of the wave's maximum (the lanes holding it re-read the batch where they
-// first saw it), and draws the in-block sample of the wave's best block (lane
-// k reads the block's 8 ids in stripe k). Both re-reads are issued together,
-// before any dependent work. Returns the partial in every lane.
-template <bool kBf16, int NB>
-__device__ __forceinline__ RowPartial wave_finish(const LaneState& st, __amdgpu_buffer_rsrc_t rsrc,
-                                                  int32_t vocab, float temp, int32_t pos, int32_t step,
-                                                  uint32_t k0, uint32_t k1, int lane) {
-  constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
-  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
-  RowPartial p;
-  p.m = wave_max(st.m);
-  float bscore = st.best;
-  int32_t bj = st.bestj;
-  wave_argmax(bscore, bj);
-  p.best = bscore;
-  p.bestj = bj;
-
-  // loads: this lane's batch if it holds the wave maximum, and stripe `lane`
-  // of the best block (offsets past the resource read nothing)
-  const bool holds_max = p.m != kNegInf && st.m == p.m;
-  uint4 mine[NB * LPS];
-  load_batch<kBf16, NB>(mine, rsrc,
-                        holds_max ? static_cast<uint32_t>(st.search + lane * kSlotIds) * kEB : kPastEnd);
-  const int64_t v0 = static_cast<int64_t>(bj >> 6) * kSgIds + static_cast<int64_t>(lane) * kStripeIds +
-                     (bj & 63) * kSlotIds;
-  const bool block_ok = bscore != kNegInf && v0 < vocab;
-  uint4 blk[LPS];
-#pragma unroll
-  for (int h = 0; h < LPS; ++h) {
-    const uint32_t off = block_ok ? static_cast<uint32_t>(v0 + 4 * h) * kEB : kPastEnd;
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(off), 0, 0);
-    blk[h] = make_uint4(v[0], v[1], v[2], v[3]);
-  }
-
-  // entropy sums (independent of the loads); every block has been folded
-  const float r = wave_max(st.ref);
-  double s = 0.0, w = 0.0;
-  if (st.ref != kNegInf) {
-    const double d = static_cast<double>(st.ref) - static_cast<double>(r);
-    const double f = scale_of(d);
-    s = f * st.s;
-    w = f * (st.w + d * st.s);
-  }
-  p.s = wave_sum(s);
-  p.w = wave_sum(w);
-  p.ref = r;
-  // element Gumbel noise of this lane's 8 block ids: words of (v0>>2) and
-  // (v0>>2)+1 (v0 is a multiple of 8: word e belongs to id v0 + e); it needs
-  // only the block index, so it is formed while the re-reads are in flight
-  const Words4 g0 = philox4x32_10(static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(pos),
-                                  static_cast<uint32_t>(step), kTagElem, k0, k1);
-  const Words4 g1 = philox4x32_10(static_cast<uint32_t>(v0 >> 2) + 1u, static_cast<uint32_t>(pos),
-                                  static_cast<uint32_t>(step), kTagElem, k0, k1);
-  const uint32_t words[8] = {g0.w[0], g0.w[1], g0.w[2], g0.w[3], g1.w[0], g1.w[1], g1.w[2], g1.w[3]};
-  float gum[kSlotIds];
-#pragma unroll
-  for (int e = 0; e < kSlotIds; ++e) gum[e] = gumbel(words[e]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // exact argmax of the wave: lowest id equal to the maximum
-  int32_t cand = 0x7FFFFFFF;
-  if (holds_max) {
-    float z[NB * kSlotIds];
-    unpack_batch<kBf16, NB>(mine, z);
-#pragma unroll
-    for (int k = NB * kSlotIds - 1; k >= 0; --k) {  // ids increase with k
-      const int64_t id = static_cast<int64_t>(st.search) + lane * kSlotIds + (k >> 3) * kStripeIds + (k & 7);
-      if (id < vocab && z[k] == p.m) cand = static_cast<int32_t>(id);
-    }
-  }
-  p.argmax = wave_min_int(cand);
-
-  // in-block resample of the wave's best block: z/T as z * (1/T), within an
-  // ulp of the quotient
-  const float inv_t = 1.0f / temp;
-  float best = kNegInf;
-  int32_t best_id = 0x7FFFFFFF;
-  if (block_ok) {
-    float zb[kSlotIds];
-    if constexpr (kBf16) {
-      const uint32_t w4[4] = {blk[0].x, blk[0].y, blk[0].z, blk[0].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        zb[2 * q] = __uint_as_float(w4[q] << 16);
-        zb[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        zb[4 * h + 0] = __uint_as_float(blk[h].x);
-        zb[4 * h + 1] = __uint_as_float(blk[h].y);
-        zb[4 * h + 2] = __uint_as_float(blk[h].z);
-        zb[4 * h + 3] = __uint_as_float(blk[h].w);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < kSlotIds; ++e) {
-      if (v0 + e < vocab) {
-        const float score = zb[e] * inv_t + gum[e];
-        if (score > best) {  // ids increase with e: strict > keeps the lower
-          best = score;
-          best_id = static_cast<int32_t>(v0 + e);
-        }
-      }
-    }
-  }
-  wave_argmax(best, best_id);
-  p.sample = best_id;
-  return p;
-}
-
 // Writes a row's outputs from its merged partial: H = ln 2 (log2 S - W/S).
 __device__ __forceinline__ void row_output(const StatsArgs& a, int32_t r, const RowPartial& p) {
   const double h = kLn2 * (log2(p.s) - p.w / p.s);
@@ -469,24 +367,61 @@ __device__ __forceinline__ void row_output(const StatsArgs& a, int32_t r, const 
   a.sample[r] = p.sample;
 }
 
-// Merges the eight wave partials in a three-level tree across lanes 0..7 of
-// wave 0 (lane l starts from partial l mod 8); lane 0 returns all eight.
+// Merges the eight wave partials across lanes 0..7 of wave 0 (lane l starts
+// from partial l mod 8; three butterfly steps within each group of 8 lanes);
+// lane 0 returns the merge of all eight. The argmax and the best block travel
+// as 64-bit keys (a maximum decides both the value and the lowest-id tie
+// break), the sample with its block; the entropy sums are rescaled once to the
+// largest reference and then added.
 __device__ __forceinline__ RowPartial merge_waves(const RowPartial* s_part, int lane) {
-  RowPartial p = s_part[lane & (kWaves - 1)];
-  merge_partial(p, partial_xor<4>(p));
-  merge_partial(p, partial_xor<2>(p));
-  merge_partial(p, partial_xor<1>(p));
+  const RowPartial q = s_part[lane & (kWaves - 1)];
+  uint64_t km = argmax_key(q.m, q.argmax);
+  uint64_t kb = argmax_key(q.best, q.bestj);
+  int32_t sample = q.sample;
+  float r = q.ref;
+#define DG_MERGE_STEP(J)                                                               \
+  {                                                                                    \
+    km = max_u64(km, lane_xor64<J>(km));                                               \
+    const uint64_t ob = lane_xor64<J>(kb);                                             \
+    const int32_t os = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(sample))); \
+    const bool take = ob > kb;                                                         \
+    kb = take ? ob : kb;                                                               \
+    sample = take ? os : sample;                                                       \
+    r = max_raw(r, f32_of(lane_xor<J>(u32_of(r))));                                    \
+  }
+  DG_MERGE_STEP(4) DG_MERGE_STEP(2) DG_MERGE_STEP(1)
+#undef DG_MERGE_STEP
+  double s = 0.0, w = 0.0;
+  if (q.ref != kNegInf) {
+    const double d = static_cast<double>(q.ref) - static_cast<double>(r);
+    const double f = scale_of(d);
+    s = f * q.s;
+    w = f * (q.w + d * q.s);
+  }
+#define DG_SUM_STEP(J)                                                                                        \
+  s += __longlong_as_double(static_cast<long long>(lane_xor64<J>(static_cast<uint64_t>(__double_as_longlong(s))))); \
+  w += __longlong_as_double(static_cast<long long>(lane_xor64<J>(static_cast<uint64_t>(__double_as_longlong(w)))));
+  DG_SUM_STEP(4) DG_SUM_STEP(2) DG_SUM_STEP(1)
+#undef DG_SUM_STEP
+  RowPartial p;
+  argmax_unkey(km, p.m, p.argmax);
+  argmax_unkey(kb, p.best, p.bestj);
+  p.sample = sample;
+  p.ref = r;
+  p.s = s;
+  p.w = w;
   return p;
 }
 
-// NB stripes per batch; DEPTH batches in the register ring (DEPTH - 1 in
-// flight while one is reduced).
-template <bool kBf16, int NB, int DEPTH>
+// NB stripes per batch; the register ring holds two blocks.
+template <bool kBf16, int NB>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
-  constexpr int kBatchesPerSg = kStripesPerSg / NB;
-  static_assert(kBatchesPerSg % DEPTH == 0, "the ring must divide a supergroup's batches");
+  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
+  constexpr int kBB = kChunkStripes / NB;  // batches per block
+  static_assert(kChunkStripes % NB == 0, "a block is a whole number of batches");
   __shared__ RowPartial s_part[kWaves];
+  __shared__ __align__(16) uint4 s_blk[kWaves][kChunkStripes * LPS];
 
   const int32_t r = static_cast<int32_t>(blockIdx.x) / a.nsplit;
   const int32_t split = static_cast<int32_t>(blockIdx.x) % a.nsplit;
@@ -495,7 +430,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  // wave index as a scalar, so the batch loop below is uniform control flow
+  // wave index as a scalar, so the block loop below is uniform control flow
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int32_t vocab = a.vocab;
   const char* __restrict__ row =
@@ -506,155 +441,170 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   // bf16 id and one padding id must still be read. Ids past V are masked.
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(row), 0, ((vocab * Geometry<kBf16>::kElemBytes + 15) / 16) * 16, 0x00020000);
-  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
   const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
 
-  const int32_t nsg = (vocab + kSgIds - 1) / kSgIds;
-  const int32_t sg_begin = static_cast<int32_t>((static_cast<int64_t>(split) * nsg) / a.nsplit);
-  const int32_t sg_end = static_cast<int32_t>((static_cast<int64_t>(split + 1) * nsg) / a.nsplit);
-
-  // The two waves sharing a SIMD (w and w + 4) form a pair that streams
-  // supergroups sg_begin + w, + 4, ... in batches of NB stripes. Only the
-  // row's last supergroup can be partial, and it is the pair's last, so the
-  // pair's live batches form a flat range [0, npair): batch b lies in
-  // supergroup sg_of(b) at stripe (b % kBatchesPerSg) * NB. The older wave
-  // takes the first kFirstShare/16 of that range and the younger one the
-  // rest: the SIMD arbiter favours the older wave, and with equal halves the
-  // younger one would stream on alone for the last fifth. A supergroup cut
-  // by the split is closed in two pieces that the pair combines in LDS.
-  // Batches [b_lo, n_fast) of a wave lie wholly below V; the batch that
-  // crosses V, if any, is the pair's last.
-  constexpr int32_t kFirstShare = 10;
-  const int pair = wave & 3;
-  const int second = wave >> 2;
-  const int32_t pair_sgs = (sg_end - sg_begin - pair + 3) / 4;
-  auto sg_of = [&](int32_t b) { return sg_begin + pair + (b / kBatchesPerSg) * 4; };
-  auto first_id = [&](int32_t b) {
-    return static_cast<int64_t>(sg_of(b)) * kSgIds +
-           static_cast<int64_t>(b % kBatchesPerSg) * NB * kStripeIds;
+  // The split's chunks [c_begin, c_end); wave w takes chunks c_begin + w,
+  // c_begin + w + 8, ...: its i-th block. Only the row's last chunk can be
+  // partial.
+  const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
+  const int32_t c_begin = static_cast<int32_t>((static_cast<int64_t>(split) * nchunk) / a.nsplit);
+  const int32_t c_end = static_cast<int32_t>((static_cast<int64_t>(split + 1) * nchunk) / a.nsplit);
+  const int32_t nblk = c_end - c_begin > wave ? (c_end - c_begin - wave + kWaves - 1) / kWaves : 0;
+  auto chunk_of = [&](int32_t i) { return c_begin + wave + kWaves * i; };
+  auto first_id = [&](int32_t i, int t) {
+    return static_cast<int64_t>(chunk_of(i)) * kChunkIds + static_cast<int64_t>(t) * NB * kStripeIds;
   };
-  int32_t npair = 0;
-  if (pair_sgs > 0) {
-    const int64_t last_sg_first = static_cast<int64_t>(sg_begin + pair + (pair_sgs - 1) * 4) * kSgIds;
-    const int64_t left = static_cast<int64_t>(vocab) - last_sg_first;  // > 0
-    const int64_t live_last = (left + NB * kStripeIds - 1) / (NB * kStripeIds);
-    npair = (pair_sgs - 1) * kBatchesPerSg +
-            static_cast<int32_t>(live_last < kBatchesPerSg ? live_last : kBatchesPerSg);
-  }
-  const int32_t psplit = (npair * kFirstShare / 16) / DEPTH * DEPTH;
-  const int32_t b_lo = second ? psplit : 0;
-  const int32_t n = second ? npair : psplit;
-  const int32_t n_fast = (n > b_lo && first_id(n - 1) + NB * kStripeIds > vocab) ? n - 1 : n;
-  const bool cut = psplit % kBatchesPerSg != 0;  // a supergroup is shared by the pair
-  const int32_t sg_cut = cut ? sg_of(psplit) : -1;
-  // Byte offset of batch b for this lane; batches from n_fast on point beyond
-  // the resource, where buffer loads return zero without touching memory, so
-  // every prefetch can be issued unconditionally (a load behind a branch would
-  // make the compiler wait for it before reducing the current batch).
-  auto byte_of = [&](int32_t b) {
-    return b < n_fast ? static_cast<uint32_t>(first_id(b)) * kEB + lane_bytes : kPastEnd;
+  // Byte offset of batch t of block i for this lane; batches of blocks past
+  // the wave's last and batches wholly past V point beyond the resource,
+  // where buffer loads return zero without touching memory, so every load can
+  // be issued unconditionally.
+  auto byte_of = [&](int32_t i, int t) {
+    const int64_t f = first_id(i, t);
+    return i < nblk && f < vocab ? static_cast<uint32_t>(f) * kEB + lane_bytes : kPastEnd;
   };
 
-  // Register ring of DEPTH batches. The first loads go out before the per-canvas scalars are read.
-  uint4 buf[DEPTH][NB * LPS];
+  // The ring: blocks 0 and 1 go out before the per-canvas scalars are read.
+  uint4 buf[2 * kBB][NB * LPS];
 #pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d) load_batch<kBf16, NB>(buf[d], rsrc, byte_of(b_lo + d));
-
-  // pieces of the supergroup each pair cuts, and the pair's arrival counts
-  __shared__ float s_piece_ref[4][2][kWave];
-  __shared__ float s_piece_sb[4][2][kWave];
-  __shared__ uint32_t s_pair_arrivals[4];
-  if (tid < 4) s_pair_arrivals[tid] = 0;
-  __syncthreads();
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h * kBB + t], rsrc, byte_of(h, t));
 
   if (a.active != nullptr && !active_flag(a.active, canvas)) return;
   const float temp = a.temperature[canvas];
   const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
   const float c = kLog2e / temp;
+  const float inv_t = 1.0f / temp;  // z/T as z * (1/T), within an ulp of the quotient
   const uint64_t seed = a.seeds[canvas];
   const uint32_t k0 = static_cast<uint32_t>(seed);
   const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
 
   LaneState st;
-  auto consider = [&](float score, int32_t j) {
-    if (score > st.best || (score == st.best && j < st.bestj)) {
-      st.best = score;
-      st.bestj = j;
-    }
-  };
-  auto block_score = [&](int32_t j, float ref, float sb) {
-    const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
-                                    static_cast<uint32_t>(step), kTagBlock, k0, k1);
-    return ref + __log2f(sb) + kLog2e * gumbel(rw.w[0]);
-  };
-  // A block (this lane's slot across the 64 stripes of a supergroup) ends:
-  // its score is its log-sum-exp plus its Gumbel, and its sums join the row's.
-  // For the supergroup the pair cuts, this wave's piece goes to LDS instead;
-  // the wave of the pair that closes its piece second combines both pieces.
-  auto close_block = [&](int32_t b) {
-    const int32_t sg = sg_of(b);
-    const int32_t j = sg * kSlots + lane;
-    if (sg == sg_cut) {
-      s_piece_ref[pair][second][lane] = st.sb > 0.f ? st.ref : kNegInf;
-      s_piece_sb[pair][second][lane] = st.sb;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      uint32_t prev = 0;
-      if (lane == 0) prev = __hip_atomic_fetch_add(&s_pair_arrivals[pair], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (__builtin_amdgcn_readfirstlane(prev) == 1) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        const float r0 = s_piece_ref[pair][0][lane], r1 = s_piece_ref[pair][1][lane];
-        const float q0 = s_piece_sb[pair][0][lane], q1 = s_piece_sb[pair][1][lane];
-        const float rm = fmaxf(r0, r1);
-        if (rm != kNegInf) {
-          const float sum = (r0 == kNegInf ? 0.f : q0 * __builtin_amdgcn_exp2f(r0 - rm)) +
-                            (r1 == kNegInf ? 0.f : q1 * __builtin_amdgcn_exp2f(r1 - rm));
-          consider(block_score(j, rm, sum), j);
+  // The wave's results so far (uniform): its maximum raw logit and the lowest
+  // id holding it; its best block score, that block, and the sample drawn in it.
+  float wm = kNegInf;
+  int32_t wam = 0x7FFFFFFF;
+  float wbest = kNegInf;
+  int32_t wbestj = 0x7FFFFFFF;
+  int32_t wsample = 0x7FFFFFFF;
+
+  for (int32_t i0 = 0; i0 < nblk; i0 += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int32_t i = i0 + h;
+      if (i < nblk) {
+        // ---- reduce the block's batches (ring half h)
+        float bmax = kNegInf;
+#pragma unroll
+        for (int t = 0; t < kBB; ++t) {
+          const int64_t f = first_id(i, t);
+          if (f + NB * kStripeIds <= vocab)
+            bmax = max_raw(bmax, fast_batch<kBf16, NB>(buf[h * kBB + t], f + lane * kSlotIds, vocab, c, st));
+          else if (f < vocab)
+            bmax = max_raw(bmax, tail_batch<kBf16, NB>(buf[h * kBB + t], f + lane * kSlotIds, vocab, c, st));
         }
+        const int64_t base = first_id(i, 0);  // the chunk's first id
+
+        // ---- argmax: the wave maximum rises. Blocks come in increasing id
+        // order, so an equal later maximum never replaces an earlier one. A
+        // holding lane's first match lies below V: its ids increase with
+        // (stripe, e) and an id below V holds the maximum.
+        if (__builtin_amdgcn_ballot_w64(bmax > wm) != 0) {
+          const float m2 = wave_max(bmax);
+          int32_t cand = 0x7FFFFFFF;
+          if (bmax == m2) {
+            int kf = 0;
+#pragma unroll
+            for (int k = kChunkStripes * kSlotIds - 1; k >= 0; --k) {
+              const int s = k >> 3;
+              kf = batch_logit<kBf16, NB>(buf[h * kBB + s / NB], s % NB, k & 7) == m2 ? k : kf;
+            }
+            cand = static_cast<int32_t>(base + (kf >> 3) * kStripeIds + lane * kSlotIds + (kf & 7));
+          }
+          wm = m2;
+          wam = wave_min_int(cand);
+        }
+
+        // ---- the block ends: its score is its log-sum-exp plus its Gumbel
+        const int32_t j = chunk_of(i) * kSlots + lane;
+        float score = kNegInf;
+        if (st.sb > 0.f) {
+          const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
+                                          static_cast<uint32_t>(step), kTagBlock, k0, k1);
+          score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
+        }
+        st.s += static_cast<double>(st.sb);
+        st.w += static_cast<double>(st.wb);
+        st.sb = 0.f;
+        st.wb = 0.f;
+
+        // ---- a new best block of the wave (blocks in increasing order, so
+        // an equal later score never replaces an earlier one): resample it now.
+        // The winning lane hands its 64 logits to the wave through LDS; lane k
+        // takes id e = k & 7 of stripe k >> 3.
+        if (__builtin_amdgcn_ballot_w64(score > wbest) != 0) {
+          float sc = score;
+          int32_t jj = j;
+          wave_argmax(sc, jj);
+          wbest = sc;
+          wbestj = jj;
+          const int wl = jj & (kSlots - 1);
+          if (lane == wl) {
+#pragma unroll
+            for (int q = 0; q < kChunkStripes * LPS; ++q) s_blk[wave][q] = buf[h * kBB + q / (NB * LPS)][q % (NB * LPS)];
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int sq = lane >> 3, e = lane & 7;
+          uint4 mine[LPS];
+#pragma unroll
+          for (int q = 0; q < LPS; ++q) mine[q] = s_blk[wave][sq * LPS + q];
+          float zv;
+          if constexpr (kBf16) {
+            const uint32_t w = (e >> 1) == 0 ? mine[0].x : (e >> 1) == 1 ? mine[0].y : (e >> 1) == 2 ? mine[0].z : mine[0].w;
+            zv = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          } else {
+            const uint4 v4 = (e >> 2) != 0 ? mine[LPS - 1] : mine[0];
+            zv = __uint_as_float((e & 3) == 0 ? v4.x : (e & 3) == 1 ? v4.y : (e & 3) == 2 ? v4.z : v4.w);
+          }
+          const int64_t id = base + sq * kStripeIds + wl * kSlotIds + e;
+          const Words4 g = philox4x32_10(static_cast<uint32_t>(id >> 2), static_cast<uint32_t>(pos),
+                                         static_cast<uint32_t>(step), kTagElem, k0, k1);
+          const uint32_t gw = (id & 3) == 0 ? g.w[0] : (id & 3) == 1 ? g.w[1] : (id & 3) == 2 ? g.w[2] : g.w[3];
+          float s2 = id < vocab ? zv * inv_t + gumbel(gw) : kNegInf;
+          int32_t id2 = static_cast<int32_t>(id);
+          wave_argmax(s2, id2);
+          wsample = id2;
+        }
+
+        // ---- the ring half now fetches block i + 2
+#pragma unroll
+        for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h * kBB + t], rsrc, byte_of(i + 2, t));
       }
-    } else if (st.sb > 0.f) {
-      consider(block_score(j, st.ref, st.sb), j);
     }
-    st.s += static_cast<double>(st.sb);
-    st.w += static_cast<double>(st.wb);
-    st.sb = 0.f;
-    st.wb = 0.f;
-  };
-
-  // DEPTH divides a supergroup's batch count, so blocks end only after the
-  // last batch of a ring turn.
-  for (int32_t b = b_lo; b < n_fast; b += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      load_batch<kBf16, NB>(buf[(d + DEPTH - 1) % DEPTH], rsrc, byte_of(b + d + DEPTH - 1));
-      if (b + d < n_fast)  // the loop has one exit, so load counters stay exact
-        fast_batch<kBf16, NB>(buf[d], first_id(b + d), first_id(b + d) + lane * kSlotIds, vocab, c, st);
-    }
-    if ((b + DEPTH) % kBatchesPerSg == 0 && b + DEPTH <= n_fast) close_block(b);
   }
-  if (n_fast < n) {
-    // the batch that crosses V: loaded again here (ids past V read as zero and
-    // are masked) and reduced on the slow path
-    uint4 tb[NB * LPS];
-    const int64_t bfirst = first_id(n - 1);
-    load_batch<kBf16, NB>(tb, rsrc, static_cast<uint32_t>(bfirst) * kEB + lane_bytes);
-    float z[NB * kSlotIds];
-    unpack_batch<kBf16, NB>(tb, z);
-    float bm = kNegInf;
-#pragma unroll
-    for (int q = 0; q < NB; ++q)
-#pragma unroll
-      for (int e = 0; e < kSlotIds; ++e)
-        if (bfirst + lane * kSlotIds + q * kStripeIds + e < vocab) bm = fmaxf(bm, z[q * 8 + e]);
-    if (bm > st.m) {
-      st.m = bm;
-      st.search = static_cast<int32_t>(bfirst);
-    }
-    slow_batch<kBf16, NB>(tb, bfirst + lane * kSlotIds, vocab, c, true, st);
-  }
-  if (n > b_lo && (n % kBatchesPerSg != 0 || n_fast < n)) close_block(n - 1);
 
-  const RowPartial wp = wave_finish<kBf16, NB>(st, rsrc, vocab, temp, pos, step, k0, k1, lane);
+  // the wave's partial: sums rescaled to the wave's largest reference
+  RowPartial wp;
+  {
+    const float rr = wave_max(st.ref);
+    double s = 0.0, w = 0.0;
+    if (st.ref != kNegInf) {
+      const double d = static_cast<double>(st.ref) - static_cast<double>(rr);
+      const double f = scale_of(d);
+      s = f * st.s;
+      w = f * (st.w + d * st.s);
+    }
+    wp.s = wave_sum(s);
+    wp.w = wave_sum(w);
+    wp.ref = rr;
+    wp.m = wm;
+    wp.argmax = wam;
+    wp.best = wbest;
+    wp.bestj = wbestj;
+    wp.sample = wsample;
+  }
   if (lane == 0) s_part[wave] = wp;
   __syncthreads();
   if (wave != 0) return;
@@ -680,11 +630,11 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
 }  // namespace
 
 int32_t choose_nsplit(int32_t rows, int32_t vocab) {
-  const int32_t nsg = (vocab + kSgIds - 1) / kSgIds;
+  const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
   // aim for >= 2048 waves in flight (256 CUs x 8), at most one split per
-  // kWaves supergroups so that every wave owns at least one supergroup
+  // kWaves chunks so that every wave of a split owns at least one block
   int32_t want = (2048 / kWaves + rows - 1) / rows;
-  int32_t cap = nsg / kWaves;
+  int32_t cap = nchunk / kWaves;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want > 8) want = 8;
@@ -695,10 +645,11 @@ hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream
   const dim3 grid(static_cast<unsigned>(a.rows) * static_cast<unsigned>(a.nsplit));
   const dim3 block(kStatsThreads);
   if (bf16)
-    hipLaunchKernelGGL((canvas_stats_kernel<true, 2, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((canvas_stats_kernel<true, 4>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((canvas_stats_kernel<false, 2, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((canvas_stats_kernel<false, 4>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace dg
+

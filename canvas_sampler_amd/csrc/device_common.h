@@ -12,15 +12,16 @@ constexpr int kWave = 64;
 
 // Vocabulary geometry of the sampling protocol. A stripe is 512 consecutive
 // ids = 64 slots of 8 ids; one wave64 reads one stripe with one 16-byte load
-// per lane (bf16) so every load is fully coalesced. A supergroup is 64
-// consecutive stripes; block j = 64*supergroup + slot gathers one slot across
-// the 64 stripes, so a lane of a wave streaming a supergroup owns exactly one
-// block and never needs another lane to finish it.
+// per lane (bf16), so every load is fully coalesced. A chunk is 8 consecutive
+// stripes (4096 ids); block j = 64 * chunk + slot gathers one slot across the
+// 8 stripes of its chunk (64 ids), so a lane of a wave streaming a chunk holds
+// exactly one whole block in its registers. For an id v that is
+// j = 64 * (v >> 12) + ((v >> 3) & 63).
 constexpr int kSlotIds = 8;
 constexpr int kSlots = 64;
 constexpr int kStripeIds = kSlotIds * kSlots;        // 512
-constexpr int kStripesPerSg = 64;
-constexpr int kSgIds = kStripeIds * kStripesPerSg;   // 32768
+constexpr int kChunkStripes = 8;
+constexpr int kChunkIds = kStripeIds * kChunkStripes;  // 4096
 
 // Counter word 3 of each random draw.
 constexpr uint32_t kTagInit = 0;
@@ -90,6 +91,13 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
   return r;
 }
 
+// max(a, b) as one v_max_f32, for values that are never NaN (see max3_raw).
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // ---- cross-lane moves and wave64 reductions ----
 // All moves stay in the VALU: DPP within rows of 16 lanes, and gfx950's
 // v_permlane16_swap / v_permlane32_swap across rows and halves. Neither goes
@@ -145,14 +153,15 @@ __device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
 __device__ __forceinline__ float f32_of(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t u32_of(float f) { return __float_as_uint(f); }
 
+// Maximum over the wave of values that are never NaN.
 __device__ __forceinline__ float wave_max(float v) {
-#define DG_STEP(C) v = fmaxf(v, f32_of(dpp_mov<C>(u32_of(v))))
+#define DG_STEP(C) v = max_raw(v, f32_of(dpp_mov<C>(u32_of(v))))
   DG_STEP(kDppXor8); DG_STEP(kDppRor4); DG_STEP(kDppXor2); DG_STEP(kDppXor1);
 #undef DG_STEP
   const auto p = __builtin_amdgcn_permlane16_swap(u32_of(v), u32_of(v), false, false);
-  v = fmaxf(f32_of(p[0]), f32_of(p[1]));
+  v = max_raw(f32_of(p[0]), f32_of(p[1]));
   const auto q = __builtin_amdgcn_permlane32_swap(u32_of(v), u32_of(v), false, false);
-  return fmaxf(f32_of(q[0]), f32_of(q[1]));
+  return max_raw(f32_of(q[0]), f32_of(q[1]));
 }
 
 __device__ __forceinline__ int wave_min_int(int v) {
@@ -193,30 +202,52 @@ __device__ __forceinline__ double wave_sum(double v) {
          __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(qhi[1]) << 32) | qlo[1]));
 }
 
-// (score, index) arg-max over the wave, the lowest index winning exact ties;
-// every lane returns the winner.
-__device__ __forceinline__ void argmax_combine(float& score, int& idx, float s2, int i2) {
-  if (s2 > score || (s2 == score && i2 < idx)) {
-    score = s2;
-    idx = i2;
-  }
+// (score, index) arg-max as one unsigned 64-bit key: the score's bits made
+// order-preserving (both zeros as +0, so equal scores tie) above the
+// complemented index, so that the larger key has the higher score and, among
+// equal scores, the lower index. Indices are non-negative.
+__device__ __forceinline__ uint64_t argmax_key(float score, int idx) {
+  const uint32_t b = score == 0.0f ? 0u : __float_as_uint(score);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~idx);
 }
 
+__device__ __forceinline__ void argmax_unkey(uint64_t key, float& score, int& idx) {
+  const uint32_t ord = static_cast<uint32_t>(key >> 32);
+  score = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+  idx = static_cast<int>(~static_cast<uint32_t>(key));
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int C>
+__device__ __forceinline__ uint64_t dpp_mov_u64(uint64_t v) {
+  const uint32_t lo = dpp_mov<C>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_mov<C>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Largest 64-bit key over the wave; every lane returns it. Branch-free: one
+// 64-bit compare and two selects per step.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = max_u64(k, dpp_mov_u64<kDppXor8>(k));
+  k = max_u64(k, dpp_mov_u64<kDppRor4>(k));
+  k = max_u64(k, dpp_mov_u64<kDppXor2>(k));
+  k = max_u64(k, dpp_mov_u64<kDppXor1>(k));
+  const auto plo = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(k), static_cast<uint32_t>(k), false, false);
+  const auto phi = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(k >> 32), static_cast<uint32_t>(k >> 32),
+                                                    false, false);
+  k = max_u64((static_cast<uint64_t>(phi[0]) << 32) | plo[0], (static_cast<uint64_t>(phi[1]) << 32) | plo[1]);
+  const auto qlo = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(k), static_cast<uint32_t>(k), false, false);
+  const auto qhi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(k >> 32), static_cast<uint32_t>(k >> 32),
+                                                    false, false);
+  return max_u64((static_cast<uint64_t>(qhi[0]) << 32) | qlo[0], (static_cast<uint64_t>(qhi[1]) << 32) | qlo[1]);
+}
+
+// (score, index) arg-max over the wave, the lowest index winning exact ties;
+// every lane returns the winner.
 __device__ __forceinline__ void wave_argmax(float& score, int& idx) {
-#define DG_STEP(C) argmax_combine(score, idx, f32_of(dpp_mov<C>(u32_of(score))), \
-                                  static_cast<int>(dpp_mov<C>(static_cast<uint32_t>(idx))))
-  DG_STEP(kDppXor8); DG_STEP(kDppRor4); DG_STEP(kDppXor2); DG_STEP(kDppXor1);
-#undef DG_STEP
-  const auto ps = __builtin_amdgcn_permlane16_swap(u32_of(score), u32_of(score), false, false);
-  const auto pi = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(idx), static_cast<uint32_t>(idx), false, false);
-  score = f32_of(ps[0]);
-  idx = static_cast<int>(pi[0]);
-  argmax_combine(score, idx, f32_of(ps[1]), static_cast<int>(pi[1]));
-  const auto qs = __builtin_amdgcn_permlane32_swap(u32_of(score), u32_of(score), false, false);
-  const auto qi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(idx), static_cast<uint32_t>(idx), false, false);
-  score = f32_of(qs[0]);
-  idx = static_cast<int>(qi[0]);
-  argmax_combine(score, idx, f32_of(qs[1]), static_cast<int>(qi[1]));
+  argmax_unkey(wave_max_u64(argmax_key(score, idx)), score, idx);
 }
 
 }  // namespace dg

@@ -34,12 +34,14 @@ from .philox import (TAG_BLOCK, TAG_ELEM, TAG_INIT, TAG_RENOISE, gumbel,
                      philox4x32_10, seed_key, uniform_token)
 
 # Vocabulary geometry of the sampling protocol: a stripe is 512 consecutive
-# ids cut into 64 slots of 8; a supergroup is 64 consecutive stripes; a block
-# is one slot taken across the 64 stripes of a supergroup (up to 512 ids).
+# ids cut into 64 slots of 8; a chunk is 8 consecutive stripes; a block is one
+# slot taken across the 8 stripes of a chunk (up to 64 ids). Any partition of
+# the ids into blocks gives an exact sample; this one is the protocol.
 SLOT_IDS = 8
 SLOTS = 64
 STRIPE_IDS = SLOT_IDS * SLOTS        # 512
-SUPERGROUP_IDS = STRIPE_IDS * 64     # 32768
+CHUNK_STRIPES = 8
+CHUNK_IDS = STRIPE_IDS * CHUNK_STRIPES   # 4096
 
 
 # ----------------------------------------------------------------------------
@@ -79,17 +81,17 @@ def argmax_raw(z):
 
 
 def block_index(v):
-    """Block of vocabulary id v: 64 * supergroup + slot."""
+    """Block of vocabulary id v: 64 * chunk + slot."""
     v = np.asarray(v, dtype=np.int64)
-    return SLOTS * (v // SUPERGROUP_IDS) + (v // SLOT_IDS) % SLOTS
+    return SLOTS * (v // CHUNK_IDS) + (v // SLOT_IDS) % SLOTS
 
 
 def block_members(j, vocab):
     """Vocabulary ids of block j in increasing order (ids >= V dropped)."""
-    sg, slot = divmod(int(j), SLOTS)
-    stripe = np.arange(64, dtype=np.int64)[:, None]
+    chunk, slot = divmod(int(j), SLOTS)
+    stripe = np.arange(CHUNK_STRIPES, dtype=np.int64)[:, None]
     elem = np.arange(SLOT_IDS, dtype=np.int64)[None, :]
-    v = (sg * SUPERGROUP_IDS + stripe * STRIPE_IDS + slot * SLOT_IDS + elem).ravel()
+    v = (chunk * CHUNK_IDS + stripe * STRIPE_IDS + slot * SLOT_IDS + elem).ravel()
     return v[v < vocab]
 
 
@@ -97,18 +99,18 @@ def block_logsumexp(x):
     """Log-sum-exp of x (fp64, [rows, V], already divided by T) over every
     block; result [rows, n_blocks] indexed by block number (empty -> -inf)."""
     rows, vocab = x.shape
-    n_sg = -(-vocab // SUPERGROUP_IDS)
-    pad = np.full((rows, n_sg * SUPERGROUP_IDS), -np.inf)
+    n_chunk = -(-vocab // CHUNK_IDS)
+    pad = np.full((rows, n_chunk * CHUNK_IDS), -np.inf)
     pad[:, :vocab] = x
-    # axes: row, supergroup, stripe within supergroup, slot, id within slot
-    xb = pad.reshape(rows, n_sg, 64, SLOTS, SLOT_IDS)
-    m = np.max(xb, axis=(2, 4))                       # [rows, n_sg, slot]
+    # axes: row, chunk, stripe within chunk, slot, id within slot
+    xb = pad.reshape(rows, n_chunk, CHUNK_STRIPES, SLOTS, SLOT_IDS)
+    m = np.max(xb, axis=(2, 4))                       # [rows, n_chunk, slot]
     finite = np.isfinite(m)
     m_safe = np.where(finite, m, 0.0)
     s = np.sum(np.exp(xb - m_safe[:, :, None, :, None]), axis=(2, 4))
     with np.errstate(divide="ignore"):
         lse = np.where(finite, m_safe + np.log(s), -np.inf)
-    return lse.reshape(rows, n_sg * SLOTS)
+    return lse.reshape(rows, n_chunk * SLOTS)
 
 
 def sample_two_level_detail(z, temp, seed, positions, step):

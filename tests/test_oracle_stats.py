@@ -96,23 +96,23 @@ def test_argmax_planted():
 # ------------------------------------------------------ block geometry ------
 @pytest.mark.parametrize("vocab", [1, 7, 100, 512, 4096, 5000, 32768, 40000])
 def test_blocks_partition_the_vocabulary(vocab):
-    n_sg = -(-vocab // O.SUPERGROUP_IDS)
+    n_chunk = -(-vocab // 4096)
     seen = np.zeros(vocab, dtype=int)
-    for j in range(n_sg * O.SLOTS):
+    for j in range(n_chunk * O.SLOTS):
         mem = O.block_members(j, vocab)
         assert np.all(np.diff(mem) > 0)
-        assert len(mem) <= 512
+        assert len(mem) <= 64
         seen[mem] += 1
         assert np.all(O.block_index(mem) == j)
     assert np.all(seen == 1)
 
 
 def test_block_index_brute_force():
-    # block = (supergroup of 32768 ids, position of the 8-id slot in its stripe)
-    for v in list(range(0, 2000)) + [32767, 32768, 32775, 65535, 262143]:
-        sg = v // 32768
+    # block = (chunk of 4096 ids, position of the 8-id slot in its stripe)
+    for v in list(range(0, 5000)) + [8191, 8192, 8199, 32767, 32768, 65535, 262143]:
+        chunk = v // 4096
         slot = (v % 512) // 8
-        assert O.block_index(v) == 64 * sg + slot
+        assert O.block_index(v) == 64 * chunk + slot
 
 
 def test_block_logsumexp_brute_force():
@@ -121,9 +121,9 @@ def test_block_logsumexp_brute_force():
     x = rng.normal(size=(2, vocab)) * 3
     x[1, 40:80] = -np.inf
     lse = O.block_logsumexp(x)
-    assert lse.shape == (2, 128)
+    assert lse.shape == (2, 9 * 64)
     for r in range(2):
-        for j in range(128):
+        for j in range(9 * 64):
             mem = O.block_members(j, vocab)
             if len(mem) == 0:
                 assert lse[r, j] == -np.inf
@@ -143,7 +143,7 @@ def _designed_row(vocab, ids, vals):
 
 @pytest.mark.parametrize("sampler_fn", [O.sample_two_level, O.sample_per_element])
 def test_sample_frequencies_match_softmax(sampler_fn):
-    # mass on ids in different slots, stripes and supergroups
+    # mass on ids in different slots, stripes and chunks
     vocab = 40000
     ids = np.array([3, 9, 700, 701, 4095, 12345, 33000, 39999])
     vals = np.array([0.0, 0.4, -0.3, 1.0, 0.2, -1.0, 0.7, 0.1])
