@@ -33,6 +33,8 @@
 // row split over several workgroups (for very short batches) is merged by
 // the last workgroup to finish (atomic ticket, release/acquire at agent
 // scope).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -413,7 +415,22 @@ __device__ __forceinline__ RowPartial merge_waves(const RowPartial* s_part, int 
   return p;
 }
 
-// NB stripes per batch; the register ring holds two blocks.
+// Logit e (0..7) of stripe s of a block parked in LDS (the lane's 8 stripes,
+// 16 bytes per stripe for bf16, 32 for fp32).
+template <bool kBf16>
+__device__ __forceinline__ float parked_logit(const uint4* blk, int s, int e) {
+  if constexpr (kBf16) {
+    const uint4 v4 = blk[s];
+    const uint32_t w = (e >> 1) == 0 ? v4.x : (e >> 1) == 1 ? v4.y : (e >> 1) == 2 ? v4.z : v4.w;
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    const uint4 v4 = blk[2 * s + (e >> 2)];
+    return __uint_as_float((e & 3) == 0 ? v4.x : (e & 3) == 1 ? v4.y : (e & 3) == 2 ? v4.z : v4.w);
+  }
+}
+
+// NB stripes per batch; the register ring holds two blocks (one in flight
+// while the other is reduced; deeper rings measured slower).
 template <bool kBf16, int NB>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
@@ -421,7 +438,10 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   constexpr int kBB = kChunkStripes / NB;  // batches per block
   static_assert(kChunkStripes % NB == 0, "a block is a whole number of batches");
   __shared__ RowPartial s_part[kWaves];
+  // per wave: the logits of its best block and of the block holding its
+  // maximum (one lane's slot of a chunk each), kept for the end of the pass
   __shared__ __align__(16) uint4 s_blk[kWaves][kChunkStripes * LPS];
+  __shared__ __align__(16) uint4 s_amx[kWaves][kChunkStripes * LPS];
 
   const int32_t r = static_cast<int32_t>(blockIdx.x) / a.nsplit;
   const int32_t split = static_cast<int32_t>(blockIdx.x) % a.nsplit;
@@ -462,13 +482,17 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     const int64_t f = first_id(i, t);
     return i < nblk && f < vocab ? static_cast<uint32_t>(f) * kEB + lane_bytes : kPastEnd;
   };
+  // Blocks [0, nblk_full) lie wholly below V; the block holding V, if any, is
+  // the wave's last and is reduced after the loop.
+  const int32_t nblk_full =
+      (nblk > 0 && first_id(nblk - 1, kBB - 1) + NB * kStripeIds > vocab) ? nblk - 1 : nblk;
 
   // The ring: blocks 0 and 1 go out before the per-canvas scalars are read.
-  uint4 buf[2 * kBB][NB * LPS];
+  uint4 buf[2][kBB][NB * LPS];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h * kBB + t], rsrc, byte_of(h, t));
+    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h][t], rsrc, byte_of(h, t));
 
   if (a.active != nullptr && !active_flag(a.active, canvas)) return;
   const float temp = a.temperature[canvas];
@@ -480,109 +504,147 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
 
   LaneState st;
-  // The wave's results so far (uniform): its maximum raw logit and the lowest
-  // id holding it; its best block score, that block, and the sample drawn in it.
+  // The wave's results so far (uniform): its maximum raw logit; the lowest id
+  // holding it when resolved (am_lane < 0), else the block (first id am_base)
+  // and the one lane holding it, whose logits wait in s_amx; its best block
+  // score and block j, whose winning lane's logits wait in s_blk.
   float wm = kNegInf;
   int32_t wam = 0x7FFFFFFF;
+  int64_t am_base = 0;
+  int32_t am_lane = -1;
   float wbest = kNegInf;
   int32_t wbestj = 0x7FFFFFFF;
-  int32_t wsample = 0x7FFFFFFF;
+  int64_t best_base = 0;
 
-  for (int32_t i0 = 0; i0 < nblk; i0 += 2) {
+  // Block i ends; ring slot H holds its logits (lane: its slot of the
+  // chunk's 8 stripes), bmax is the lane's maximum over them below V.
+  auto close_block = [&](auto slot, int32_t i, float bmax) {
+    constexpr int H = decltype(slot)::value;
+    const int64_t base = first_id(i, 0);  // the chunk's first id
+
+    // ---- argmax: the wave maximum rises. Blocks come in increasing id
+    // order, so an equal later maximum never replaces an earlier one. With
+    // one holding lane, that lane parks its logits and the first id is found
+    // after the pass; with several (exact ties), the first id is found now. A
+    // holding lane's first match lies below V: its ids increase with
+    // (stripe, e) and an id below V holds the maximum.
+    if (__builtin_amdgcn_ballot_w64(bmax > wm) != 0) {
+      const float m2 = wave_max(bmax);
+      const uint64_t holders = __builtin_amdgcn_ballot_w64(bmax == m2);
+      wm = m2;
+      if (__builtin_popcountll(holders) == 1) {
+        am_lane = static_cast<int32_t>(__builtin_ctzll(holders));
+        am_base = base;
+        if (lane == am_lane) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int32_t i = i0 + h;
-      if (i < nblk) {
-        // ---- reduce the block's batches (ring half h)
-        float bmax = kNegInf;
-#pragma unroll
-        for (int t = 0; t < kBB; ++t) {
-          const int64_t f = first_id(i, t);
-          if (f + NB * kStripeIds <= vocab)
-            bmax = max_raw(bmax, fast_batch<kBf16, NB>(buf[h * kBB + t], f + lane * kSlotIds, vocab, c, st));
-          else if (f < vocab)
-            bmax = max_raw(bmax, tail_batch<kBf16, NB>(buf[h * kBB + t], f + lane * kSlotIds, vocab, c, st));
+          for (int q = 0; q < kChunkStripes * LPS; ++q) s_amx[wave][q] = buf[H][q / (NB * LPS)][q % (NB * LPS)];
         }
-        const int64_t base = first_id(i, 0);  // the chunk's first id
-
-        // ---- argmax: the wave maximum rises. Blocks come in increasing id
-        // order, so an equal later maximum never replaces an earlier one. A
-        // holding lane's first match lies below V: its ids increase with
-        // (stripe, e) and an id below V holds the maximum.
-        if (__builtin_amdgcn_ballot_w64(bmax > wm) != 0) {
-          const float m2 = wave_max(bmax);
-          int32_t cand = 0x7FFFFFFF;
-          if (bmax == m2) {
-            int kf = 0;
+      } else {
+        int32_t cand = 0x7FFFFFFF;
+        if (bmax == m2) {
+          int kf = 0;
 #pragma unroll
-            for (int k = kChunkStripes * kSlotIds - 1; k >= 0; --k) {
-              const int s = k >> 3;
-              kf = batch_logit<kBf16, NB>(buf[h * kBB + s / NB], s % NB, k & 7) == m2 ? k : kf;
-            }
-            cand = static_cast<int32_t>(base + (kf >> 3) * kStripeIds + lane * kSlotIds + (kf & 7));
+          for (int k = kChunkStripes * kSlotIds - 1; k >= 0; --k) {
+            const int s = k >> 3;
+            kf = batch_logit<kBf16, NB>(buf[H][s / NB], s % NB, k & 7) == m2 ? k : kf;
           }
-          wm = m2;
-          wam = wave_min_int(cand);
+          cand = static_cast<int32_t>(base + (kf >> 3) * kStripeIds + lane * kSlotIds + (kf & 7));
         }
-
-        // ---- the block ends: its score is its log-sum-exp plus its Gumbel
-        const int32_t j = chunk_of(i) * kSlots + lane;
-        float score = kNegInf;
-        if (st.sb > 0.f) {
-          const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
-                                          static_cast<uint32_t>(step), kTagBlock, k0, k1);
-          score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
-        }
-        st.s += static_cast<double>(st.sb);
-        st.w += static_cast<double>(st.wb);
-        st.sb = 0.f;
-        st.wb = 0.f;
-
-        // ---- a new best block of the wave (blocks in increasing order, so
-        // an equal later score never replaces an earlier one): resample it now.
-        // The winning lane hands its 64 logits to the wave through LDS; lane k
-        // takes id e = k & 7 of stripe k >> 3.
-        if (__builtin_amdgcn_ballot_w64(score > wbest) != 0) {
-          float sc = score;
-          int32_t jj = j;
-          wave_argmax(sc, jj);
-          wbest = sc;
-          wbestj = jj;
-          const int wl = jj & (kSlots - 1);
-          if (lane == wl) {
-#pragma unroll
-            for (int q = 0; q < kChunkStripes * LPS; ++q) s_blk[wave][q] = buf[h * kBB + q / (NB * LPS)][q % (NB * LPS)];
-          }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int sq = lane >> 3, e = lane & 7;
-          uint4 mine[LPS];
-#pragma unroll
-          for (int q = 0; q < LPS; ++q) mine[q] = s_blk[wave][sq * LPS + q];
-          float zv;
-          if constexpr (kBf16) {
-            const uint32_t w = (e >> 1) == 0 ? mine[0].x : (e >> 1) == 1 ? mine[0].y : (e >> 1) == 2 ? mine[0].z : mine[0].w;
-            zv = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-          } else {
-            const uint4 v4 = (e >> 2) != 0 ? mine[LPS - 1] : mine[0];
-            zv = __uint_as_float((e & 3) == 0 ? v4.x : (e & 3) == 1 ? v4.y : (e & 3) == 2 ? v4.z : v4.w);
-          }
-          const int64_t id = base + sq * kStripeIds + wl * kSlotIds + e;
-          const Words4 g = philox4x32_10(static_cast<uint32_t>(id >> 2), static_cast<uint32_t>(pos),
-                                         static_cast<uint32_t>(step), kTagElem, k0, k1);
-          const uint32_t gw = (id & 3) == 0 ? g.w[0] : (id & 3) == 1 ? g.w[1] : (id & 3) == 2 ? g.w[2] : g.w[3];
-          float s2 = id < vocab ? zv * inv_t + gumbel(gw) : kNegInf;
-          int32_t id2 = static_cast<int32_t>(id);
-          wave_argmax(s2, id2);
-          wsample = id2;
-        }
-
-        // ---- the ring half now fetches block i + 2
-#pragma unroll
-        for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h * kBB + t], rsrc, byte_of(i + 2, t));
+        wam = wave_min_int(cand);
+        am_lane = -1;
       }
     }
+
+    // ---- its score is its log-sum-exp plus its Gumbel
+    const int32_t j = chunk_of(i) * kSlots + lane;
+    float score = kNegInf;
+    if (st.sb > 0.f) {
+      const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
+                                      static_cast<uint32_t>(step), kTagBlock, k0, k1);
+      score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
+    }
+    st.s += static_cast<double>(st.sb);
+    st.w += static_cast<double>(st.wb);
+    st.sb = 0.f;
+    st.wb = 0.f;
+
+    // ---- a new best block of the wave (blocks in increasing order, so an
+    // equal later score never replaces an earlier one): its winning lane parks
+    // the block's logits; the sample is drawn in it after the pass.
+    if (__builtin_amdgcn_ballot_w64(score > wbest) != 0) {
+      float sc = score;
+      int32_t jj = j;
+      wave_argmax(sc, jj);
+      wbest = sc;
+      wbestj = jj;
+      best_base = base;
+      if (lane == (jj & (kSlots - 1))) {
+#pragma unroll
+        for (int q = 0; q < kChunkStripes * LPS; ++q) s_blk[wave][q] = buf[H][q / (NB * LPS)][q % (NB * LPS)];
+      }
+    }
+  };
+
+  // Full blocks: reduce, close, and refill the ring slot with block i + 2.
+  auto run_block = [&](auto slot, int32_t i) {
+    constexpr int H = decltype(slot)::value;
+    float bmax = kNegInf;
+#pragma unroll
+    for (int t = 0; t < kBB; ++t)
+      bmax = max_raw(bmax, fast_batch<kBf16, NB>(buf[H][t], first_id(i, t) + lane * kSlotIds, vocab, c, st));
+    close_block(slot, i, bmax);
+#pragma unroll
+    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[H][t], rsrc, byte_of(i + 2, t));
+  };
+  for (int32_t i0 = 0; i0 < nblk_full; i0 += 2) {
+    run_block(std::integral_constant<int, 0>{}, i0);
+    if (i0 + 1 < nblk_full) run_block(std::integral_constant<int, 1>{}, i0 + 1);
+  }
+  if (nblk_full < nblk) {
+    // the block holding V sits in ring slot nblk_full % 2 (moved to slot 0);
+    // batches below V are reduced with ids past V masked, the rest skipped
+    const int32_t i = nblk_full;
+    if (i & 1) {
+#pragma unroll
+      for (int t = 0; t < kBB; ++t)
+#pragma unroll
+        for (int q = 0; q < NB * LPS; ++q) buf[0][t][q] = buf[1][t][q];
+    }
+    float bmax = kNegInf;
+#pragma unroll
+    for (int t = 0; t < kBB; ++t) {
+      const int64_t f = first_id(i, t);
+      if (f < vocab) bmax = fmaxf(bmax, tail_batch<kBf16, NB>(buf[0][t], f + lane * kSlotIds, vocab, c, st));
+    }
+    close_block(std::integral_constant<int, 0>{}, i, bmax);
+  }
+
+  // ---- the parked blocks: lane k takes logit e = k & 7 of stripe k >> 3,
+  // whose ids increase with k
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int sq = lane >> 3, e = lane & 7;
+  if (am_lane >= 0) {
+    const int64_t id = am_base + sq * kStripeIds + am_lane * kSlotIds + e;
+    const bool hit = id < vocab && parked_logit<kBf16>(s_amx[wave], sq, e) == wm;
+    const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);  // never empty: the lane holds wm below V
+    if (hits != 0) {
+      const int k = static_cast<int>(__builtin_ctzll(hits));
+      wam = static_cast<int32_t>(am_base + (k >> 3) * kStripeIds + am_lane * kSlotIds + (k & 7));
+    }
+  }
+  int32_t wsample = 0x7FFFFFFF;
+  if (wbestj != 0x7FFFFFFF) {
+    const int wl = wbestj & (kSlots - 1);
+    const int64_t id = best_base + sq * kStripeIds + wl * kSlotIds + e;
+    const Words4 g = philox4x32_10(static_cast<uint32_t>(id >> 2), static_cast<uint32_t>(pos),
+                                   static_cast<uint32_t>(step), kTagElem, k0, k1);
+    const uint32_t gw = (id & 3) == 0 ? g.w[0] : (id & 3) == 1 ? g.w[1] : (id & 3) == 2 ? g.w[2] : g.w[3];
+    float s2 = id < vocab ? parked_logit<kBf16>(s_blk[wave], sq, e) * inv_t + gumbel(gw) : kNegInf;
+    int32_t id2 = static_cast<int32_t>(id);
+    wave_argmax(s2, id2);
+    wsample = id2;
   }
 
   // the wave's partial: sums rescaled to the wave's largest reference

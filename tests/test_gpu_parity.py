@@ -52,7 +52,12 @@ def test_c1_stats_match_oracle():
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("V", [2, 7, 100, 1000, 4100, 33000, 70001])
+# V relative to the 4096-id chunks of the sampling blocks (a block's 8
+# stripes arrive as two 4-stripe batches): inside the first batch (1000, 4100,
+# 33000, 70001), inside the second (3000, 10340, 39864), on the batch border
+# (6144); the block holding V is a wave's first, second (39864, 33000) or
+# third block (70001, which also splits each row over two workgroups at L=40).
+@pytest.mark.parametrize("V", [2, 7, 100, 1000, 3000, 4100, 6144, 10340, 33000, 39864, 70001])
 def test_ragged_vocab(dtype, V):
     L = 40
     ctx = _ctx(L, V)
