@@ -88,6 +88,9 @@ def sweep_leg(torch, B, synth):
         smp = torch.empty(Bn * L, dtype=torch.int32, device="cuda")
         o = ctx.step_out(canvas)
         stream = torch.cuda.Stream()
+        # the inputs were made on the default stream: let that work finish (and
+        # its freed temporaries stop being in use) before launching on `stream`
+        torch.cuda.synchronize()
 
         def timed(fn):
             with torch.cuda.stream(stream):
@@ -131,6 +134,9 @@ def lmhead_leg(args, torch, B, synth):
     canvas = torch.empty(Bn * L, dtype=torch.int32, device="cuda")
     out = ctx.step_out(canvas)
     stream = torch.cuda.Stream()
+    # the inputs were made on the default stream: let that work finish (and
+    # its freed temporaries stop being in use) before launching on `stream`
+    torch.cuda.synchronize()
     k = max(1, args.lmhead_steps)
 
     def timed(fn):
@@ -217,6 +223,9 @@ def main():
     ent = torch.empty(L, device=dev)
     smp = torch.empty(L, dtype=torch.int32, device=dev)
     stream = torch.cuda.Stream()
+    # the inputs were made on the default stream: let that work finish (and
+    # its freed temporaries stop being in use) before launching on `stream`
+    torch.cuda.synchronize()
 
     def full_step(r):
         out = ctx.step_out(canvas, argmax_out=am[r & 1], stop_out=stop, n_accept_out=nacc)

@@ -429,8 +429,202 @@ __device__ __forceinline__ float parked_logit(const uint4* blk, int s, int e) {
   }
 }
 
-// NB stripes per batch; the register ring holds two blocks (one in flight
-// while the other is reduced; deeper rings measured slower).
+// The wave's results so far (uniform across the wave): its maximum raw logit;
+// the lowest id holding it when resolved (am_lane < 0), else the block (first
+// id am_base) and the one lane holding it, whose logits wait in LDS; its best
+// block score and block j, whose winning lane's logits wait in LDS.
+struct WaveResult {
+  float wm = kNegInf;
+  int32_t wam = 0x7FFFFFFF;
+  int64_t am_base = 0;
+  int32_t am_lane = -1;
+  float wbest = kNegInf;
+  int32_t wbestj = 0x7FFFFFFF;
+  int64_t best_base = 0;
+};
+
+// Per-row constants of a pass.
+struct RowConsts {
+  int32_t pos;      // canvas position (counter word 1)
+  int32_t step;     // counter word 2
+  uint32_t k0, k1;  // Philox key: the canvas seed
+  float c;          // log2(e) / T
+  float inv_t;      // 1 / T: z/T as z * (1/T), within an ulp of the quotient
+};
+
+template <bool kBf16, int NB>
+using Ring = uint4[2][kChunkStripes / NB][NB * Geometry<kBf16>::kLoadsPerStripe];
+
+// Block j (first id base, its 64 logits per lane in ring slot H) ends; bmax
+// is the lane's maximum over them below V.
+template <bool kBf16, int NB, int H>
+__device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t j, float bmax,
+                                            int32_t vocab, const RowConsts& rc, LaneState& st,
+                                            WaveResult& wr, uint4* park_best, uint4* park_max, int lane) {
+  constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
+  // ---- argmax: the wave maximum rises. Blocks come in increasing id order,
+  // so an equal later maximum never replaces an earlier one. With one holding
+  // lane, that lane parks its logits and the first id is found after the pass;
+  // with several (exact ties), the first id is found now. A holding lane's
+  // first match lies below V: its ids increase with (stripe, e) and an id
+  // below V holds the maximum.
+  if (__builtin_amdgcn_ballot_w64(bmax > wr.wm) != 0) {
+    const float m2 = wave_max(bmax);
+    const uint64_t holders = __builtin_amdgcn_ballot_w64(bmax == m2);
+    wr.wm = m2;
+    if (__builtin_popcountll(holders) == 1) {
+      wr.am_lane = static_cast<int32_t>(__builtin_ctzll(holders));
+      wr.am_base = base;
+      if (lane == wr.am_lane) {
+#pragma unroll
+        for (int q = 0; q < kChunkStripes * LPS; ++q) park_max[q] = buf[H][q / (NB * LPS)][q % (NB * LPS)];
+      }
+    } else {
+      int32_t cand = 0x7FFFFFFF;
+      if (bmax == m2) {
+        int kf = 0;
+#pragma unroll
+        for (int k = kChunkStripes * kSlotIds - 1; k >= 0; --k) {
+          const int s = k >> 3;
+          kf = batch_logit<kBf16, NB>(buf[H][s / NB], s % NB, k & 7) == m2 ? k : kf;
+        }
+        cand = static_cast<int32_t>(base + (kf >> 3) * kStripeIds + lane * kSlotIds + (kf & 7));
+      }
+      wr.wam = wave_min_int(cand);
+      wr.am_lane = -1;
+    }
+  }
+
+  // ---- its score is its log-sum-exp plus its Gumbel
+  float score = kNegInf;
+  if (st.sb > 0.f) {
+    const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(rc.pos),
+                                    static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
+    score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
+  }
+  st.s += static_cast<double>(st.sb);
+  st.w += static_cast<double>(st.wb);
+  st.sb = 0.f;
+  st.wb = 0.f;
+
+  // ---- a new best block of the wave (blocks in increasing order, so an equal
+  // later score never replaces an earlier one): its winning lane parks the
+  // block's logits; the sample is drawn in it after the pass.
+  if (__builtin_amdgcn_ballot_w64(score > wr.wbest) != 0) {
+    float sc = score;
+    int32_t jj = j;
+    wave_argmax(sc, jj);
+    wr.wbest = sc;
+    wr.wbestj = jj;
+    wr.best_base = base;
+    if (lane == (jj & (kSlots - 1))) {
+#pragma unroll
+      for (int q = 0; q < kChunkStripes * LPS; ++q) park_best[q] = buf[H][q / (NB * LPS)][q % (NB * LPS)];
+    }
+  }
+}
+
+// The wave's partial once its blocks are done: the parked blocks give the
+// first id of its maximum and the sample inside its best block (lane k takes
+// logit e = k & 7 of stripe k >> 3, whose ids increase with k); the sums are
+// rescaled to the wave's largest reference. Every lane returns it.
+template <bool kBf16>
+__device__ __forceinline__ RowPartial wave_partial(const LaneState& st, const WaveResult& wr, int32_t vocab,
+                                                   const RowConsts& rc, const uint4* park_best,
+                                                   const uint4* park_max, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  RowPartial p;
+  const int sq = lane >> 3, e = lane & 7;
+  p.argmax = wr.wam;
+  if (wr.am_lane >= 0) {
+    const int64_t id = wr.am_base + sq * kStripeIds + wr.am_lane * kSlotIds + e;
+    const bool hit = id < vocab && parked_logit<kBf16>(park_max, sq, e) == wr.wm;
+    const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);  // never empty: the lane holds wm below V
+    if (hits != 0) {
+      const int k = static_cast<int>(__builtin_ctzll(hits));
+      p.argmax = static_cast<int32_t>(wr.am_base + (k >> 3) * kStripeIds + wr.am_lane * kSlotIds + (k & 7));
+    }
+  }
+  p.sample = 0x7FFFFFFF;
+  if (wr.wbestj != 0x7FFFFFFF) {
+    const int wl = wr.wbestj & (kSlots - 1);
+    const int64_t id = wr.best_base + sq * kStripeIds + wl * kSlotIds + e;
+    const Words4 g = philox4x32_10(static_cast<uint32_t>(id >> 2), static_cast<uint32_t>(rc.pos),
+                                   static_cast<uint32_t>(rc.step), kTagElem, rc.k0, rc.k1);
+    const uint32_t gw = (id & 3) == 0 ? g.w[0] : (id & 3) == 1 ? g.w[1] : (id & 3) == 2 ? g.w[2] : g.w[3];
+    float s2 = id < vocab ? parked_logit<kBf16>(park_best, sq, e) * rc.inv_t + gumbel(gw) : kNegInf;
+    int32_t id2 = static_cast<int32_t>(id);
+    wave_argmax(s2, id2);
+    p.sample = id2;
+  }
+  const float rr = wave_max(st.ref);
+  double s = 0.0, w = 0.0;
+  if (st.ref != kNegInf) {
+    const double d = static_cast<double>(st.ref) - static_cast<double>(rr);
+    const double f = scale_of(d);
+    s = f * st.s;
+    w = f * (st.w + d * st.s);
+  }
+  p.s = wave_sum(s);
+  p.w = wave_sum(w);
+  p.ref = rr;
+  p.m = wr.wm;
+  p.best = wr.wbest;
+  p.bestj = wr.wbestj;
+  return p;
+}
+
+// Reduces the kBB batches of a full block in ring slot H; returns the lane's
+// maximum over them.
+template <bool kBf16, int NB, int H>
+__device__ __forceinline__ float reduce_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t vocab, float c,
+                                              LaneState& st, int lane) {
+  float bmax = kNegInf;
+#pragma unroll
+  for (int t = 0; t < kChunkStripes / NB; ++t)
+    bmax = max_raw(bmax, fast_batch<kBf16, NB>(buf[H][t], base + t * NB * kStripeIds + lane * kSlotIds, vocab, c, st));
+  return bmax;
+}
+
+template <bool kBf16, int NB, int H>
+__device__ __forceinline__ void load_block(Ring<kBf16, NB>& buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte0,
+                                           bool live) {
+#pragma unroll
+  for (int t = 0; t < kChunkStripes / NB; ++t)
+    load_batch<kBf16, NB>(buf[H][t], rsrc,
+                          live ? byte0 + static_cast<uint32_t>(t * NB * kStripeIds * Geometry<kBf16>::kElemBytes)
+                               : kPastEnd);
+}
+
+template <bool kBf16>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const StatsArgs& a, int32_t r) {
+  // The resource covers the row rounded up to 16 bytes (inside the row
+  // stride): the range check works per dword, and a dword holding the last
+  // bf16 id and one padding id must still be read. Ids past V are masked.
+  constexpr int kEB = Geometry<kBf16>::kElemBytes;
+  const char* row = static_cast<const char*>(a.logits) + static_cast<int64_t>(r) * a.row_stride * kEB;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), 0, ((a.vocab * kEB + 15) / 16) * 16, 0x00020000);
+}
+
+__device__ __forceinline__ RowConsts row_consts(const StatsArgs& a, int32_t r) {
+  const int32_t canvas = r / a.canvas_len;
+  RowConsts rc;
+  rc.pos = r % a.canvas_len;
+  rc.step = a.steps != nullptr ? a.steps[canvas] : a.step;
+  const float temp = a.temperature[canvas];
+  rc.c = kLog2e / temp;
+  rc.inv_t = 1.0f / temp;
+  const uint64_t seed = a.seeds[canvas];
+  rc.k0 = static_cast<uint32_t>(seed);
+  rc.k1 = static_cast<uint32_t>(seed >> 32);
+  return rc;
+}
+
+// One workgroup per row (or per split of a row). NB stripes per batch; the
+// register ring holds two blocks (one in flight while the other is reduced;
+// deeper rings measured slower).
 template <bool kBf16, int NB>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
@@ -446,21 +640,12 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const int32_t r = static_cast<int32_t>(blockIdx.x) / a.nsplit;
   const int32_t split = static_cast<int32_t>(blockIdx.x) % a.nsplit;
   const int32_t canvas = r / a.canvas_len;
-  const int32_t pos = r % a.canvas_len;
-
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   // wave index as a scalar, so the block loop below is uniform control flow
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int32_t vocab = a.vocab;
-  const char* __restrict__ row =
-      static_cast<const char*>(a.logits) + static_cast<int64_t>(r) * a.row_stride * Geometry<kBf16>::kElemBytes;
-
-  // The resource covers the row rounded up to 16 bytes (inside the row
-  // stride): the range check works per dword, and a dword holding the last
-  // bf16 id and one padding id must still be read. Ids past V are masked.
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(row), 0, ((vocab * Geometry<kBf16>::kElemBytes + 15) / 16) * 16, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc = row_rsrc<kBf16>(a, r);
   const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
 
   // The split's chunks [c_begin, c_end); wave w takes chunks c_begin + w,
@@ -471,130 +656,39 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const int32_t c_end = static_cast<int32_t>((static_cast<int64_t>(split + 1) * nchunk) / a.nsplit);
   const int32_t nblk = c_end - c_begin > wave ? (c_end - c_begin - wave + kWaves - 1) / kWaves : 0;
   auto chunk_of = [&](int32_t i) { return c_begin + wave + kWaves * i; };
-  auto first_id = [&](int32_t i, int t) {
-    return static_cast<int64_t>(chunk_of(i)) * kChunkIds + static_cast<int64_t>(t) * NB * kStripeIds;
-  };
-  // Byte offset of batch t of block i for this lane; batches of blocks past
-  // the wave's last and batches wholly past V point beyond the resource,
-  // where buffer loads return zero without touching memory, so every load can
-  // be issued unconditionally.
-  auto byte_of = [&](int32_t i, int t) {
-    const int64_t f = first_id(i, t);
+  auto base_of = [&](int32_t i) { return static_cast<int64_t>(chunk_of(i)) * kChunkIds; };
+  // Block i's byte offset for this lane; batches wholly past V point beyond
+  // the resource, where buffer loads return zero without touching memory, so
+  // every load can be issued unconditionally.
+  auto batch_byte = [&](int32_t i, int t) {
+    const int64_t f = base_of(i) + t * NB * kStripeIds;
     return i < nblk && f < vocab ? static_cast<uint32_t>(f) * kEB + lane_bytes : kPastEnd;
   };
   // Blocks [0, nblk_full) lie wholly below V; the block holding V, if any, is
   // the wave's last and is reduced after the loop.
   const int32_t nblk_full =
-      (nblk > 0 && first_id(nblk - 1, kBB - 1) + NB * kStripeIds > vocab) ? nblk - 1 : nblk;
+      (nblk > 0 && base_of(nblk - 1) + kChunkIds > vocab) ? nblk - 1 : nblk;
 
   // The ring: blocks 0 and 1 go out before the per-canvas scalars are read.
-  uint4 buf[2][kBB][NB * LPS];
+  Ring<kBf16, NB> buf;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h][t], rsrc, byte_of(h, t));
+    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h][t], rsrc, batch_byte(h, t));
 
   if (a.active != nullptr && !active_flag(a.active, canvas)) return;
-  const float temp = a.temperature[canvas];
-  const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
-  const float c = kLog2e / temp;
-  const float inv_t = 1.0f / temp;  // z/T as z * (1/T), within an ulp of the quotient
-  const uint64_t seed = a.seeds[canvas];
-  const uint32_t k0 = static_cast<uint32_t>(seed);
-  const uint32_t k1 = static_cast<uint32_t>(seed >> 32);
-
+  const RowConsts rc = row_consts(a, r);
   LaneState st;
-  // The wave's results so far (uniform): its maximum raw logit; the lowest id
-  // holding it when resolved (am_lane < 0), else the block (first id am_base)
-  // and the one lane holding it, whose logits wait in s_amx; its best block
-  // score and block j, whose winning lane's logits wait in s_blk.
-  float wm = kNegInf;
-  int32_t wam = 0x7FFFFFFF;
-  int64_t am_base = 0;
-  int32_t am_lane = -1;
-  float wbest = kNegInf;
-  int32_t wbestj = 0x7FFFFFFF;
-  int64_t best_base = 0;
-
-  // Block i ends; ring slot H holds its logits (lane: its slot of the
-  // chunk's 8 stripes), bmax is the lane's maximum over them below V.
-  auto close_block = [&](auto slot, int32_t i, float bmax) {
-    constexpr int H = decltype(slot)::value;
-    const int64_t base = first_id(i, 0);  // the chunk's first id
-
-    // ---- argmax: the wave maximum rises. Blocks come in increasing id
-    // order, so an equal later maximum never replaces an earlier one. With
-    // one holding lane, that lane parks its logits and the first id is found
-    // after the pass; with several (exact ties), the first id is found now. A
-    // holding lane's first match lies below V: its ids increase with
-    // (stripe, e) and an id below V holds the maximum.
-    if (__builtin_amdgcn_ballot_w64(bmax > wm) != 0) {
-      const float m2 = wave_max(bmax);
-      const uint64_t holders = __builtin_amdgcn_ballot_w64(bmax == m2);
-      wm = m2;
-      if (__builtin_popcountll(holders) == 1) {
-        am_lane = static_cast<int32_t>(__builtin_ctzll(holders));
-        am_base = base;
-        if (lane == am_lane) {
-#pragma unroll
-          for (int q = 0; q < kChunkStripes * LPS; ++q) s_amx[wave][q] = buf[H][q / (NB * LPS)][q % (NB * LPS)];
-        }
-      } else {
-        int32_t cand = 0x7FFFFFFF;
-        if (bmax == m2) {
-          int kf = 0;
-#pragma unroll
-          for (int k = kChunkStripes * kSlotIds - 1; k >= 0; --k) {
-            const int s = k >> 3;
-            kf = batch_logit<kBf16, NB>(buf[H][s / NB], s % NB, k & 7) == m2 ? k : kf;
-          }
-          cand = static_cast<int32_t>(base + (kf >> 3) * kStripeIds + lane * kSlotIds + (kf & 7));
-        }
-        wam = wave_min_int(cand);
-        am_lane = -1;
-      }
-    }
-
-    // ---- its score is its log-sum-exp plus its Gumbel
-    const int32_t j = chunk_of(i) * kSlots + lane;
-    float score = kNegInf;
-    if (st.sb > 0.f) {
-      const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(pos),
-                                      static_cast<uint32_t>(step), kTagBlock, k0, k1);
-      score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
-    }
-    st.s += static_cast<double>(st.sb);
-    st.w += static_cast<double>(st.wb);
-    st.sb = 0.f;
-    st.wb = 0.f;
-
-    // ---- a new best block of the wave (blocks in increasing order, so an
-    // equal later score never replaces an earlier one): its winning lane parks
-    // the block's logits; the sample is drawn in it after the pass.
-    if (__builtin_amdgcn_ballot_w64(score > wbest) != 0) {
-      float sc = score;
-      int32_t jj = j;
-      wave_argmax(sc, jj);
-      wbest = sc;
-      wbestj = jj;
-      best_base = base;
-      if (lane == (jj & (kSlots - 1))) {
-#pragma unroll
-        for (int q = 0; q < kChunkStripes * LPS; ++q) s_blk[wave][q] = buf[H][q / (NB * LPS)][q % (NB * LPS)];
-      }
-    }
-  };
+  WaveResult wr;
 
   // Full blocks: reduce, close, and refill the ring slot with block i + 2.
   auto run_block = [&](auto slot, int32_t i) {
     constexpr int H = decltype(slot)::value;
-    float bmax = kNegInf;
+    const float bmax = reduce_block<kBf16, NB, H>(buf, base_of(i), vocab, rc.c, st, lane);
+    close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, vocab, rc, st, wr,
+                              s_blk[wave], s_amx[wave], lane);
 #pragma unroll
-    for (int t = 0; t < kBB; ++t)
-      bmax = max_raw(bmax, fast_batch<kBf16, NB>(buf[H][t], first_id(i, t) + lane * kSlotIds, vocab, c, st));
-    close_block(slot, i, bmax);
-#pragma unroll
-    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[H][t], rsrc, byte_of(i + 2, t));
+    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[H][t], rsrc, batch_byte(i + 2, t));
   };
   for (int32_t i0 = 0; i0 < nblk_full; i0 += 2) {
     run_block(std::integral_constant<int, 0>{}, i0);
@@ -613,60 +707,14 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
     float bmax = kNegInf;
 #pragma unroll
     for (int t = 0; t < kBB; ++t) {
-      const int64_t f = first_id(i, t);
-      if (f < vocab) bmax = fmaxf(bmax, tail_batch<kBf16, NB>(buf[0][t], f + lane * kSlotIds, vocab, c, st));
+      const int64_t f = base_of(i) + t * NB * kStripeIds;
+      if (f < vocab) bmax = fmaxf(bmax, tail_batch<kBf16, NB>(buf[0][t], f + lane * kSlotIds, vocab, rc.c, st));
     }
-    close_block(std::integral_constant<int, 0>{}, i, bmax);
+    close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, vocab, rc, st, wr,
+                              s_blk[wave], s_amx[wave], lane);
   }
 
-  // ---- the parked blocks: lane k takes logit e = k & 7 of stripe k >> 3,
-  // whose ids increase with k
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int sq = lane >> 3, e = lane & 7;
-  if (am_lane >= 0) {
-    const int64_t id = am_base + sq * kStripeIds + am_lane * kSlotIds + e;
-    const bool hit = id < vocab && parked_logit<kBf16>(s_amx[wave], sq, e) == wm;
-    const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);  // never empty: the lane holds wm below V
-    if (hits != 0) {
-      const int k = static_cast<int>(__builtin_ctzll(hits));
-      wam = static_cast<int32_t>(am_base + (k >> 3) * kStripeIds + am_lane * kSlotIds + (k & 7));
-    }
-  }
-  int32_t wsample = 0x7FFFFFFF;
-  if (wbestj != 0x7FFFFFFF) {
-    const int wl = wbestj & (kSlots - 1);
-    const int64_t id = best_base + sq * kStripeIds + wl * kSlotIds + e;
-    const Words4 g = philox4x32_10(static_cast<uint32_t>(id >> 2), static_cast<uint32_t>(pos),
-                                   static_cast<uint32_t>(step), kTagElem, k0, k1);
-    const uint32_t gw = (id & 3) == 0 ? g.w[0] : (id & 3) == 1 ? g.w[1] : (id & 3) == 2 ? g.w[2] : g.w[3];
-    float s2 = id < vocab ? parked_logit<kBf16>(s_blk[wave], sq, e) * inv_t + gumbel(gw) : kNegInf;
-    int32_t id2 = static_cast<int32_t>(id);
-    wave_argmax(s2, id2);
-    wsample = id2;
-  }
-
-  // the wave's partial: sums rescaled to the wave's largest reference
-  RowPartial wp;
-  {
-    const float rr = wave_max(st.ref);
-    double s = 0.0, w = 0.0;
-    if (st.ref != kNegInf) {
-      const double d = static_cast<double>(st.ref) - static_cast<double>(rr);
-      const double f = scale_of(d);
-      s = f * st.s;
-      w = f * (st.w + d * st.s);
-    }
-    wp.s = wave_sum(s);
-    wp.w = wave_sum(w);
-    wp.ref = rr;
-    wp.m = wm;
-    wp.argmax = wam;
-    wp.best = wbest;
-    wp.bestj = wbestj;
-    wp.sample = wsample;
-  }
+  const RowPartial wp = wave_partial<kBf16>(st, wr, vocab, rc, s_blk[wave], s_amx[wave], lane);
   if (lane == 0) s_part[wave] = wp;
   __syncthreads();
   if (wave != 0) return;
@@ -689,6 +737,82 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   row_output(a, r, p);
 }
 
+// Row loop: a persistent grid of workgroups, workgroup b taking rows b,
+// b + grid, ... (V a multiple of 4096, one workgroup per row, no active
+// mask). Each wave's blocks of all its rows form one sequence g = 0, 1, ...;
+// the ring refills slot g % 2 with block g + 2 even when that block belongs
+// to the next row, so a row's finish and merge overlap the next row's loads.
+template <bool kBf16, int NB>
+__global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsArgs a) {
+  constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
+  constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
+  __shared__ RowPartial s_part[2][kWaves];  // by row parity
+  __shared__ __align__(16) uint4 s_blk[kWaves][kChunkStripes * LPS];
+  __shared__ __align__(16) uint4 s_amx[kWaves][kChunkStripes * LPS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int32_t vocab = a.vocab;
+  const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
+  const int32_t grid = static_cast<int32_t>(gridDim.x);
+  const int32_t first_row = static_cast<int32_t>(blockIdx.x);
+  const int32_t my_rows = (a.rows - first_row + grid - 1) / grid;  // >= 1
+  const int32_t nchunk = vocab / kChunkIds;
+  const int32_t nblk = nchunk > wave ? (nchunk - wave + kWaves - 1) / kWaves : 0;  // per row
+  const int64_t total = static_cast<int64_t>(my_rows) * nblk;
+
+  // Block g of the wave's sequence is block g % nblk (chunk wave + 8 (g % nblk))
+  // of row first_row + (g / nblk) * grid; past the sequence, loads read nothing.
+  Ring<kBf16, NB> buf;
+  auto fetch = [&](auto slot, int64_t g) {
+    constexpr int H = decltype(slot)::value;
+    int32_t r = first_row;
+    uint32_t byte0 = 0;
+    const bool live = g < total;
+    if (live) {
+      r = first_row + static_cast<int32_t>(g / nblk) * grid;
+      byte0 = static_cast<uint32_t>(wave + kWaves * static_cast<int32_t>(g % nblk)) * (kChunkIds * kEB) + lane_bytes;
+    }
+    load_block<kBf16, NB, H>(buf, row_rsrc<kBf16>(a, r), byte0, live);
+  };
+  fetch(std::integral_constant<int, 0>{}, 0);
+  fetch(std::integral_constant<int, 1>{}, 1);
+
+  int64_t g = 0;
+  for (int32_t k = 0; k < my_rows; ++k) {
+    const int32_t r = first_row + k * grid;
+    const RowConsts rc = row_consts(a, r);
+    LaneState st;
+    WaveResult wr;
+    auto run_block = [&](auto slot, int32_t i) {
+      constexpr int H = decltype(slot)::value;
+      const int64_t base = static_cast<int64_t>(wave + kWaves * i) * kChunkIds;
+      const float bmax = reduce_block<kBf16, NB, H>(buf, base, vocab, rc.c, st, lane);
+      close_block<kBf16, NB, H>(buf, base, (wave + kWaves * i) * kSlots + lane, bmax, vocab, rc, st, wr,
+                                s_blk[wave], s_amx[wave], lane);
+      fetch(slot, g + 2);
+    };
+    for (int32_t i = 0; i < nblk; ++i, ++g) {
+      if ((g & 1) == 0)
+        run_block(std::integral_constant<int, 0>{}, i);
+      else
+        run_block(std::integral_constant<int, 1>{}, i);
+    }
+    const RowPartial wp = wave_partial<kBf16>(st, wr, vocab, rc, s_blk[wave], s_amx[wave], lane);
+    if (lane == 0) s_part[k & 1][wave] = wp;
+    __syncthreads();
+    // the merge of row k falls to wave k mod 8; the other waves go on. The
+    // partials are double-buffered by row parity: row k + 2 writes them only
+    // after the barrier of row k + 1, which the merging wave reaches after
+    // its merge.
+    if (wave == (k & (kWaves - 1))) {
+      const RowPartial p = merge_waves(s_part[k & 1], lane);
+      if (lane == 0) row_output(a, r, p);
+    }
+  }
+}
+
 }  // namespace
 
 int32_t choose_nsplit(int32_t rows, int32_t vocab) {
@@ -703,9 +827,25 @@ int32_t choose_nsplit(int32_t rows, int32_t vocab) {
   return want < 1 ? 1 : want;
 }
 
+int32_t stats_row_grid(int32_t rows, int32_t vocab, int32_t nsplit, bool has_active, int32_t cu_count) {
+  // the row loop needs whole chunks, one workgroup per row and every row to be
+  // processed; it pays off once there are more rows than resident workgroups
+  // (one per CU at this kernel's register use)
+  if (nsplit != 1 || has_active || vocab % kChunkIds != 0 || cu_count < 1 || rows <= cu_count) return 0;
+  return cu_count;
+}
+
 hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(a.rows) * static_cast<unsigned>(a.nsplit));
   const dim3 block(kStatsThreads);
+  if (a.row_grid > 0) {
+    const dim3 grid(static_cast<unsigned>(a.row_grid));
+    if (bf16)
+      hipLaunchKernelGGL((canvas_stats_rows_kernel<true, 4>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((canvas_stats_rows_kernel<false, 4>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>(a.rows) * static_cast<unsigned>(a.nsplit));
   if (bf16)
     hipLaunchKernelGGL((canvas_stats_kernel<true, 4>), grid, block, 0, stream, a);
   else

@@ -19,6 +19,7 @@ struct dg_ctx {
   dg_params p{};
   int32_t nsplit_override = 0;
   int32_t nsplit_max = 8;
+  int32_t cu_count = 0;                 // compute units of the device
   // device scratch
   dg::RowPartial* partials = nullptr;   // [max_rows * nsplit_max]
   uint32_t* tickets = nullptr;          // [max_rows], zero between launches
@@ -163,6 +164,7 @@ dg::StatsArgs stats_args(const dg_ctx* ctx, int32_t B, const void* logits, int64
   a.sample = sample;
   a.partials = ctx->partials;
   a.tickets = ctx->tickets;
+  a.row_grid = dg::stats_row_grid(a.rows, a.vocab, a.nsplit, active != nullptr, ctx->cu_count);
   return a;
 }
 
@@ -363,6 +365,8 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
 
   dg_ctx* c = new dg_ctx();
   c->device = device;
+  if (hipDeviceGetAttribute(&c->cu_count, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    c->cu_count = 0;  // no row loop
   c->max_batch = max_batch;
   c->p = *params;
   const size_t rows = static_cast<size_t>(max_batch) * params->canvas_len;

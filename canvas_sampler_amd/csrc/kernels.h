@@ -65,6 +65,7 @@ struct StatsArgs {
   int32_t* sample;
   RowPartial* partials;    // [rows * nsplit] when nsplit > 1
   uint32_t* tickets;       // [rows], zero between launches
+  int32_t row_grid;        // > 0: a persistent grid of this many workgroups loops over the rows
 };
 
 // LM-head projection: logits[r, v] = sum_k hidden[r, k] * weight[k, v].
@@ -85,6 +86,9 @@ constexpr int kAcceptThreads = 256;
 
 // Chooses the number of workgroups per row for `rows` rows of `vocab` ids.
 int32_t choose_nsplit(int32_t rows, int32_t vocab);
+// Workgroups of the persistent row loop for this launch, or 0 for one
+// workgroup per row (or split).
+int32_t stats_row_grid(int32_t rows, int32_t vocab, int32_t nsplit, bool has_active, int32_t cu_count);
 
 hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_renoise(const AcceptArgs& a, int32_t batch, hipStream_t stream);

@@ -69,6 +69,35 @@ def test_ragged_vocab(dtype, V):
     compare_stats(host_values(z), np.float32(0.7), V * 31 + 5, np.arange(L), 3, h, am, smp)
 
 
+# Shapes that take the persistent row loop (more rows than compute units, V a
+# multiple of 4096, no active mask): each workgroup handles rows b, b + grid,
+# ..., and the register ring runs on into the next row. Rows are sampled at
+# workgroup and loop-iteration borders.
+@pytest.mark.parametrize("dtype,L,Bn,V", [
+    (torch.bfloat16, 256, 4, 262144),  # four rows per workgroup
+    (torch.float32, 150, 2, 12288),    # three chunks per row (waves 3-7 idle); rows not a multiple of the grid
+    (torch.bfloat16, 100, 3, 4096),    # one chunk per row: the ring slot alternates from row to row
+])
+def test_row_loop_matches_oracle(dtype, L, Bn, V):
+    ctx = _ctx(L, V, max_batch=Bn)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = Bn * L
+    assert rows > cu
+    zs = [synth.margin_logits(900 + c, L, V, m_max=4.0, dtype=dtype, device="cuda") for c in range(Bn)]
+    z = torch.cat(zs)
+    temps = [0.8, 0.5, 1.3, 0.7][:Bn]
+    seeds = [11, 2**40 + 3, 7, 99][:Bn]
+    h, am, smp = _stats(ctx, z, temps, seeds, 4, Bn)
+    pick = {0, 1, cu - 1, cu, cu + 1, rows - 2, rows - 1} | set(range(0, rows, 97))
+    pick |= {min(2 * cu - 1, rows - 1), min(2 * cu, rows - 1)}
+    for c in range(Bn):
+        sel = sorted(r for r in pick if c * L <= r < (c + 1) * L)
+        if not sel:
+            continue
+        compare_stats(host_values(z[sel]), np.float32(temps[c]), seeds[c], np.array(sel) - c * L, 4,
+                      h[sel], am[sel], smp[sel])
+
+
 def test_row_stride_padding_is_ignored():
     L, V = 32, 4096
     ctx = _ctx(L, V)
