@@ -12,8 +12,8 @@
 //   - one multinomial sample (§2 item 5) by the two-level Gumbel-max protocol:
 //     a block is one 8-id slot across the 8 stripes of a 4096-id chunk; each
 //     lane forms its block's log-sum-exp on the fly and adds the block's
-//     Gumbel, and the sample is the id of the best block j* with the largest
-//     z/T + element Gumbel.
+//     Gumbel (one Philox call per four blocks), and the sample is the id of
+//     the best block j* with the largest z/T + element Gumbel.
 //
 // Layout and schedule (gfx950, wave64): rows are V-contiguous. A workgroup of
 // eight waves handles a row (or one split of it); wave w takes the split's
@@ -23,16 +23,17 @@
 // and a register ring holds two blocks: one is reduced while the other is in
 // flight. Loads are raw buffer loads on a per-row resource (hardware range
 // check, no branches), marked non-temporal. Per element the loop costs one
-// convert, half a max, one fma, one v_exp_f32, one add and one fma; per block
-// (64 ids per lane) one Philox draw. When a block ends its logits are still
-// in registers, so nothing is read twice: if the block beats the wave's best
-// block, the wave resamples it on the spot (the winning lane hands its 64
-// logits to the wave through LDS), and if a lane's block holds a new wave
-// maximum, the lane finds its first id on the spot. After the stream each
-// wave folds its sums, and the workgroup merges eight 40-byte partials. A
-// row split over several workgroups (for very short batches) is merged by
-// the last workgroup to finish (atomic ticket, release/acquire at agent
-// scope).
+// convert, half a max, one fma, one v_exp_f32, one add and one fma; per four
+// blocks (256 ids per lane) one Philox call. When a block ends its logits are
+// still in registers, so nothing is read twice: if the block beats the wave's
+// best block, or a lane of it holds a new wave maximum, that lane parks the
+// block's 64 logits in LDS, and after its stream the wave draws the sample in
+// its best block and finds the first id of its maximum from the parked
+// logits. The workgroup then merges eight 40-byte partials. With more rows
+// than compute units a persistent grid loops over the rows, and the register
+// ring runs on into the next row. A row split over several workgroups (for
+// very short batches) is merged by the last workgroup to finish (atomic
+// ticket, release/acquire at agent scope).
 #include <type_traits>
 
 #include "device_common.h"
@@ -443,6 +444,19 @@ struct WaveResult {
   int64_t best_base = 0;
 };
 
+// The Philox call behind the Gumbels of the lane's current group of four
+// blocks: blocks that differ only in bits 9-10 of j (chunks 8 apart, so four
+// consecutive blocks of a wave whose first chunk is a multiple of 32 chunks
+// away from the split's start) share the call with counter c0 = j with those
+// bits cleared, block j taking word (j >> 9) & 3. The words are kept as a
+// shift register: the wave's block i takes w0 (a call at i % 4 == 0 refills
+// it), so no word is picked by a runtime index.
+constexpr int32_t kDrawGroupChunks = 32;  // chunks spanned by one group of four block draws
+
+struct BlockWords {
+  uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+};
+
 // Per-row constants of a pass.
 struct RowConsts {
   int32_t pos;      // canvas position (counter word 1)
@@ -458,9 +472,10 @@ using Ring = uint4[2][kChunkStripes / NB][NB * Geometry<kBf16>::kLoadsPerStripe]
 // Block j (first id base, its 64 logits per lane in ring slot H) ends; bmax
 // is the lane's maximum over them below V.
 template <bool kBf16, int NB, int H>
-__device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t j, float bmax,
-                                            int32_t vocab, const RowConsts& rc, LaneState& st,
-                                            WaveResult& wr, uint4* park_best, uint4* park_max, int lane) {
+__device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t j, int32_t i,
+                                            float bmax, int32_t vocab, const RowConsts& rc, LaneState& st,
+                                            WaveResult& wr, BlockWords& bw, uint4* park_best, uint4* park_max,
+                                            int lane) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
   // ---- argmax: the wave maximum rises. Blocks come in increasing id order,
   // so an equal later maximum never replaces an earlier one. With one holding
@@ -496,12 +511,20 @@ __device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t 
   }
 
   // ---- its score is its log-sum-exp plus its Gumbel
-  float score = kNegInf;
-  if (st.sb > 0.f) {
+  if ((i & 3) == 0) {  // (j >> 9) & 3 == 0
     const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(rc.pos),
                                     static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
-    score = st.ref + __log2f(st.sb) + kLog2e * gumbel(rw.w[0]);
+    bw.w0 = rw.w[0];
+    bw.w1 = rw.w[1];
+    bw.w2 = rw.w[2];
+    bw.w3 = rw.w[3];
   }
+  const uint32_t word = bw.w0;
+  bw.w0 = bw.w1;
+  bw.w1 = bw.w2;
+  bw.w2 = bw.w3;
+  float score = kNegInf;
+  if (st.sb > 0.f) score = st.ref + __log2f(st.sb) + kLog2e * gumbel(word);
   st.s += static_cast<double>(st.sb);
   st.w += static_cast<double>(st.wb);
   st.sb = 0.f;
@@ -648,12 +671,15 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const __amdgpu_buffer_rsrc_t rsrc = row_rsrc<kBf16>(a, r);
   const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
 
-  // The split's chunks [c_begin, c_end); wave w takes chunks c_begin + w,
-  // c_begin + w + 8, ...: its i-th block. Only the row's last chunk can be
-  // partial.
+  // The split's chunks [c_begin, c_end), split at multiples of 32 chunks so
+  // that the block draws' groups of four stay within a split; wave w takes
+  // chunks c_begin + w, c_begin + w + 8, ...: its i-th block. Only the row's
+  // last chunk can be partial.
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
-  const int32_t c_begin = static_cast<int32_t>((static_cast<int64_t>(split) * nchunk) / a.nsplit);
-  const int32_t c_end = static_cast<int32_t>((static_cast<int64_t>(split + 1) * nchunk) / a.nsplit);
+  const int32_t ngroup = (nchunk + kDrawGroupChunks - 1) / kDrawGroupChunks;
+  const int32_t c_begin = static_cast<int32_t>((static_cast<int64_t>(split) * ngroup) / a.nsplit) * kDrawGroupChunks;
+  const int32_t c_end = min(static_cast<int32_t>((static_cast<int64_t>(split + 1) * ngroup) / a.nsplit) *
+                            kDrawGroupChunks, nchunk);
   const int32_t nblk = c_end - c_begin > wave ? (c_end - c_begin - wave + kWaves - 1) / kWaves : 0;
   auto chunk_of = [&](int32_t i) { return c_begin + wave + kWaves * i; };
   auto base_of = [&](int32_t i) { return static_cast<int64_t>(chunk_of(i)) * kChunkIds; };
@@ -680,12 +706,13 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const RowConsts rc = row_consts(a, r);
   LaneState st;
   WaveResult wr;
+  BlockWords bw;
 
   // Full blocks: reduce, close, and refill the ring slot with block i + 2.
   auto run_block = [&](auto slot, int32_t i) {
     constexpr int H = decltype(slot)::value;
     const float bmax = reduce_block<kBf16, NB, H>(buf, base_of(i), vocab, rc.c, st, lane);
-    close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, vocab, rc, st, wr,
+    close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, i, bmax, vocab, rc, st, wr, bw,
                               s_blk[wave], s_amx[wave], lane);
 #pragma unroll
     for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[H][t], rsrc, batch_byte(i + 2, t));
@@ -710,7 +737,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
       const int64_t f = base_of(i) + t * NB * kStripeIds;
       if (f < vocab) bmax = fmaxf(bmax, tail_batch<kBf16, NB>(buf[0][t], f + lane * kSlotIds, vocab, rc.c, st));
     }
-    close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, vocab, rc, st, wr,
+    close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, i, bmax, vocab, rc, st, wr, bw,
                               s_blk[wave], s_amx[wave], lane);
   }
 
@@ -785,11 +812,12 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
     const RowConsts rc = row_consts(a, r);
     LaneState st;
     WaveResult wr;
+    BlockWords bw;
     auto run_block = [&](auto slot, int32_t i) {
       constexpr int H = decltype(slot)::value;
       const int64_t base = static_cast<int64_t>(wave + kWaves * i) * kChunkIds;
       const float bmax = reduce_block<kBf16, NB, H>(buf, base, vocab, rc.c, st, lane);
-      close_block<kBf16, NB, H>(buf, base, (wave + kWaves * i) * kSlots + lane, bmax, vocab, rc, st, wr,
+      close_block<kBf16, NB, H>(buf, base, (wave + kWaves * i) * kSlots + lane, i, bmax, vocab, rc, st, wr, bw,
                                 s_blk[wave], s_amx[wave], lane);
       fetch(slot, g + 2);
     };
@@ -817,10 +845,11 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
 
 int32_t choose_nsplit(int32_t rows, int32_t vocab) {
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
-  // aim for >= 2048 waves in flight (256 CUs x 8), at most one split per
-  // kWaves chunks so that every wave of a split owns at least one block
+  // aim for >= 2048 waves in flight (256 CUs x 8), at most one split per 32
+  // chunks: splits start at multiples of 32 chunks, where the groups of four
+  // block draws start
   int32_t want = (2048 / kWaves + rows - 1) / rows;
-  int32_t cap = nchunk / kWaves;
+  int32_t cap = nchunk / kDrawGroupChunks;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want > 8) want = 8;

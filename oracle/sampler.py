@@ -95,6 +95,15 @@ def block_members(j, vocab):
     return v[v < vocab]
 
 
+def block_word(j, pos, step, k0, k1):
+    """Random word of block j's Gumbel: one Philox call serves the four blocks
+    that differ only in bits 9-10 of j (chunks 8 apart), block j taking word
+    (j >> 9) & 3 of the call with counter c0 = j with those bits cleared."""
+    j = np.asarray(j, dtype=np.int64)
+    words = philox4x32_10(j & ~0x600, pos, step, TAG_BLOCK, k0, k1)
+    return np.choose((j >> 9) & 3, words)
+
+
 def block_logsumexp(x):
     """Log-sum-exp of x (fp64, [rows, V], already divided by T) over every
     block; result [rows, n_blocks] indexed by block number (empty -> -inf)."""
@@ -130,8 +139,7 @@ def sample_two_level_detail(z, temp, seed, positions, step):
     n_blocks = lse.shape[1]
     j = np.arange(n_blocks, dtype=np.int64)[None, :]
     pos = np.asarray(positions, dtype=np.int64)[:, None]
-    w0 = philox4x32_10(j, pos, step, TAG_BLOCK, k0, k1)[0]
-    block_score = lse + gumbel(w0)
+    block_score = lse + gumbel(block_word(j, pos, step, k0, k1))
     j_star = np.argmax(block_score, axis=1)
     out = np.empty(rows, dtype=np.int64)
     detail = np.full((4, rows), np.inf)

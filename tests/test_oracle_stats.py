@@ -282,3 +282,19 @@ def test_stop_truth_table():
     assert O.stop_test(a, b, 0.001, 0.005) is False             # argmax changed
     assert O.stop_test(a, a.copy(), 0.01, 0.005) is False       # not confident
     assert O.stop_test(a, a.copy(), float(np.float32(0.005)), np.float32(0.005)) is False  # strict
+
+
+def test_block_words_are_distinct_draws():
+    # four blocks share a Philox call, each taking its own word: no two
+    # blocks of a row may end up with the same (counter, word) pair, and the
+    # words match the Philox outputs of that counter
+    j = np.arange(8192, dtype=np.int64)
+    pairs = set(zip((j & ~0x600).tolist(), ((j >> 9) & 3).tolist()))
+    assert len(pairs) == len(j)
+    w = O.block_word(j, 5, 3, 11, 22)
+    for q in range(4):
+        sel = j[((j >> 9) & 3) == q]
+        ref = philox.philox4x32_10(sel & ~0x600, 5, 3, philox.TAG_BLOCK, 11, 22)[q]
+        assert np.array_equal(w[sel], ref)
+    # distinct blocks get distinct words (collisions among 8192 32-bit words are unlikely)
+    assert len(np.unique(w)) > 8180
