@@ -119,6 +119,56 @@ def sweep_leg(torch, B, synth):
     return out
 
 
+def exp_b_leg(torch, B, synth):
+    """The confidence-growth and entropy-bound sweeps of the pages' EXP B on
+    the single-canvas workload (256 x 262144 bf16 sharpening logits, T 0.8 ->
+    0.4 over 16 steps): steps to the adaptive stop and wall time of the whole
+    loop (dg_run_canvas, logits made by the generator each step, one stop-flag
+    read per step) for growth 0.75/1.5/3/6 per step, and commits per step for
+    bounds 0.01/0.1/1/10."""
+    L, V = 256, 262144
+    torch.cuda.synchronize()
+    out = {"growth": [], "bound": []}
+    logits = torch.empty(L, V, dtype=torch.bfloat16, device="cuda")
+    final = torch.empty(1, L, dtype=torch.int32, device="cuda")
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16), max_batch=1)
+    for growth in (0.75, 1.5, 3.0, 6.0):
+        def den(step, canvas_ptr, active_ptr, lg, stream, g=growth):
+            synth.sharpening_logits(1002, step, L, V, m0_max=6.0, growth=g, dtype=torch.bfloat16,
+                                    device="cuda", out=lg)
+        ctx.dg_run_canvas([0], den, logits, final)       # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        steps, stopped = ctx.dg_run_canvas([0], den, logits, final)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        out["growth"].append({"growth": growth, "steps": int(steps[0]), "stopped": bool(stopped[0]),
+                              "run_ms": 1e3 * dt, "ms_per_step": 1e3 * dt / max(1, steps[0])})
+    ctx.close()
+    for bound in (0.01, 0.1, 1.0, 10.0):
+        ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16, entropy_bound=bound),
+                        max_batch=1)
+        am = [torch.empty(L, dtype=torch.int32, device="cuda") for _ in range(2)]
+        canvas = torch.empty(L, dtype=torch.int32, device="cuda")
+        nacc = torch.empty(1, dtype=torch.int32, device="cuda")
+        stop = torch.empty(1, dtype=torch.uint8, device="cuda")
+        seeds = torch.zeros(1, dtype=torch.int64, device="cuda")
+        counts = []
+        for s in range(48):
+            synth.sharpening_logits(1002, s, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda",
+                                    out=logits)
+            temp = torch.tensor([B.dg_temperature(ctx.params, s)], device="cuda")
+            o = ctx.step_out(canvas, argmax_out=am[s & 1], n_accept_out=nacc, stop_out=stop)
+            ctx.dg_sampler_step(logits, temp, s, seeds, o, prev_argmax=am[(s + 1) & 1] if s else None)
+            counts.append(int(nacc.item()))
+            if stop.item():
+                break
+        out["bound"].append({"bound": bound, "steps": len(counts),
+                             "commits_per_step": sum(counts) / len(counts)})
+        ctx.close()
+    return out
+
+
 def lmhead_leg(args, torch, B, synth):
     """The 64-canvas step whose logits come from the LM head: hidden bf16
     [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
@@ -177,6 +227,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head step")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch and dtype sweep")
+    ap.add_argument("--no-exp-b", action="store_true", help="skip the confidence-growth and bound sweeps")
     ap.add_argument("--lmhead-only", action="store_true",
                     help="only run the LM-head product and step (for counter runs)")
     ap.add_argument("--lmhead-steps", type=int, default=10)
@@ -308,6 +359,7 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_per_launch},
         "cpu_baseline": cpu,
         "sweep": None if args.no_sweep else sweep_leg(torch, B, synth),
+        "exp_b": None if args.no_exp_b else exp_b_leg(torch, B, synth),
         "lmhead": None if args.no_lmhead else lmhead_leg(args, torch, B, synth),
     }
     print(json.dumps(rec), flush=True)

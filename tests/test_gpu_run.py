@@ -125,6 +125,78 @@ def _explain_divergence(z, orec, seed, step, L, V, gpu_next_canvas):
     return "; ".join(reasons)
 
 
+def test_exp_b_growth_sweep_matches_oracle():
+    # "DiffusionGemma Lab" EXP B: the confidence-growth rate scaled by
+    # 0.5/1/2/4 (sharpening margin growth 0.75/1.5/3/6 per step). Each run
+    # through dg_run_canvas must stop where the oracle's does, with the same
+    # final argmax canvas (or part from it only at a near-tie), and faster
+    # growth must need fewer steps. V is reduced so the oracle runs in seconds.
+    L, V = 256, 4096
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16), max_batch=1)
+    gpu_steps = []
+    for growth in (0.75, 1.5, 3.0, 6.0):
+        def den_gpu(step, canvas_ptr, active_ptr, logits, stream, g=growth):
+            synth.sharpening_logits(1002, step, L, V, m0_max=6.0, growth=g, dtype=torch.bfloat16,
+                                    device="cuda", out=logits)
+        final, steps, stopped, canvases = _run_gpu(ctx, [0], den_gpu, torch.bfloat16, record_canvas=True)
+        zs = {}
+
+        def den(s, canvas, g=growth):
+            zs[s] = synth.sharpening_logits(1002, s, L, V, m0_max=6.0, growth=g, dtype=torch.bfloat16,
+                                            device="cuda")
+            return host_values(zs[s])
+
+        ofinal, osteps, ostopped, rec = O.run(den, 0, L, V, n_sched=16, record=True)
+        parted = next((s for s in range(min(osteps, steps[0]))
+                       if not np.array_equal(canvases[s][0], rec[s]["canvas_in"])), None)
+        if parted is None:
+            assert stopped[0] == ostopped == 1
+            assert steps[0] == osteps, f"growth {growth}: {steps[0]} steps, oracle {osteps}"
+            assert np.array_equal(final[0], ofinal)
+            print(f"growth {growth}: stops after {steps[0]} steps, as the oracle")
+        else:
+            why = _explain_divergence(zs[parted - 1], rec[parted - 1], 0, parted - 1, L, V, canvases[parted][0])
+            print(f"growth {growth}: {steps[0]} steps (oracle {osteps}); parts at step {parted} ({why})")
+        gpu_steps.append(steps[0])
+    assert all(a >= b for a, b in zip(gpu_steps, gpu_steps[1:])) and gpu_steps[0] > gpu_steps[-1]
+
+
+def test_exp_b_bound_sweep_commits_match_oracle():
+    # "DiffusionGemma Lab" EXP B: raising the entropy bound raises the commits
+    # per step. The sharpening denoiser is open loop (its logits do not depend
+    # on the canvas), so every step can be compared with the oracle's on the
+    # same logits: the commit count must agree (or sit at an acceptance near-tie)
+    # and the mean commits per step must grow with the bound.
+    from gpu_util import accept_near_tie
+    L, V, steps = 256, 4096, 12
+    require_gpu()
+    means = []
+    for bound in (0.01, 0.1, 1.0, 10.0):
+        ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16, entropy_bound=bound),
+                        max_batch=1)
+        bufs = dict(canvas_out=torch.empty(L, dtype=torch.int32, device="cuda"),
+                    entropy_out=torch.empty(L, device="cuda"),
+                    n_accept_out=torch.empty(1, dtype=torch.int32, device="cuda"))
+        counts = []
+        for s in range(steps):
+            z = synth.sharpening_logits(1002, s, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda")
+            t = np.float32(O.temperature(s, 0.8, 0.4, 16))
+            ctx.dg_sampler_step(z, torch.tensor([t], device="cuda"), s, seeds_tensor([0]),
+                                ctx.step_out(**bufs))
+            torch.cuda.synchronize()
+            k = int(bufs["n_accept_out"].item())
+            orec = O.step(host_values(z), t, 0, s, bound=np.float32(bound))
+            if k != orec["n_accept"]:
+                dh = float(np.max(np.abs(bufs["entropy_out"].cpu().numpy() - orec["entropy"])))
+                assert accept_near_tie(orec["entropy"], float(np.float32(bound)), dh), \
+                    f"bound {bound} step {s}: {k} commits, oracle {orec['n_accept']}"
+            counts.append(k)
+        means.append(float(np.mean(counts)))
+        print(f"bound {bound}: {means[-1]:.1f} commits per step over {steps} steps")
+    assert all(a <= b for a, b in zip(means, means[1:])) and means[0] < means[-1]
+
+
 def test_full_vocab_steps_sampled_rows_and_exact_decisions():
     # the benchmark's single-canvas shape (B=1, 256 x 262144 bf16, nsplit auto),
     # stepped from Python so every step's outputs are visible: oracle statistics
