@@ -24,18 +24,20 @@
  *
  * The pages fix the rules but not how the multinomial sample or the noise is
  * drawn. This library fixes one random protocol so that its integer outputs
- * are reproducible bit for bit (a "two-level Gumbel-max" over interleaved
- * vocabulary blocks driven by Philox4x32-10, Salmon et al., SC'11):
+ * are reproducible bit for bit (a "two-level Gumbel-max" over vocabulary
+ * blocks driven by Philox4x32-10, Salmon et al., SC'11):
  *
  *   key      = (low 32 bits of seed_c, high 32 bits of seed_c) for canvas c
  *   counter  = (c0, position l, step s, tag)
  *   tags     INIT = 0, BLOCK = 1, ELEM = 2, RENOISE = 3
  *   uniform  U(w) = (2*(w >> 9) + 1) * 2^-24   (in (0,1), exact in fp32)
  *   Gumbel   G(w) = -ln(-ln U(w))
- *   blocks   vocabulary id v lies in block j = 64*(v >> 15) + ((v >> 3) & 63):
- *            a block is one 8-id slot of each of the 64 consecutive 512-id
- *            stripes of a 32768-id supergroup (512 ids when full).
- *   sample   j* = argmax_j (LSE_{v in j}(z_v/T) + G(w0 of (j, l, s, BLOCK)));
+ *   blocks   vocabulary id v lies in block j = 64*(v >> 12) + ((v >> 3) & 63):
+ *            a block is one 8-id slot of each of the 8 consecutive 512-id
+ *            stripes of a 4096-id chunk (64 ids when full).
+ *   sample   j* = argmax_j (LSE_{v in j}(z_v/T) + G_j), G_j = G(word (j>>9)&3
+ *            of (j & ~0x600, l, s, BLOCK)): one call serves the four blocks
+ *            whose numbers differ only in bits 9-10;
  *            y  = argmax_{v in j*} (z_v/T + G(word v&3 of (v>>2, l, s, ELEM)));
  *            ties go to the lowest j, then the lowest v. By the Gumbel-max
  *            property P(y = v) = softmax(z/T)_v exactly.

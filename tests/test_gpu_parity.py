@@ -114,7 +114,7 @@ def test_neg_inf_and_degenerate_rows():
     z = torch.randn(L, V, device="cuda")
     z[0, :] = float("-inf")
     z[0, 12345] = 0.5                       # single finite logit
-    z[1, :40000] = float("-inf")            # whole supergroup of -inf
+    z[1, :40000] = float("-inf")            # whole chunks of -inf
     z[2, ::3] = float("-inf")               # scattered -inf
     z[3, :] = 1.0                           # constant row: H = ln V, argmax 0
     z[4, :] = -3.0e4
