@@ -65,6 +65,40 @@ def _time_graphs(graphs, k, torch):
     return start.elapsed_time(stop) / 1e3
 
 
+def read_ceiling_leg(torch, buffers, stream, k):
+    """The rate of a plain streaming read (libdgprobe.so) over the same rotating
+    logits buffers, for a few launch shapes; the best one is the measured
+    ceiling that the statistics pass is set against."""
+    from canvas_sampler_amd import probe
+
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    nbytes = buffers[0].numel() * buffers[0].element_size()
+    shapes = [(256, 512), (512, 256), (2048, 256), (4096, 1024), (8192, 1024)]
+    best = None
+    with torch.cuda.stream(stream):
+        for grid, block in shapes:
+            def launch(r, grid=grid, block=block):
+                probe.stream_read(buffers[r], grid, block, sink, stream)
+            for i in range(20):
+                launch(i % len(buffers))
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for i in range(k):
+                launch(i % len(buffers))
+            stop.record()
+            torch.cuda.synchronize()
+            us = start.elapsed_time(stop) * 1e3 / k
+            if best is None or us < best[0]:
+                best = (us, grid, block)
+    us, grid, block = best
+    return {"kernel": "stream_read_kernel", "avg_kernel_us": us, "GB/s": nbytes / us * 1e-3,
+            "frac_of_peak": nbytes / us * 1e-3 / PEAK_HBM_GBS, "grid": grid, "block": block,
+            "bytes_per_launch": nbytes, "shapes_tried": len(shapes)}
+
+
 def sweep_leg(torch, B, synth):
     """Whole steps at other batch sizes (bf16, V = 262144) and the fp32
     single canvas: steps/s, positions/s and the statistics kernel's achieved
@@ -322,6 +356,7 @@ def main():
         _time_graphs(step_graphs, args.warmup, torch)
         t_graph = _time_graphs(step_graphs, args.steps, torch)
 
+    read_ceiling = read_ceiling_leg(torch, logits, stream, args.steps)
     steps_per_s = args.steps / t_step
     bytes_per_launch = Bn * L * V * 2
     stats_s = t_stats / args.steps
@@ -356,7 +391,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "canvas_stats_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic, "avg_kernel_us": stats_s * 1e6,
-                     "algorithmic_bytes_per_launch": bytes_per_launch},
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "frac_of_read_ceiling": read_ceiling["GB/s"] and achieved / read_ceiling["GB/s"]},
+        "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,
         "sweep": None if args.no_sweep else sweep_leg(torch, B, synth),
         "exp_b": None if args.no_exp_b else exp_b_leg(torch, B, synth),

@@ -1,4 +1,6 @@
-"""Builds the HIP library libdgcanvas.so for gfx950 with hipcc, in-tree.
+"""Builds the HIP library libdgcanvas.so for gfx950 with hipcc, in-tree, and
+beside it libdgprobe.so, the plain streaming read that the measurements set
+next to the statistics pass.
 
 Every source is compiled on each call (the caller decides when to build).
 Packed-FP32 instructions are disabled for all device code.
@@ -13,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdgcanvas.so")
 SOURCES = ["dg_canvas.hip", "canvas_stats.hip", "accept_renoise.hip", "lmhead_gemm.hip"]
+PROBE_LIB = os.path.join(PKG, "libdgprobe.so")
+PROBE_SOURCES = ["stream_read_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -31,17 +35,17 @@ def flags():
 
 def build(verbose=False):
     """Compiles every source to an object in _build/ (in parallel), links the
-    shared library next to this file and returns its path."""
+    two shared libraries next to this file and returns the sampler's path."""
     obj_dir = os.path.join(ROOT, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    procs, objs = [], []
-    for src in SOURCES:
+    procs, objs = [], {}
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
         cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
-        objs.append(obj)
+        objs[src] = obj
     failed = []
     for src, p in procs:
         out, _ = p.communicate()
@@ -52,10 +56,11 @@ def build(verbose=False):
             print(text, flush=True)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"]
+        subprocess.run(cmd + [objs[s] for s in srcs] + ["-o", tmp], check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -16,8 +16,8 @@ from oracle import sampler as O
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "dg_canvas.h")).read()
+def _declared_functions(header="dg_canvas.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", text)) - {"dg_denoise_fn"})
 
@@ -33,6 +33,21 @@ def test_library_exports_every_declared_symbol():
     exported = set(re.findall(r"\bT (dg_\w+)", out))
     assert set(names) <= exported
     assert sorted(B.EXPORTS) == names
+
+
+def test_probe_library_exports_its_symbol():
+    from canvas_sampler_amd import probe
+
+    names = _declared_functions("dg_probe.h")
+    assert names == sorted(probe.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (dg_\w+)", out))
+    lib = probe.lib()
+    # argument checks run before any launch, so they need no GPU
+    assert lib.dg_probe_stream_read(None, 16, 1, 64, None, None) == 1
+    assert lib.dg_probe_stream_read(ctypes.c_void_p(16), 24, 1, 64, ctypes.c_void_p(16), None) == 1
+    assert lib.dg_probe_stream_read(ctypes.c_void_p(16), 16, 1, 96, ctypes.c_void_p(16), None) == 1
 
 
 def test_version_and_defaults():
