@@ -203,6 +203,64 @@ def exp_b_leg(torch, B, synth):
     return out
 
 
+def run_loop_leg(torch, B, synth, reps=5):
+    """The whole 48-step loop of one canvas at 256 x 262144 bf16, three ways:
+    the host loop (dg_run_canvas: one stop-flag read and wait per step), the
+    device-resident loop (dg_run_canvas_resident, stop flags kept on the
+    device, no wait) and that loop captured once into a HIP graph and
+    replayed. The denoiser does nothing and the logits are the sharpening
+    denoiser's first step, which never meets the stop rule, so every run takes
+    all 48 steps over the same 128 MiB logits buffer; what differs between the
+    three is the loop's own overhead."""
+    L, V, cap = 256, 262144, 48
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=16, max_steps=cap)
+    ctx = B.Context(params, max_batch=1)
+    logits = synth.sharpening_logits(1002, 0, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda")
+    final = torch.empty(1, L, dtype=torch.int32, device="cuda")
+    steps = torch.empty(1, dtype=torch.int32, device="cuda")
+    stopped = torch.empty(1, dtype=torch.uint8, device="cuda")
+    seeds = torch.zeros(1, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def den(step, canvas_ptr, active_ptr, lg, strm):
+        return None
+
+    def wall(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps
+
+    out = {}
+    with torch.cuda.stream(stream):
+        def host():
+            st, sp = ctx.dg_run_canvas([0], den, logits, final)
+            assert st == [cap] and sp == [False]
+        out["host_loop_ms"] = 1e3 * wall(host)
+        for k in (0, 8):
+            out[f"resident_check{k}_ms"] = 1e3 * wall(
+                lambda k=k: ctx.dg_run_canvas_resident(seeds, den, logits, final, steps, stopped,
+                                                       check_every=k))
+            assert steps.item() == cap and stopped.item() == 0
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            ctx.dg_run_canvas_resident(seeds, den, logits, final, steps, stopped, check_every=0)
+        torch.cuda.synchronize()
+        steps.fill_(-1)
+        out["resident_graph_ms"] = 1e3 * wall(graph.replay)
+        assert steps.item() == cap
+    for k in list(out):
+        out[k.replace("_ms", "_us_per_step")] = out[k] * 1e3 / cap
+    out.update(workload="one canvas, 256 x 262144 bf16, 48 steps (no stop), no-op denoiser, "
+                        "one logits buffer", steps=cap, reps=reps)
+    ctx.close()
+    return out
+
+
 def lmhead_leg(args, torch, B, synth):
     """The 64-canvas step whose logits come from the LM head: hidden bf16
     [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
@@ -262,6 +320,8 @@ def main():
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head step")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch and dtype sweep")
     ap.add_argument("--no-exp-b", action="store_true", help="skip the confidence-growth and bound sweeps")
+    ap.add_argument("--no-run-loop", action="store_true",
+                    help="skip the host-loop / device-resident / graph comparison of the 48-step loop")
     ap.add_argument("--lmhead-only", action="store_true",
                     help="only run the LM-head product and step (for counter runs)")
     ap.add_argument("--lmhead-steps", type=int, default=10)
@@ -397,6 +457,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": None if args.no_sweep else sweep_leg(torch, B, synth),
         "exp_b": None if args.no_exp_b else exp_b_leg(torch, B, synth),
+        "run_loop": None if args.no_run_loop else run_loop_leg(torch, B, synth),
         "lmhead": None if args.no_lmhead else lmhead_leg(args, torch, B, synth),
     }
     print(json.dumps(rec), flush=True)

@@ -28,6 +28,7 @@ STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_INVALID_ARG", 2: "DG_ERR_UNSUPPORTED",
 EXPORTS = ["dg_params_default", "dg_params_check", "dg_create", "dg_destroy", "dg_last_error",
            "dg_get_params", "dg_temperature", "dg_set_stats_split", "dg_canvas_init",
            "dg_canvas_stats", "dg_accept_renoise", "dg_sampler_step", "dg_run_canvas",
+           "dg_run_canvas_resident",
            "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_version"]
 
 
@@ -81,6 +82,8 @@ def lib():
             "dg_sampler_step": [vp, i32, vp, ctypes.c_int, i64, vp, i32, vp, vp, vp,
                                 ctypes.POINTER(DgStepOut), vp],
             "dg_run_canvas": [vp, i32, vp, DENOISE_FN, vp, ctypes.c_int, vp, vp, vp, vp, vp],
+            "dg_run_canvas_resident": [vp, i32, vp, DENOISE_FN, vp, ctypes.c_int, vp, vp, vp, vp,
+                                       i32, vp],
             "dg_lmhead_logits": [vp, i32, vp, vp, i32, vp, i64, vp],
             "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp,
                                        ctypes.POINTER(DgStepOut), vp],
@@ -261,6 +264,33 @@ class Context:
             raise errors[0]
         self._chk(status)
         return list(steps), [bool(x) for x in stopped]
+
+    def dg_run_canvas_resident(self, seeds, denoise, logits_scratch, final_argmax, steps_used,
+                               stopped, check_every=0, stream=None):
+        """seeds: device uint64 tensor [B] (torch.int64); steps_used (int32 [B])
+        and stopped (uint8 [B]) are device outputs. denoise as for
+        dg_run_canvas. With check_every == 0 nothing waits for the device, so
+        the call may run under HIP graph capture; the callback object is kept
+        on the context until the next call (a replayed graph does not call it)."""
+        B = seeds.numel()
+        errors = []
+
+        def _cb(user, step, canvas_p, active_p, logits_p, stream_p):
+            try:
+                denoise(step, canvas_p, active_p, logits_scratch, stream)
+                return 0
+            except Exception as exc:  # reported through DG_ERR_CALLBACK
+                errors.append(exc)
+                return 1
+
+        self._resident_cb = cb = DENOISE_FN(_cb)
+        status = lib().dg_run_canvas_resident(self.handle, B, _ptr(seeds), cb, None,
+                                              _dtype_code(logits_scratch), _ptr(logits_scratch),
+                                              _ptr(final_argmax), _ptr(steps_used), _ptr(stopped),
+                                              int(check_every), _stream(stream))
+        if errors and status == DG_ERR_CALLBACK:
+            raise errors[0]
+        self._chk(status)
 
 
 _hip = None

@@ -1,6 +1,5 @@
 // Acceptance, renoise and stop of one canvas (the per-canvas half of a
-// sampler step), shared by accept_renoise_kernel and by the statistics kernel
-// when the last workgroup of a canvas finishes the step itself.
+// sampler step), run by accept_renoise_kernel with one workgroup per canvas.
 //
 // One thread per position, kAcceptThreads (256) positions at most:
 //   - sort the L keys (entropy bits << 32 | position) ascending with a
@@ -181,6 +180,14 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
     if (a.n_accept_out) a.n_accept_out[canvas] = kstar;
     if (a.mean_entropy_out) a.mean_entropy_out[canvas] = static_cast<float>(mean_h);
     if (a.stop_out) a.stop_out[canvas] = stop ? 1 : 0;
+    if (a.run_active) {
+      a.run_steps_used[canvas] = a.step + 1;
+      a.run_temperature[canvas] = a.run_next_temperature;
+      if (stop) {
+        a.run_stopped[canvas] = 1;
+        a.run_active[canvas] = 0;
+      }
+    }
   }
 }
 

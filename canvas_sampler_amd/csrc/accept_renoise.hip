@@ -37,7 +37,26 @@ __global__ void canvas_init_kernel(const uint64_t* __restrict__ seeds, int32_t c
   canvas[i] = uniform_token(rw.w[0], static_cast<uint32_t>(vocab));
 }
 
+__global__ void run_state_init_kernel(int32_t batch, uint8_t* __restrict__ active,
+                                      int32_t* __restrict__ steps_used, uint8_t* __restrict__ stopped,
+                                      float* __restrict__ temperature, float t0) {
+  const int32_t c = static_cast<int32_t>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (c >= batch) return;
+  active[c] = 1;
+  steps_used[c] = 0;
+  stopped[c] = 0;
+  temperature[c] = t0;
+}
+
 }  // namespace
+
+hipError_t launch_run_state_init(int32_t batch, uint8_t* active, int32_t* steps_used,
+                                 uint8_t* stopped, float* temperature, float t0, hipStream_t stream) {
+  const int threads = 256;
+  hipLaunchKernelGGL(run_state_init_kernel, dim3((batch + threads - 1) / threads), dim3(threads), 0,
+                     stream, batch, active, steps_used, stopped, temperature, t0);
+  return hipGetLastError();
+}
 
 hipError_t launch_accept_renoise(const AcceptArgs& a, int32_t batch, hipStream_t stream) {
   hipLaunchKernelGGL(accept_renoise_kernel, dim3(batch), dim3(kAcceptThreads), 0, stream, a);

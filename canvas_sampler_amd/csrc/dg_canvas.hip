@@ -522,9 +522,14 @@ dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, con
                       prev_argmax, active, ent, am, smp, out, false, s);
 }
 
-dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
-                        void* user, dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
-                        int32_t* steps_used, uint8_t* stopped, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments shared by the two run loops, checked before anything is enqueued.
+dg_status check_run(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
+                    dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
+                    int32_t* steps_used, uint8_t* stopped, const char* entry) {
   if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   dg_status st = check_batch(ctx, B);
   if (st != DG_OK) return st;
@@ -534,8 +539,8 @@ dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denois
   if ((st = check_logits(ctx, logits_scratch, dtype, V)) != DG_OK) {
     if (st == DG_ERR_UNSUPPORTED && std::strstr(ctx->err.c_str(), "row_stride"))
       return set_err(ctx, DG_ERR_UNSUPPORTED,
-                     "vocab = %lld must be a multiple of %d for dg_run_canvas with this dtype",
-                     static_cast<long long>(V), dtype == DG_DTYPE_BF16 ? 8 : 4);
+                     "vocab = %lld must be a multiple of %d for %s with this dtype",
+                     static_cast<long long>(V), dtype == DG_DTYPE_BF16 ? 8 : 4, entry);
     if (std::strstr(ctx->err.c_str(), "logits"))
       return set_err(ctx, st, "logits_scratch: %s", ctx->err.c_str());
     return st;
@@ -543,6 +548,20 @@ dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denois
   if (!final_argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "final_argmax is NULL");
   if (!steps_used) return set_err(ctx, DG_ERR_INVALID_ARG, "steps_used is NULL");
   if (!stopped) return set_err(ctx, DG_ERR_INVALID_ARG, "stopped is NULL");
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
+                        void* user, dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
+                        int32_t* steps_used, uint8_t* stopped, void* stream) {
+  dg_status st = check_run(ctx, B, seeds, denoise, dtype, logits_scratch, final_argmax, steps_used,
+                           stopped, "dg_run_canvas");
+  if (st != DG_OK) return st;
+  const int64_t V = ctx->p.vocab;
   DeviceGuard guard(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t L = ctx->p.canvas_len;
@@ -590,6 +609,61 @@ dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denois
     if (changed && remaining > 0)
       DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->active, ctx->active_host, B, hipMemcpyHostToDevice, s));
   }
+  return DG_OK;
+}
+
+dg_status dg_run_canvas_resident(dg_ctx* ctx, int32_t B, const uint64_t* seeds,
+                                 dg_denoise_fn denoise, void* user, dg_dtype dtype,
+                                 void* logits_scratch, int32_t* final_argmax, int32_t* steps_used,
+                                 uint8_t* stopped, int32_t check_every, void* stream) {
+  dg_status st = check_run(ctx, B, seeds, denoise, dtype, logits_scratch, final_argmax, steps_used,
+                           stopped, "dg_run_canvas_resident");
+  if (st != DG_OK) return st;
+  if (check_every < 0)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "check_every = %d must be >= 0", check_every);
+  const int64_t V = ctx->p.vocab;
+  DeviceGuard guard(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t L = ctx->p.canvas_len;
+
+  // Loop state on the device: active flags, steps used, stop flags and the
+  // temperature of the coming step, which each step's acceptance kernel
+  // advances for the canvases that ran it.
+  float t = 0.0f;
+  (void)dg_temperature(&ctx->p, 0, &t);
+  DG_CHECK_HIP(ctx, dg::launch_run_state_init(B, ctx->active, steps_used, stopped, ctx->temperature, t, s));
+  DG_CHECK_HIP(ctx, dg::launch_canvas_init(seeds, B, L, ctx->p.vocab, ctx->canvas, s));
+
+  for (int32_t step = 0; step < ctx->p.max_steps; ++step) {
+    if (denoise(user, step, ctx->canvas, ctx->active, logits_scratch, stream) != 0)
+      return set_err(ctx, DG_ERR_CALLBACK, "denoise callback failed at step %d", step);
+    float t_next = 0.0f;
+    (void)dg_temperature(&ctx->p, step + 1, &t_next);
+    int32_t* am_cur = ctx->argmax[step & 1];
+    const int32_t* am_prev = step > 0 ? ctx->argmax[(step - 1) & 1] : nullptr;
+    dg_step_out o{};
+    o.canvas_out = ctx->canvas;
+    o.argmax_out = final_argmax;
+    st = enqueue_stats(ctx, B, logits_scratch, dtype, V, ctx->temperature, step, nullptr, seeds,
+                       ctx->active, ctx->entropy, am_cur, ctx->sample, s);
+    if (st != DG_OK) return st;
+    dg::AcceptArgs a = accept_args(ctx, ctx->entropy, am_cur, ctx->sample, step, nullptr, seeds,
+                                   am_prev, ctx->active, &o, true);
+    a.run_active = ctx->active;
+    a.run_steps_used = steps_used;
+    a.run_stopped = stopped;
+    a.run_temperature = ctx->temperature;
+    a.run_next_temperature = t_next;
+    DG_CHECK_HIP(ctx, dg::launch_accept_renoise(a, B, s));
+    if (check_every > 0 && (step + 1) % check_every == 0 && step + 1 < ctx->p.max_steps) {
+      DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->active_host, ctx->active, B, hipMemcpyDeviceToHost, s));
+      DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
+      bool any = false;
+      for (int32_t c = 0; c < B && !any; ++c) any = ctx->active_host[c] != 0;
+      if (!any) break;
+    }
+  }
+  if (check_every > 0) DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
   return DG_OK;
 }
 

@@ -46,6 +46,15 @@ struct AcceptArgs {
   int32_t* n_accept_out;       // may be null
   float* mean_entropy_out;     // may be null
   uint8_t* stop_out;           // may be null
+  // Loop state of a device-resident run (all null outside one): a canvas
+  // that runs this step records step + 1 in run_steps_used and the next
+  // step's temperature in run_temperature; when its stop fires it sets
+  // run_stopped and clears run_active (the same flags as `active`).
+  uint8_t* run_active;
+  int32_t* run_steps_used;
+  uint8_t* run_stopped;
+  float* run_temperature;
+  float run_next_temperature;
 };
 
 struct StatsArgs {
@@ -93,6 +102,10 @@ int32_t stats_row_grid(int32_t rows, int32_t vocab, int32_t nsplit, bool has_act
 hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_renoise(const AcceptArgs& a, int32_t batch, hipStream_t stream);
 hipError_t launch_lmhead_gemm(const GemmArgs& g, hipStream_t stream);
+// Start of a device-resident run: every canvas active, no steps used, not
+// stopped, temperature t0.
+hipError_t launch_run_state_init(int32_t batch, uint8_t* active, int32_t* steps_used,
+                                 uint8_t* stopped, float* temperature, float t0, hipStream_t stream);
 hipError_t launch_canvas_init(const uint64_t* seeds, int32_t batch, int32_t canvas_len,
                               int32_t vocab, int32_t* canvas, hipStream_t stream);
 

@@ -54,7 +54,8 @@
  *     device memory after dg_create.
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work on
  *     it and return without waiting, except dg_run_canvas, which waits once per
- *     step for the stop flags.
+ *     step for the stop flags, and dg_run_canvas_resident with check_every > 0,
+ *     which waits once per check_every steps.
  *   - Every argument is validated before anything is enqueued. On any error
  *     nothing is written to any output; dg_last_error() names the offending
  *     argument or the failing runtime call.
@@ -231,6 +232,35 @@ typedef int (*dg_denoise_fn)(void* user, int32_t step, const int32_t* canvas_dev
 dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
                         void* user, dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
                         int32_t* steps_used, uint8_t* stopped, void* stream);
+
+/* The run of dg_run_canvas with its loop state kept on the device
+ * ("DiffusionGemma Lab", §2 items 3 and 5; boxwrench.dev Algorithm 1: the
+ * loop that stops a canvas once its argmax canvas is stable and its mean
+ * entropy is low, or at the step cap). The acceptance kernel itself clears a
+ * canvas's active flag when its stop fires, records the steps it used and
+ * writes the next step's temperature, so no step waits for the host: the
+ * steps are enqueued back to back. Results (final_argmax, steps_used,
+ * stopped) equal those of dg_run_canvas for the same seeds and denoiser.
+ *   seeds        device uint64 [B] (read by every step; keep it unchanged
+ *                until the run's work is done)
+ *   final_argmax device int32 [B, L], written
+ *   steps_used   device int32 [B], written (1..max_steps)
+ *   stopped      device uint8 [B], written: 1 if the adaptive stop fired
+ *   check_every  0: enqueue all max_steps steps and return without waiting;
+ *                nothing in the call copies memory or synchronises, so a
+ *                caller may capture the whole call into a HIP graph and replay
+ *                it (steps after every canvas has stopped find no active
+ *                canvas and exit at once). k > 0: after every k steps copy the
+ *                B active flags to the host, wait for the stream, and end the
+ *                loop once no canvas is active; returns after that wait.
+ * The denoiser is called once per enqueued step, with the device active flags
+ * as they will be when its work runs; logits_scratch, dtype and the callback
+ * are as for dg_run_canvas. Errors: as dg_run_canvas, plus DG_ERR_INVALID_ARG
+ * for check_every < 0. */
+dg_status dg_run_canvas_resident(dg_ctx* ctx, int32_t B, const uint64_t* seeds,
+                                 dg_denoise_fn denoise, void* user, dg_dtype dtype,
+                                 void* logits_scratch, int32_t* final_argmax, int32_t* steps_used,
+                                 uint8_t* stopped, int32_t check_every, void* stream);
 
 /* LM-head projection feeding the sampler: the pages' sampling stage runs a
  * full-vocabulary softmax over the 256 canvas positions (boxwrench.dev,

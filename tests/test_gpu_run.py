@@ -337,3 +337,120 @@ def test_callback_failure_reports_and_keeps_steps():
         [1], lambda s, cp, ap, lg, st: synth.iid_normal_logits(5, s, L, V, device="cuda", out=lg),
         logits, final)
     assert steps == [48] and stopped == [False]
+
+
+def _run_resident(ctx, seeds, denoise, dtype, check_every, record_canvas=False):
+    """dg_run_canvas_resident with device seeds and outputs; the same return
+    shape as _run_gpu."""
+    Bn, L, V = len(seeds), ctx.L, ctx.V
+    logits = torch.empty(Bn * L, V, dtype=dtype, device="cuda")
+    final = torch.full((Bn, L), -1, dtype=torch.int32, device="cuda")
+    steps = torch.full((Bn,), -1, dtype=torch.int32, device="cuda")
+    stopped = torch.full((Bn,), 7, dtype=torch.uint8, device="cuda")
+    canvases = []
+
+    def wrapped(step, canvas_ptr, active_ptr, lg, stream):
+        if record_canvas:
+            buf = torch.empty(Bn, L, dtype=torch.int32, device="cuda")
+            B.copy_from_device(buf, canvas_ptr)
+            canvases.append(buf)
+        denoise(step, canvas_ptr, active_ptr, lg, stream)
+
+    ctx.dg_run_canvas_resident(seeds_tensor(seeds), wrapped, logits, final, steps, stopped,
+                               check_every=check_every)
+    torch.cuda.synchronize()
+    return (final.cpu().numpy(), steps.cpu().tolist(), [bool(x) for x in stopped.cpu().tolist()],
+            [c.cpu().numpy() for c in canvases])
+
+
+def test_resident_run_matches_host_loop_and_oracle():
+    # the device-resident loop (stop flags cleared on the device, no per-step
+    # host wait) must give the host loop's results bit for bit, whether it
+    # checks the flags every step, every 5 steps or never, and follow the
+    # oracle's trajectories (or part from them only at a near-tie)
+    L, V = 256, 16384
+    gens = [1002, 2002, 3002]
+    seeds = [0, 7, 2**63 + 5]
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V, temp_steps=16), max_batch=3)
+    den = _sharpening_denoiser(gens, L, V, 6.0, torch.bfloat16)
+    hfinal, hsteps, hstopped, _ = _run_gpu(ctx, seeds, den, torch.bfloat16)
+    runs = {k: _run_resident(ctx, seeds, den, torch.bfloat16, k, record_canvas=(k == 0))
+            for k in (0, 1, 5)}
+    for k, (final, steps, stopped, _) in runs.items():
+        assert steps == hsteps and stopped == hstopped, f"check_every {k}"
+        assert np.array_equal(final, hfinal), f"check_every {k}"
+    final, steps, stopped, canvases = runs[0]
+    # with check_every 0 all 48 steps are enqueued; canvases that stopped
+    # keep their state through the later (empty) steps
+    assert len(canvases) == 48
+    for c in range(3):
+        zs = {}
+
+        def oden(s, canvas, g=gens[c]):
+            zs[s] = synth.sharpening_logits(g, s, L, V, m0_max=6.0, dtype=torch.bfloat16,
+                                            device="cuda")
+            return host_values(zs[s])
+
+        ofinal, osteps, ostopped, rec = O.run(oden, seeds[c], L, V, n_sched=16, record=True)
+        parted = next((s for s in range(min(osteps, steps[c]))
+                       if not np.array_equal(canvases[s][c], rec[s]["canvas_in"])), None)
+        if parted is None:
+            assert steps[c] == osteps and stopped[c] == bool(ostopped)
+            assert np.array_equal(final[c], ofinal)
+            for s in range(osteps, 48):
+                assert np.array_equal(canvases[s][c], canvases[osteps][c])
+            print(f"canvas {c}: resident loop stops after {osteps} steps, as the oracle")
+        else:
+            why = _explain_divergence(zs[parted - 1], rec[parted - 1], seeds[c], parted - 1, L, V,
+                                      canvases[parted][c])
+            print(f"canvas {c}: parts from the oracle at step {parted} ({why})")
+
+
+def test_resident_run_graph_replays():
+    # the resident loop with check_every 0 waits for nothing, so the whole
+    # run (denoiser included) is captured into one HIP graph; each replay,
+    # with other work and a synchronisation between replays and new seeds
+    # written into the device seed array, must equal an eager run
+    L, V, Bn, cap = 256, 4096, 2, 24
+    require_gpu()
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=16, max_steps=cap)
+    ctx = B.Context(params, max_batch=Bn)
+    gens = [1002, 4002]
+    pre = [torch.cat([synth.sharpening_logits(g, s, L, V, m0_max=6.0, dtype=torch.bfloat16,
+                                              device="cuda") for g in gens]) for s in range(cap)]
+
+    def den(step, canvas_ptr, active_ptr, lg, stream):
+        lg.copy_(pre[step])
+
+    eager = {}
+    for seeds in ([0, 7], [123, 2**63 + 5]):
+        r = _run_resident(ctx, seeds, den, torch.bfloat16, 0)
+        h = _run_gpu(ctx, seeds, den, torch.bfloat16)
+        assert r[1] == h[1] and r[2] == h[2] and np.array_equal(r[0], h[0])
+        assert all(r[2]) and max(r[1]) < cap
+        eager[tuple(seeds)] = r
+
+    logits = torch.empty(Bn * L, V, dtype=torch.bfloat16, device="cuda")
+    final = torch.empty(Bn, L, dtype=torch.int32, device="cuda")
+    steps = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    stopped = torch.empty(Bn, dtype=torch.uint8, device="cuda")
+    seeds_dev = seeds_tensor([0, 7])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ctx.dg_run_canvas_resident(seeds_dev, den, logits, final, steps, stopped, check_every=0)
+    torch.cuda.synchronize()
+    for seeds in ([0, 7], [123, 2**63 + 5], [0, 7], [123, 2**63 + 5]):
+        seeds_dev.copy_(seeds_tensor(seeds))
+        final.fill_(-1)
+        steps.fill_(-1)
+        stopped.fill_(9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ef, es, est, _ = eager[tuple(seeds)]
+        assert steps.cpu().tolist() == es
+        assert [bool(x) for x in stopped.cpu().tolist()] == est
+        assert np.array_equal(final.cpu().numpy(), ef)
+    print("graph replays equal the eager runs; steps", {k: v[1] for k, v in eager.items()})

@@ -99,3 +99,7 @@ def test_null_context_is_rejected():
     st = B.lib().dg_canvas_init(None, 1, None, None, None)
     assert st == B.DG_ERR_INVALID_ARG
     assert "ctx" in B.lib().dg_last_error(None).decode()
+    st = B.lib().dg_run_canvas_resident(None, 1, None, B.DENOISE_FN(lambda *a: 0), None, 1, None,
+                                        None, None, None, 0, None)
+    assert st == B.DG_ERR_INVALID_ARG
+    assert "ctx" in B.lib().dg_last_error(None).decode()
