@@ -17,6 +17,12 @@ Workloads:
                       target ("DiffusionGemma Lab", EXP B: synthetic logits
                       whose confidence ramps over steps, per-position
                       difficulty).
+  chained_targets,    block-autoregressive stand-in: canvas k of a stream has
+  chained_logits      per-position targets that continue the previous finished
+                      canvas (target_l = (prev_{(l+1) mod L} + shift_k) mod V,
+                      shift_k drawn per canvas; canvas 0 draws them uniformly)
+                      and sharpens on them like sharpening_logits ("DiffusionGemma
+                      Lab", Figure 1: finished canvases chain block-autoregressively).
   iid_normal_logits   untrained-model stand-in: iid N(0, variance), fresh each
                       step, no margin ("DiffusionGemma Lab", EXP A).
   lmhead_operands     hidden states N(0,1) and weights N(0, 1/K) in bf16, so
@@ -71,6 +77,30 @@ def sharpening_logits(gen_seed, step, canvas_len, vocab, m0_max=6.0, growth=1.5,
     target, m0 = _targets_and_margins(gen_seed, canvas_len, vocab, m0_max, device)
     g = _gen(device, gen_seed, 0x5EED, step)
     z = torch.randn(canvas_len, vocab, generator=g, device=device, dtype=torch.float32)
+    return _finish(z, target, m0 + growth * step, dtype, out)
+
+
+def chained_targets(gen_seed, canvas_index, prev_canvas, canvas_len, vocab, m0_max=6.0,
+                    device="cpu"):
+    """(target ids [L] int64, base margins m0 [L]) of canvas `canvas_index` of
+    the block-autoregressive stand-in; prev_canvas: the previous finished
+    canvas (tensor [L] on `device`), None for canvas 0."""
+    g = _gen(device, gen_seed, 0xC4A1, canvas_index)
+    m0 = torch.rand(canvas_len, generator=g, device=device, dtype=torch.float32) * m0_max
+    if prev_canvas is None:
+        target = torch.randint(0, vocab, (canvas_len,), generator=g, device=device)
+    else:
+        shift = torch.randint(1, vocab, (1,), generator=g, device=device)
+        target = (torch.roll(prev_canvas.to(device=device, dtype=torch.int64), -1) + shift) % vocab
+    return target, m0
+
+
+def chained_logits(gen_seed, canvas_index, step, target, m0, vocab, growth=1.5,
+                   dtype=torch.bfloat16, device="cpu", out=None):
+    """Step `step` of canvas `canvas_index`: fresh N(0,1) plus m0 + growth*step
+    at the targets from chained_targets."""
+    g = _gen(device, gen_seed, 0xC4A2, canvas_index, step)
+    z = torch.randn(target.shape[0], vocab, generator=g, device=device, dtype=torch.float32)
     return _finish(z, target, m0 + growth * step, dtype, out)
 
 

@@ -28,6 +28,7 @@ TAG_INIT = 0      # initial canvas token
 TAG_BLOCK = 1     # block-level Gumbel noise of the sample
 TAG_ELEM = 2      # element-level Gumbel noise inside the chosen block
 TAG_RENOISE = 3   # uniform token at a non-accepted position
+TAG_CANVAS = 4    # seed of a later canvas of a block-autoregressive stream
 
 
 def _u32(x):
