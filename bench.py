@@ -261,6 +261,74 @@ def run_loop_leg(torch, B, synth, reps=5):
     return out
 
 
+def generate_leg(torch, B, synth, n_canvases=4, reps=3):
+    """Block-autoregressive generation of one stream of 4 canvases (1024
+    tokens) at 256 x 262144 bf16 with the chained sharpening stand-in (canvas
+    k sharpens on targets that continue canvas k-1; fresh N(0,1) logits each
+    step, written by the stand-in on the device). Reports steps per canvas,
+    tokens per forward (one cache-update forward per canvas counted), wall
+    time, TPS = tokens / wall time, t_fwd = wall time / forwards, and the
+    stand-in's own time per step, for the device loop checking its stop flags
+    every step and every 4 steps."""
+    L, V = 256, 262144
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=16)
+    ctx = B.Context(params, max_batch=1)
+    logits = torch.empty(L, V, dtype=torch.bfloat16, device="cuda")
+    tokens = torch.empty(1, n_canvases * L, dtype=torch.int32, device="cuda")
+    steps = torch.empty(n_canvases, 1, dtype=torch.int32, device="cuda")
+    stopped = torch.empty(n_canvases, 1, dtype=torch.uint8, device="cuda")
+    seeds = torch.zeros(1, dtype=torch.int64, device="cuda")
+    gen = 1002
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    state = {}
+
+    def denoise(k, step, canvas_ptr, active_ptr, lg, strm):
+        tgt, m0 = state[k]
+        synth.chained_logits(gen, k, step, tgt, m0, V, dtype=torch.bfloat16, device="cuda", out=lg)
+
+    def cache_update(k, canvas_ptr, strm):
+        fin = torch.empty(L, dtype=torch.int32, device="cuda")
+        B.copy_from_device(fin, canvas_ptr)
+        state[k + 1] = synth.chained_targets(gen, k + 1, fin, L, V, device="cuda")
+
+    out = {"workload": f"one stream of {n_canvases} canvases ({n_canvases * L} tokens), 256 x 262144 "
+                       "bf16, chained sharpening stand-in (fresh N(0,1) logits per step on the "
+                       "device), T 0.8->0.4 over 16 steps, b = 0.1", "canvases": n_canvases}
+    with torch.cuda.stream(stream):
+        for check_every in (1, 4):
+            times = []
+            for _ in range(reps + 1):
+                state.clear()
+                state[0] = synth.chained_targets(gen, 0, None, L, V, device="cuda")
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                ctx.dg_generate(seeds, n_canvases, denoise, cache_update, logits, tokens, steps,
+                                stopped, check_every=check_every)
+                torch.cuda.synchronize()
+                times.append(time.perf_counter() - t0)
+            wall = min(times[1:])
+            st = steps.cpu().numpy()
+            _, tpf = B.tokens_per_forward(st, L)
+            fwd = int(st.sum()) + n_canvases
+            out[f"check{check_every}"] = {"wall_ms": 1e3 * wall, "tps": n_canvases * L / wall,
+                                          "t_fwd_us": 1e6 * wall / fwd}
+        out["steps_per_canvas"] = st[:, 0].tolist()
+        out["stopped"] = [bool(x) for x in stopped.cpu().numpy()[:, 0]]
+        out["tpf"] = tpf
+        out["forwards"] = fwd
+        # the stand-in alone, to separate its share of t_fwd from the sampler's
+        tgt, m0 = state[0]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(20):
+            synth.chained_logits(gen, 0, i, tgt, m0, V, dtype=torch.bfloat16, device="cuda", out=logits)
+        torch.cuda.synchronize()
+        out["stand_in_us_per_step"] = 1e6 * (time.perf_counter() - t0) / 20
+    ctx.close()
+    return out
+
+
 def lmhead_leg(args, torch, B, synth):
     """The 64-canvas step whose logits come from the LM head: hidden bf16
     [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
@@ -320,6 +388,8 @@ def main():
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head step")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch and dtype sweep")
     ap.add_argument("--no-exp-b", action="store_true", help="skip the confidence-growth and bound sweeps")
+    ap.add_argument("--no-generate", action="store_true",
+                    help="skip the block-autoregressive generation of four canvases (TPF/TPS)")
     ap.add_argument("--no-run-loop", action="store_true",
                     help="skip the host-loop / device-resident / graph comparison of the 48-step loop")
     ap.add_argument("--lmhead-only", action="store_true",
@@ -458,6 +528,7 @@ def main():
         "sweep": None if args.no_sweep else sweep_leg(torch, B, synth),
         "exp_b": None if args.no_exp_b else exp_b_leg(torch, B, synth),
         "run_loop": None if args.no_run_loop else run_loop_leg(torch, B, synth),
+        "generate": None if args.no_generate else generate_leg(torch, B, synth),
         "lmhead": None if args.no_lmhead else lmhead_leg(args, torch, B, synth),
     }
     print(json.dumps(rec), flush=True)

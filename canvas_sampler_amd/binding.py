@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_INVALID_ARG", 2: "DG_ERR_UNSUPPORTED",
 EXPORTS = ["dg_params_default", "dg_params_check", "dg_create", "dg_destroy", "dg_last_error",
            "dg_get_params", "dg_temperature", "dg_set_stats_split", "dg_canvas_init",
            "dg_canvas_stats", "dg_accept_renoise", "dg_sampler_step", "dg_run_canvas",
-           "dg_run_canvas_resident",
+           "dg_run_canvas_resident", "dg_generate", "dg_tokens_per_forward",
            "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_version"]
 
 
@@ -48,6 +48,10 @@ class DgStepOut(ctypes.Structure):
 
 DENOISE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p)
+BLOCK_DENOISE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p)
+CACHE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                            ctypes.c_void_p)
 
 _lib = None
 
@@ -84,6 +88,9 @@ def lib():
             "dg_run_canvas": [vp, i32, vp, DENOISE_FN, vp, ctypes.c_int, vp, vp, vp, vp, vp],
             "dg_run_canvas_resident": [vp, i32, vp, DENOISE_FN, vp, ctypes.c_int, vp, vp, vp, vp,
                                        i32, vp],
+            "dg_generate": [vp, i32, vp, i32, BLOCK_DENOISE_FN, CACHE_FN, vp, ctypes.c_int, vp, vp,
+                            vp, vp, i32, vp],
+            "dg_tokens_per_forward": [vp, i32, i32, i32, vp, vp],
             "dg_lmhead_logits": [vp, i32, vp, vp, i32, vp, i64, vp],
             "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp,
                                        ctypes.POINTER(DgStepOut), vp],
@@ -98,6 +105,19 @@ def lib():
         L.dg_version.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def tokens_per_forward(steps_used, canvas_len):
+    """dg_tokens_per_forward on a host int32 array [n_canvases, B]; returns
+    (per-stream TPF list, TPF over all streams)."""
+    import numpy as np
+    steps = np.ascontiguousarray(steps_used, dtype=np.int32)
+    n, b = steps.shape
+    per = (ctypes.c_double * b)()
+    total = ctypes.c_double()
+    _check(lib().dg_tokens_per_forward(steps.ctypes.data_as(ctypes.c_void_p), n, b, canvas_len,
+                                       per, ctypes.byref(total)))
+    return list(per), total.value
 
 
 def _check(status, ctx=None):
@@ -264,6 +284,43 @@ class Context:
             raise errors[0]
         self._chk(status)
         return list(steps), [bool(x) for x in stopped]
+
+    def dg_generate(self, seeds, n_canvases, denoise, cache_update, logits_scratch, tokens,
+                    steps_used, stopped, check_every=0, stream=None):
+        """seeds: device uint64 tensor [B] (torch.int64); tokens int32
+        [B, n_canvases * L], steps_used int32 [n_canvases, B] and stopped uint8
+        [n_canvases, B] are device outputs. denoise(k, step, canvas_ptr,
+        active_ptr, logits, stream) and cache_update(k, canvas_ptr, stream)
+        (or None) enqueue their work on `stream`."""
+        B = seeds.numel()
+        errors = []
+
+        def _den(user, k, step, canvas_p, active_p, logits_p, stream_p):
+            try:
+                denoise(k, step, canvas_p, active_p, logits_scratch, stream)
+                return 0
+            except Exception as exc:  # reported through DG_ERR_CALLBACK
+                errors.append(exc)
+                return 1
+
+        def _cache(user, k, canvas_p, stream_p):
+            try:
+                cache_update(k, canvas_p, stream)
+                return 0
+            except Exception as exc:
+                errors.append(exc)
+                return 1
+
+        den_cb = BLOCK_DENOISE_FN(_den)
+        cache_cb = CACHE_FN(_cache) if cache_update is not None else CACHE_FN()
+        self._generate_cbs = (den_cb, cache_cb)
+        status = lib().dg_generate(self.handle, B, _ptr(seeds), n_canvases, den_cb, cache_cb, None,
+                                   _dtype_code(logits_scratch), _ptr(logits_scratch), _ptr(tokens),
+                                   _ptr(steps_used), _ptr(stopped), int(check_every),
+                                   _stream(stream))
+        if errors and status == DG_ERR_CALLBACK:
+            raise errors[0]
+        self._chk(status)
 
     def dg_run_canvas_resident(self, seeds, denoise, logits_scratch, final_argmax, steps_used,
                                stopped, check_every=0, stream=None):

@@ -48,7 +48,48 @@ __global__ void run_state_init_kernel(int32_t batch, uint8_t* __restrict__ activ
   temperature[c] = t0;
 }
 
+// Seed of canvas k of each stream ("DiffusionGemma Lab", Figure 1: canvases
+// chain block-autoregressively; each needs noise of its own).
+__global__ void canvas_seeds_kernel(const uint64_t* __restrict__ seeds, int32_t batch, int32_t k,
+                                    uint64_t* __restrict__ out) {
+  const int32_t c = static_cast<int32_t>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (c >= batch) return;
+  const uint64_t seed = seeds[c];
+  if (k == 0) {
+    out[c] = seed;
+    return;
+  }
+  const Words4 w = philox4x32_10(static_cast<uint32_t>(k), 0u, 0u, kTagCanvas, static_cast<uint32_t>(seed),
+                                 static_cast<uint32_t>(seed >> 32));
+  out[c] = static_cast<uint64_t>(w.w[0]) | (static_cast<uint64_t>(w.w[1]) << 32);
+}
+
+__global__ void place_canvas_kernel(const int32_t* __restrict__ canvas, int32_t canvas_len, int64_t total,
+                                    int32_t* __restrict__ tokens, int64_t ld, int64_t offset) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t c = i / canvas_len;
+  tokens[c * ld + offset + (i - c * canvas_len)] = canvas[i];
+}
+
 }  // namespace
+
+hipError_t launch_canvas_seeds(const uint64_t* seeds, int32_t batch, int32_t k, uint64_t* out,
+                               hipStream_t stream) {
+  const int threads = 256;
+  hipLaunchKernelGGL(canvas_seeds_kernel, dim3((batch + threads - 1) / threads), dim3(threads), 0, stream,
+                     seeds, batch, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_place_canvas(const int32_t* canvas, int32_t batch, int32_t canvas_len, int32_t* tokens,
+                               int64_t ld, int64_t offset, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(batch) * canvas_len;
+  const int threads = 256;
+  hipLaunchKernelGGL(place_canvas_kernel, dim3(static_cast<unsigned>((total + threads - 1) / threads)),
+                     dim3(threads), 0, stream, canvas, canvas_len, total, tokens, ld, offset);
+  return hipGetLastError();
+}
 
 hipError_t launch_run_state_init(int32_t batch, uint8_t* active, int32_t* steps_used,
                                  uint8_t* stopped, float* temperature, float t0, hipStream_t stream) {

@@ -28,6 +28,7 @@ constexpr uint32_t kTagInit = 0;
 constexpr uint32_t kTagBlock = 1;
 constexpr uint32_t kTagElem = 2;
 constexpr uint32_t kTagRenoise = 3;
+constexpr uint32_t kTagCanvas = 4;   // seed of a later canvas of a block-autoregressive stream
 
 struct Words4 {
   uint32_t w[4];

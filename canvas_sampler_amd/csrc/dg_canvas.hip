@@ -27,6 +27,7 @@ struct dg_ctx {
   int32_t* argmax[2] = {nullptr, nullptr};
   int32_t* sample = nullptr;
   int32_t* canvas = nullptr;
+  int32_t* finished = nullptr;          // [max_rows]: the last finished canvases of dg_generate
   uint64_t* seeds = nullptr;            // [max_batch]
   float* temperature = nullptr;
   uint8_t* active = nullptr;
@@ -293,6 +294,7 @@ void free_ctx(dg_ctx* c) {
   hipFree(c->argmax[1]);
   hipFree(c->sample);
   hipFree(c->canvas);
+  hipFree(c->finished);
   hipFree(c->seeds);
   hipFree(c->temperature);
   hipFree(c->active);
@@ -372,10 +374,9 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
   const size_t rows = static_cast<size_t>(max_batch) * params->canvas_len;
   bool ok = dev_alloc(&c->partials, rows * c->nsplit_max) == hipSuccess &&
             dev_alloc(&c->tickets, rows) == hipSuccess && dev_alloc(&c->entropy, rows) == hipSuccess &&
-
             dev_alloc(&c->argmax[0], rows) == hipSuccess && dev_alloc(&c->argmax[1], rows) == hipSuccess &&
             dev_alloc(&c->sample, rows) == hipSuccess && dev_alloc(&c->canvas, rows) == hipSuccess &&
-            dev_alloc(&c->seeds, max_batch) == hipSuccess &&
+            dev_alloc(&c->finished, rows) == hipSuccess && dev_alloc(&c->seeds, max_batch) == hipSuccess &&
             dev_alloc(&c->temperature, max_batch) == hipSuccess &&
             dev_alloc(&c->active, max_batch) == hipSuccess && dev_alloc(&c->stop, max_batch) == hipSuccess &&
             hipHostMalloc(reinterpret_cast<void**>(&c->stop_host), max_batch) == hipSuccess &&
@@ -387,7 +388,6 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
     return set_err(nullptr, DG_ERR_OUT_OF_MEMORY, "could not allocate scratch for max_batch = %d", max_batch);
   }
   if (hipMemset(c->tickets, 0, rows * sizeof(uint32_t)) != hipSuccess ||
-
       hipDeviceSynchronize() != hipSuccess) {
     free_ctx(c);
     return set_err(nullptr, DG_ERR_DEVICE, "could not clear the ticket scratch");
@@ -527,14 +527,15 @@ dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, con
 namespace {
 
 // Arguments shared by the two run loops, checked before anything is enqueued.
-dg_status check_run(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
+dg_status check_run(dg_ctx* ctx, int32_t B, const uint64_t* seeds, bool has_denoise,
                     dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
-                    int32_t* steps_used, uint8_t* stopped, const char* entry) {
+                    int32_t* steps_used, uint8_t* stopped, const char* entry,
+                    const char* final_name = "final_argmax") {
   if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   dg_status st = check_batch(ctx, B);
   if (st != DG_OK) return st;
   if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
-  if (!denoise) return set_err(ctx, DG_ERR_INVALID_ARG, "denoise is NULL");
+  if (!has_denoise) return set_err(ctx, DG_ERR_INVALID_ARG, "denoise is NULL");
   const int64_t V = ctx->p.vocab;
   if ((st = check_logits(ctx, logits_scratch, dtype, V)) != DG_OK) {
     if (st == DG_ERR_UNSUPPORTED && std::strstr(ctx->err.c_str(), "row_stride"))
@@ -545,9 +546,55 @@ dg_status check_run(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn
       return set_err(ctx, st, "logits_scratch: %s", ctx->err.c_str());
     return st;
   }
-  if (!final_argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "final_argmax is NULL");
+  if (!final_argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "%s is NULL", final_name);
   if (!steps_used) return set_err(ctx, DG_ERR_INVALID_ARG, "steps_used is NULL");
   if (!stopped) return set_err(ctx, DG_ERR_INVALID_ARG, "stopped is NULL");
+  return DG_OK;
+}
+
+// The device-resident loop over the steps of B canvases: state initialised on
+// the device, then per step the denoiser (denoise(step)), the statistics pass
+// and the acceptance kernel, which advances the loop state itself. With
+// check_every > 0 it waits for the active flags every check_every steps and
+// stops once none is set; otherwise it never waits.
+template <class Denoise>
+dg_status resident_run(dg_ctx* ctx, int32_t B, const uint64_t* seeds, Denoise& denoise, dg_dtype dtype,
+                       void* logits, int32_t* final_argmax, int32_t* steps_used, uint8_t* stopped,
+                       int32_t check_every, hipStream_t s) {
+  const int32_t L = ctx->p.canvas_len;
+  const int64_t V = ctx->p.vocab;
+  float t = 0.0f;
+  (void)dg_temperature(&ctx->p, 0, &t);
+  DG_CHECK_HIP(ctx, dg::launch_run_state_init(B, ctx->active, steps_used, stopped, ctx->temperature, t, s));
+  DG_CHECK_HIP(ctx, dg::launch_canvas_init(seeds, B, L, ctx->p.vocab, ctx->canvas, s));
+  for (int32_t step = 0; step < ctx->p.max_steps; ++step) {
+    if (denoise(step) != 0) return set_err(ctx, DG_ERR_CALLBACK, "denoise callback failed at step %d", step);
+    float t_next = 0.0f;
+    (void)dg_temperature(&ctx->p, step + 1, &t_next);
+    int32_t* am_cur = ctx->argmax[step & 1];
+    const int32_t* am_prev = step > 0 ? ctx->argmax[(step - 1) & 1] : nullptr;
+    dg_step_out o{};
+    o.canvas_out = ctx->canvas;
+    o.argmax_out = final_argmax;
+    dg_status st = enqueue_stats(ctx, B, logits, dtype, V, ctx->temperature, step, nullptr, seeds, ctx->active,
+                                 ctx->entropy, am_cur, ctx->sample, s);
+    if (st != DG_OK) return st;
+    dg::AcceptArgs a = accept_args(ctx, ctx->entropy, am_cur, ctx->sample, step, nullptr, seeds, am_prev,
+                                   ctx->active, &o, true);
+    a.run_active = ctx->active;
+    a.run_steps_used = steps_used;
+    a.run_stopped = stopped;
+    a.run_temperature = ctx->temperature;
+    a.run_next_temperature = t_next;
+    DG_CHECK_HIP(ctx, dg::launch_accept_renoise(a, B, s));
+    if (check_every > 0 && (step + 1) % check_every == 0 && step + 1 < ctx->p.max_steps) {
+      DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->active_host, ctx->active, B, hipMemcpyDeviceToHost, s));
+      DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
+      bool any = false;
+      for (int32_t c = 0; c < B && !any; ++c) any = ctx->active_host[c] != 0;
+      if (!any) break;
+    }
+  }
   return DG_OK;
 }
 
@@ -558,8 +605,8 @@ extern "C" {
 dg_status dg_run_canvas(dg_ctx* ctx, int32_t B, const uint64_t* seeds, dg_denoise_fn denoise,
                         void* user, dg_dtype dtype, void* logits_scratch, int32_t* final_argmax,
                         int32_t* steps_used, uint8_t* stopped, void* stream) {
-  dg_status st = check_run(ctx, B, seeds, denoise, dtype, logits_scratch, final_argmax, steps_used,
-                           stopped, "dg_run_canvas");
+  dg_status st = check_run(ctx, B, seeds, denoise != nullptr, dtype, logits_scratch, final_argmax,
+                           steps_used, stopped, "dg_run_canvas");
   if (st != DG_OK) return st;
   const int64_t V = ctx->p.vocab;
   DeviceGuard guard(ctx->device);
@@ -616,54 +663,72 @@ dg_status dg_run_canvas_resident(dg_ctx* ctx, int32_t B, const uint64_t* seeds,
                                  dg_denoise_fn denoise, void* user, dg_dtype dtype,
                                  void* logits_scratch, int32_t* final_argmax, int32_t* steps_used,
                                  uint8_t* stopped, int32_t check_every, void* stream) {
-  dg_status st = check_run(ctx, B, seeds, denoise, dtype, logits_scratch, final_argmax, steps_used,
-                           stopped, "dg_run_canvas_resident");
+  dg_status st = check_run(ctx, B, seeds, denoise != nullptr, dtype, logits_scratch, final_argmax,
+                           steps_used, stopped, "dg_run_canvas_resident");
   if (st != DG_OK) return st;
   if (check_every < 0)
     return set_err(ctx, DG_ERR_INVALID_ARG, "check_every = %d must be >= 0", check_every);
-  const int64_t V = ctx->p.vocab;
   DeviceGuard guard(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  auto call = [&](int32_t step) {
+    return denoise(user, step, ctx->canvas, ctx->active, logits_scratch, stream);
+  };
+  st = resident_run(ctx, B, seeds, call, dtype, logits_scratch, final_argmax, steps_used, stopped,
+                    check_every, s);
+  if (st == DG_OK && check_every > 0) DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
+  return st;
+}
+
+dg_status dg_generate(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t n_canvases,
+                      dg_block_denoise_fn denoise, dg_cache_fn cache_update, void* user, dg_dtype dtype,
+                      void* logits_scratch, int32_t* tokens, int32_t* steps_used, uint8_t* stopped,
+                      int32_t check_every, void* stream) {
+  dg_status st = check_run(ctx, B, seeds, denoise != nullptr, dtype, logits_scratch, tokens, steps_used,
+                           stopped, "dg_generate", "tokens");
+  if (st != DG_OK) return st;
+  if (check_every < 0)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "check_every = %d must be >= 0", check_every);
   const int32_t L = ctx->p.canvas_len;
-
-  // Loop state on the device: active flags, steps used, stop flags and the
-  // temperature of the coming step, which each step's acceptance kernel
-  // advances for the canvases that ran it.
-  float t = 0.0f;
-  (void)dg_temperature(&ctx->p, 0, &t);
-  DG_CHECK_HIP(ctx, dg::launch_run_state_init(B, ctx->active, steps_used, stopped, ctx->temperature, t, s));
-  DG_CHECK_HIP(ctx, dg::launch_canvas_init(seeds, B, L, ctx->p.vocab, ctx->canvas, s));
-
-  for (int32_t step = 0; step < ctx->p.max_steps; ++step) {
-    if (denoise(user, step, ctx->canvas, ctx->active, logits_scratch, stream) != 0)
-      return set_err(ctx, DG_ERR_CALLBACK, "denoise callback failed at step %d", step);
-    float t_next = 0.0f;
-    (void)dg_temperature(&ctx->p, step + 1, &t_next);
-    int32_t* am_cur = ctx->argmax[step & 1];
-    const int32_t* am_prev = step > 0 ? ctx->argmax[(step - 1) & 1] : nullptr;
-    dg_step_out o{};
-    o.canvas_out = ctx->canvas;
-    o.argmax_out = final_argmax;
-    st = enqueue_stats(ctx, B, logits_scratch, dtype, V, ctx->temperature, step, nullptr, seeds,
-                       ctx->active, ctx->entropy, am_cur, ctx->sample, s);
+  if (n_canvases < 1 || static_cast<int64_t>(n_canvases) * L > INT32_MAX)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "n_canvases = %d must be in 1..%d", n_canvases, INT32_MAX / L);
+  DeviceGuard guard(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ld = static_cast<int64_t>(n_canvases) * L;
+  for (int32_t k = 0; k < n_canvases; ++k) {
+    DG_CHECK_HIP(ctx, dg::launch_canvas_seeds(seeds, B, k, ctx->seeds, s));
+    auto call = [&](int32_t step) {
+      return denoise(user, k, step, ctx->canvas, ctx->active, logits_scratch, stream);
+    };
+    st = resident_run(ctx, B, ctx->seeds, call, dtype, logits_scratch, ctx->finished,
+                      steps_used + static_cast<int64_t>(k) * B, stopped + static_cast<int64_t>(k) * B,
+                      check_every, s);
     if (st != DG_OK) return st;
-    dg::AcceptArgs a = accept_args(ctx, ctx->entropy, am_cur, ctx->sample, step, nullptr, seeds,
-                                   am_prev, ctx->active, &o, true);
-    a.run_active = ctx->active;
-    a.run_steps_used = steps_used;
-    a.run_stopped = stopped;
-    a.run_temperature = ctx->temperature;
-    a.run_next_temperature = t_next;
-    DG_CHECK_HIP(ctx, dg::launch_accept_renoise(a, B, s));
-    if (check_every > 0 && (step + 1) % check_every == 0 && step + 1 < ctx->p.max_steps) {
-      DG_CHECK_HIP(ctx, hipMemcpyAsync(ctx->active_host, ctx->active, B, hipMemcpyDeviceToHost, s));
-      DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
-      bool any = false;
-      for (int32_t c = 0; c < B && !any; ++c) any = ctx->active_host[c] != 0;
-      if (!any) break;
-    }
+    DG_CHECK_HIP(ctx, dg::launch_place_canvas(ctx->finished, B, L, tokens, ld, static_cast<int64_t>(k) * L, s));
+    if (cache_update && cache_update(user, k, ctx->finished, stream) != 0)
+      return set_err(ctx, DG_ERR_CALLBACK, "cache_update callback failed after canvas %d", k);
   }
   if (check_every > 0) DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+dg_status dg_tokens_per_forward(const int32_t* steps_used, int32_t n_canvases, int32_t B,
+                                int32_t canvas_len, double* tpf, double* tpf_all) {
+  if (!steps_used) return set_err(nullptr, DG_ERR_INVALID_ARG, "steps_used is NULL");
+  if (n_canvases < 1) return set_err(nullptr, DG_ERR_INVALID_ARG, "n_canvases = %d must be >= 1", n_canvases);
+  if (B < 1) return set_err(nullptr, DG_ERR_INVALID_ARG, "B = %d must be >= 1", B);
+  if (canvas_len < 1) return set_err(nullptr, DG_ERR_INVALID_ARG, "canvas_len = %d must be >= 1", canvas_len);
+  for (int64_t i = 0; i < static_cast<int64_t>(n_canvases) * B; ++i)
+    if (steps_used[i] < 0)
+      return set_err(nullptr, DG_ERR_INVALID_ARG, "steps_used[%lld] = %d is negative",
+                     static_cast<long long>(i), steps_used[i]);
+  int64_t all = 0;
+  for (int32_t c = 0; c < B; ++c) {
+    int64_t fwd = n_canvases;  // one cache-update forward per canvas
+    for (int32_t k = 0; k < n_canvases; ++k) fwd += steps_used[static_cast<int64_t>(k) * B + c];
+    all += fwd;
+    if (tpf) tpf[c] = static_cast<double>(n_canvases) * canvas_len / static_cast<double>(fwd);
+  }
+  if (tpf_all) tpf_all[0] = static_cast<double>(n_canvases) * B * canvas_len / static_cast<double>(all);
   return DG_OK;
 }
 

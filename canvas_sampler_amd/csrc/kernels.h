@@ -106,6 +106,14 @@ hipError_t launch_lmhead_gemm(const GemmArgs& g, hipStream_t stream);
 // stopped, temperature t0.
 hipError_t launch_run_state_init(int32_t batch, uint8_t* active, int32_t* steps_used,
                                  uint8_t* stopped, float* temperature, float t0, hipStream_t stream);
+// Seeds of canvas k of B block-autoregressive streams: out[c] = seeds[c] for
+// k = 0, else words 0 and 1 of Philox4x32-10 at counter (k, 0, 0, CANVAS)
+// under key(seeds[c]).
+hipError_t launch_canvas_seeds(const uint64_t* seeds, int32_t batch, int32_t k, uint64_t* out,
+                               hipStream_t stream);
+// tokens[c * ld + offset + l] = canvas[c * canvas_len + l] for c < batch, l < canvas_len.
+hipError_t launch_place_canvas(const int32_t* canvas, int32_t batch, int32_t canvas_len, int32_t* tokens,
+                               int64_t ld, int64_t offset, hipStream_t stream);
 hipError_t launch_canvas_init(const uint64_t* seeds, int32_t batch, int32_t canvas_len,
                               int32_t vocab, int32_t* canvas, hipStream_t stream);
 

@@ -262,6 +262,60 @@ dg_status dg_run_canvas_resident(dg_ctx* ctx, int32_t B, const uint64_t* seeds,
                                  void* logits_scratch, int32_t* final_argmax, int32_t* steps_used,
                                  uint8_t* stopped, int32_t check_every, void* stream);
 
+/* Callbacks of dg_generate. Like dg_denoise_fn they enqueue work on `stream`
+ * and return 0 on success.
+ *   dg_block_denoise_fn  writes the logits of step `step` of canvas
+ *                        `canvas_index` (arguments otherwise as dg_denoise_fn).
+ *   dg_cache_fn          is told, once per canvas and before the next canvas's
+ *                        first step, the finished argmax canvases of every
+ *                        stream (device int32 [B, L], valid in stream order
+ *                        until the next canvas finishes): the extra forward
+ *                        pass that appends them to the model's cache. */
+typedef int (*dg_block_denoise_fn)(void* user, int32_t canvas_index, int32_t step,
+                                   const int32_t* canvas_dev, const uint8_t* active_dev,
+                                   void* logits_dev, void* stream);
+typedef int (*dg_cache_fn)(void* user, int32_t canvas_index, const int32_t* canvas_dev, void* stream);
+
+/* Block-autoregressive generation of B streams of n_canvases canvases each
+ * ("DiffusionGemma Lab", §2, Figure 1: finished canvases chain
+ * block-autoregressively; "DiffusionGemma: When the LLM Stops Writing Left to
+ * Right", "What DiffusionGemma Actually Is": one canvas at a time, each
+ * conditioned on the finished ones; boxwrench.dev "Finding": committed
+ * canvases are appended to the encoder's cache canvas by canvas). For
+ * k = 0 .. n_canvases-1: the device-resident run of dg_run_canvas_resident
+ * for canvas k, whose seed is seeds[c] for k = 0 and otherwise words 0 and 1
+ * (low, high) of Philox4x32-10 at counter (k, 0, 0, CANVAS = 4) under
+ * key(seeds[c]); its argmax canvas goes to the stream's tokens; then
+ * cache_update (if not NULL) is told the finished canvases.
+ *   seeds        device uint64 [B]
+ *   n_canvases   >= 1, n_canvases * L <= INT32_MAX
+ *   tokens       device int32 [B, n_canvases * L], written: stream c's
+ *                canvases one after the other
+ *   steps_used   device int32 [n_canvases, B], written: steps of canvas k of
+ *                stream c at [k * B + c]
+ *   stopped      device uint8 [n_canvases, B], written: adaptive stop fired
+ *   check_every  as for dg_run_canvas_resident; 0 enqueues every step of every
+ *                canvas without waiting (capturable into a HIP graph)
+ * Other arguments and errors as dg_run_canvas_resident; a failing
+ * cache_update returns DG_ERR_CALLBACK. */
+dg_status dg_generate(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t n_canvases,
+                      dg_block_denoise_fn denoise, dg_cache_fn cache_update, void* user, dg_dtype dtype,
+                      void* logits_scratch, int32_t* tokens, int32_t* steps_used, uint8_t* stopped,
+                      int32_t check_every, void* stream);
+
+/* Tokens per forward pass of finished dg_generate streams (boxwrench.dev,
+ * "Finding", hardware paragraph: TPF counts the extra forward pass that
+ * updates the cache; throughput is TPS = TPF / t_fwd). A stream's forwards
+ * are its denoising steps plus one cache update per canvas, and every canvas
+ * contributes its L tokens:
+ *   tpf[c]   = n_canvases * L / (sum_k steps_used[k * B + c] + n_canvases)
+ *   tpf_all  = n_canvases * B * L / (sum over streams of those forwards)
+ *   steps_used  host int32 [n_canvases, B], each >= 0
+ *   tpf         host double [B] or NULL;  tpf_all: host double or NULL
+ * Host arithmetic only; no context needed. */
+dg_status dg_tokens_per_forward(const int32_t* steps_used, int32_t n_canvases, int32_t B,
+                                int32_t canvas_len, double* tpf, double* tpf_all);
+
 /* LM-head projection feeding the sampler: the pages' sampling stage runs a
  * full-vocabulary softmax over the 256 canvas positions (boxwrench.dev,
  * "DiffusionGemma: Parallel Denoising From an Autoregressive Checkpoint", the

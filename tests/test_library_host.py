@@ -103,3 +103,19 @@ def test_null_context_is_rejected():
                                         None, None, None, 0, None)
     assert st == B.DG_ERR_INVALID_ARG
     assert "ctx" in B.lib().dg_last_error(None).decode()
+
+
+def test_tokens_per_forward_matches_oracle():
+    from oracle import blockar as BA
+    rng = np.random.default_rng(0)
+    for n, b in ((1, 1), (3, 2), (7, 5)):
+        steps = rng.integers(0, 49, size=(n, b))
+        per, total = B.tokens_per_forward(steps, 256)
+        for c in range(b):
+            assert per[c] == pytest.approx(BA.tokens_per_forward(steps[:, c].tolist(), 256), rel=1e-15)
+        fwd = sum(BA.forwards(steps[:, c].tolist()) for c in range(b))
+        assert total == pytest.approx(n * b * 256 / fwd, rel=1e-15)
+    with pytest.raises(B.DgError, match="steps_used"):
+        B.tokens_per_forward(np.array([[3, -1]]), 256)
+    st = B.lib().dg_tokens_per_forward(None, 1, 1, 256, None, None)
+    assert st == B.DG_ERR_INVALID_ARG and "steps_used" in B.lib().dg_last_error(None).decode()
