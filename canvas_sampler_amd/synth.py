@@ -27,6 +27,8 @@ Workloads:
                       step, no margin ("DiffusionGemma Lab", EXP A).
   lmhead_operands     hidden states N(0,1) and weights N(0, 1/K) in bf16, so
                       that logits = hidden @ weight are about unit scale.
+  selfcond_embedding  fp32 [V, d] ~ N(0,1): synthetic parameters of the
+                      self-conditioning matmul (7.86 M at V = 262144, d = 30).
 """
 import torch
 
@@ -127,3 +129,9 @@ def lmhead_operands(gen_seed, rows, k, vocab, device="cpu"):
                            dtype=torch.float32)
         weight[k0:k0 + part.shape[0]] = (part * (1.0 / k) ** 0.5).to(torch.bfloat16)
     return hidden, weight
+
+
+def selfcond_embedding(gen_seed, vocab, d=30, device="cpu"):
+    """fp32 [vocab, d] ~ N(0, 1)."""
+    g = _gen(device, gen_seed, 0x5C0D)
+    return torch.randn(vocab, d, generator=g, device=device, dtype=torch.float32)
