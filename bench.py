@@ -329,6 +329,70 @@ def generate_leg(torch, B, synth, n_canvases=4, reps=3):
     return out
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def selfcond_leg(torch, B, synth, k=200, d=30):
+    """The sampling stage of the benchmark canvas with the self-conditioning
+    matmul: statistics pass, then out = softmax(z/T) @ E with E fp32
+    [262144, 30] (7.86 M parameters), over the same 4 rotating 128 MiB bf16
+    logits buffers. Reports the matmul's time, its fp32 matrix-core rate
+    (2 * rows * V * d flops) and the HBM rate of its logits and embedding
+    reads, and the whole stage (statistics + self-conditioning)."""
+    L, V, R = 256, 262144, 4
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=16)
+    ctx = B.Context(params, max_batch=1)
+    logits = [synth.sharpening_logits(1002, r, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda")
+              for r in range(R)]
+    E = synth.selfcond_embedding(5, V, d, device="cuda")
+    temps = [torch.tensor([B.dg_temperature(params, r)], device="cuda") for r in range(R)]
+    seeds = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ent = torch.empty(L, device="cuda")
+    smp = torch.empty(L, dtype=torch.int32, device="cuda")
+    am = [torch.empty(L, dtype=torch.int32, device="cuda") for _ in range(R)]
+    out = torch.empty(L, d, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def stats(r):
+        ctx.dg_canvas_stats(logits[r], temps[r], r, seeds, ent, am[r], smp)
+
+    def sc(r):
+        ctx.dg_self_condition(logits[r], temps[r], am[r], E, out)
+
+    def stage(r):
+        stats(r)
+        sc(r)
+
+    def timed(fn):
+        for i in range(20):
+            fn(i % R)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(k):
+            fn(i % R)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) * 1e3 / k
+
+    with torch.cuda.stream(stream):
+        for r in range(R):
+            stats(r)
+        t_sc = timed(sc)
+        t_stage = timed(stage)
+    flops = 2.0 * L * V * d
+    nbytes = L * V * 2 + V * d * 4
+    ctx.close()
+    return {"workload": "256 x 262144 bf16 logits (4 rotating buffers), E fp32 [262144, 30]",
+            "kernel": "self_cond_kernel", "sc_us": t_sc, "tflops": flops / t_sc * 1e-6,
+            "peak_fp32_mfma_tflops": PEAK_FP32_MFMA_TFLOPS,
+            "mfma_frac": flops / t_sc * 1e-6 / PEAK_FP32_MFMA_TFLOPS,
+            "read_gbs": nbytes / t_sc * 1e-3, "flops_per_launch": flops, "bytes_per_launch": nbytes,
+            "stage_us": t_stage}
+
+
 def lmhead_leg(args, torch, B, synth):
     """The 64-canvas step whose logits come from the LM head: hidden bf16
     [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
@@ -388,6 +452,8 @@ def main():
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head step")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch and dtype sweep")
     ap.add_argument("--no-exp-b", action="store_true", help="skip the confidence-growth and bound sweeps")
+    ap.add_argument("--no-selfcond", action="store_true",
+                    help="skip the self-conditioning matmul of the sampling stage")
     ap.add_argument("--no-generate", action="store_true",
                     help="skip the block-autoregressive generation of four canvases (TPF/TPS)")
     ap.add_argument("--no-run-loop", action="store_true",
@@ -529,6 +595,7 @@ def main():
         "exp_b": None if args.no_exp_b else exp_b_leg(torch, B, synth),
         "run_loop": None if args.no_run_loop else run_loop_leg(torch, B, synth),
         "generate": None if args.no_generate else generate_leg(torch, B, synth),
+        "selfcond": None if args.no_selfcond else selfcond_leg(torch, B, synth),
         "lmhead": None if args.no_lmhead else lmhead_leg(args, torch, B, synth),
     }
     print(json.dumps(rec), flush=True)

@@ -29,6 +29,7 @@ EXPORTS = ["dg_params_default", "dg_params_check", "dg_create", "dg_destroy", "d
            "dg_get_params", "dg_temperature", "dg_set_stats_split", "dg_canvas_init",
            "dg_canvas_stats", "dg_accept_renoise", "dg_sampler_step", "dg_run_canvas",
            "dg_run_canvas_resident", "dg_generate", "dg_tokens_per_forward",
+           "dg_self_condition",
            "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_version"]
 
 
@@ -91,6 +92,7 @@ def lib():
             "dg_generate": [vp, i32, vp, i32, BLOCK_DENOISE_FN, CACHE_FN, vp, ctypes.c_int, vp, vp,
                             vp, vp, i32, vp],
             "dg_tokens_per_forward": [vp, i32, i32, i32, vp, vp],
+            "dg_self_condition": [vp, i32, vp, ctypes.c_int, i64, vp, vp, vp, i32, vp, vp],
             "dg_lmhead_logits": [vp, i32, vp, vp, i32, vp, i64, vp],
             "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp,
                                        ctypes.POINTER(DgStepOut), vp],
@@ -284,6 +286,16 @@ class Context:
             raise errors[0]
         self._chk(status)
         return list(steps), [bool(x) for x in stopped]
+
+    def dg_self_condition(self, logits, temperature, argmax, embed, out, batch=None,
+                          row_stride=None, stream=None):
+        """out [B*L, d] fp32 = softmax(logits / T) @ embed ([V, d] fp32), with
+        argmax the statistics pass's output for these logits."""
+        B = batch if batch is not None else temperature.shape[0]
+        stride = row_stride if row_stride is not None else logits.stride(0)
+        self._chk(lib().dg_self_condition(self.handle, B, _ptr(logits), _dtype_code(logits), stride,
+                                          _ptr(temperature), _ptr(argmax), _ptr(embed),
+                                          embed.shape[1], _ptr(out), _stream(stream)))
 
     def dg_generate(self, seeds, n_canvases, denoise, cache_update, logits_scratch, tokens,
                     steps_used, stopped, check_every=0, stream=None):

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdgcanvas.so")
-SOURCES = ["dg_canvas.hip", "canvas_stats.hip", "accept_renoise.hip", "lmhead_gemm.hip"]
+SOURCES = ["dg_canvas.hip", "canvas_stats.hip", "accept_renoise.hip", "lmhead_gemm.hip",
+           "self_cond.hip"]
 PROBE_LIB = os.path.join(PKG, "libdgprobe.so")
 PROBE_SOURCES = ["stream_read_probe.hip"]
 ARCH = "gfx950"

@@ -28,6 +28,8 @@ struct dg_ctx {
   int32_t* sample = nullptr;
   int32_t* canvas = nullptr;
   int32_t* finished = nullptr;          // [max_rows]: the last finished canvases of dg_generate
+  float* sc_partials = nullptr;         // self-conditioning partial tiles
+  int64_t sc_partial_floats = 0;
   uint64_t* seeds = nullptr;            // [max_batch]
   float* temperature = nullptr;
   uint8_t* active = nullptr;
@@ -295,6 +297,7 @@ void free_ctx(dg_ctx* c) {
   hipFree(c->sample);
   hipFree(c->canvas);
   hipFree(c->finished);
+  hipFree(c->sc_partials);
   hipFree(c->seeds);
   hipFree(c->temperature);
   hipFree(c->active);
@@ -382,6 +385,20 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
             hipHostMalloc(reinterpret_cast<void**>(&c->stop_host), max_batch) == hipSuccess &&
             hipHostMalloc(reinterpret_cast<void**>(&c->active_host), max_batch) == hipSuccess &&
             hipHostMalloc(reinterpret_cast<void**>(&c->temp_host), sizeof(float) * max_batch) == hipSuccess;
+  // partial tiles of the self-conditioning matmul: the most any batch up to
+  // max_batch needs (none once the row tiles alone fill the target grid)
+  for (int32_t b = 1; ok && b <= max_batch; ++b) {
+    int32_t nslice = 0, kslice = 0;
+    const int32_t rows_b = b * params->canvas_len;
+    dg::choose_self_cond_slices(rows_b, params->vocab, &nslice, &kslice);
+    if (nslice > 1) {
+      const int64_t rows_pad = (rows_b + dg::kScRowTile - 1) / dg::kScRowTile * dg::kScRowTile;
+      const int64_t need = static_cast<int64_t>(nslice) * rows_pad * 32;
+      if (need > c->sc_partial_floats) c->sc_partial_floats = need;
+    }
+    if (nslice == 1) break;  // larger batches need no partials either
+  }
+  if (ok && c->sc_partial_floats > 0) ok = dev_alloc(&c->sc_partials, static_cast<size_t>(c->sc_partial_floats)) == hipSuccess;
   if (!ok) {
     free_ctx(c);
     (void)hipGetLastError();
@@ -708,6 +725,41 @@ dg_status dg_generate(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t n_c
       return set_err(ctx, DG_ERR_CALLBACK, "cache_update callback failed after canvas %d", k);
   }
   if (check_every > 0) DG_CHECK_HIP(ctx, hipStreamSynchronize(s));
+  return DG_OK;
+}
+
+dg_status dg_self_condition(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype, int64_t row_stride,
+                           const float* temperature, const int32_t* argmax, const float* embed, int32_t d,
+                           float* out, void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  if ((st = check_logits(ctx, logits, dtype, row_stride)) != DG_OK) return st;
+  if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
+  if (!argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "argmax is NULL");
+  if (!embed) return set_err(ctx, DG_ERR_INVALID_ARG, "embed is NULL");
+  if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
+  if (d < 1 || d > 31) return set_err(ctx, DG_ERR_INVALID_ARG, "d = %d is outside 1..31", d);
+  if ((reinterpret_cast<uintptr_t>(embed) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "embed and out must be 4-byte aligned");
+  dg::SelfCondArgs a{};
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = ctx->p.vocab;
+  a.canvas_len = ctx->p.canvas_len;
+  a.rows = B * ctx->p.canvas_len;
+  a.temperature = temperature;
+  a.argmax = argmax;
+  a.embed = embed;
+  a.d = d;
+  a.out = out;
+  dg::choose_self_cond_slices(a.rows, a.vocab, &a.nslice, &a.kslice);
+  a.rows_pad = (a.rows + dg::kScRowTile - 1) / dg::kScRowTile * dg::kScRowTile;
+  a.partials = ctx->sc_partials;
+  if (a.nslice > 1 && static_cast<int64_t>(a.nslice) * a.rows_pad * 32 > ctx->sc_partial_floats)
+    return set_err(ctx, DG_ERR_DEVICE, "self-conditioning scratch too small (internal error)");
+  DeviceGuard guard(ctx->device);
+  DG_CHECK_HIP(ctx, dg::launch_self_cond(a, dtype == DG_DTYPE_BF16, static_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 

@@ -88,6 +88,33 @@ struct GemmArgs {
   int32_t vocab;           // multiple of 8
 };
 
+// Self-conditioning matmul: out[r, n] = sum_v softmax(z_r / T)_v E[v, n].
+struct SelfCondArgs {
+  const void* logits;      // [rows, row_stride], bf16 or fp32
+  int64_t row_stride;      // elements
+  int32_t vocab;
+  int32_t canvas_len;      // rows of one canvas (temperature index = row / canvas_len)
+  int32_t rows;
+  const float* temperature;  // [rows / canvas_len]
+  const int32_t* argmax;   // [rows]: id of each row's largest logit
+  const float* embed;      // fp32 [vocab, d]
+  int32_t d;               // 1..31
+  float* out;              // fp32 [rows, d]
+  int32_t nslice;          // vocabulary slices per row tile
+  int32_t kslice;          // ids per slice (a multiple of 64)
+  int32_t rows_pad;        // rows rounded up to the row tile
+  float* partials;         // [nslice, rows_pad, 32] when nslice > 1
+};
+
+constexpr int kScThreads = 512;          // 8 waves x 32 rows
+constexpr int kScRowTile = 256;
+constexpr int kScTargetWorkgroups = 512; // slices are cut so that tiles * slices <= this
+
+// Vocabulary slices for `rows` rows: one per row tile when the tiles alone
+// fill the target, else about kScTargetWorkgroups / tiles slices.
+void choose_self_cond_slices(int32_t rows, int32_t vocab, int32_t* nslice, int32_t* kslice);
+hipError_t launch_self_cond(const SelfCondArgs& a, bool bf16, hipStream_t stream);
+
 constexpr int kGemmThreads = 512;
 
 constexpr int kStatsThreads = 512;   // 8 waves: one workgroup streams a whole row

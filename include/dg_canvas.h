@@ -303,6 +303,31 @@ dg_status dg_generate(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t n_c
                       void* logits_scratch, int32_t* tokens, int32_t* steps_used, uint8_t* stopped,
                       int32_t check_every, void* stream);
 
+/* The self-conditioning matmul of the sampling stage (boxwrench.dev,
+ * "DiffusionGemma: Parallel Denoising From an Autoregressive Checkpoint",
+ * "Finding": a 7.8 M-parameter self-conditioning block feeds the previous
+ * step's prediction back; hardware paragraph: the sampling stage runs it with
+ * the full-vocabulary softmax, in full precision, over the canvas positions).
+ * The pages give no shapes; this library reads it as the expected token
+ * embedding under the step's tempered prediction:
+ *   out[r, n] = sum_v softmax(z_r / T_c)_v * embed[v, n],  n < d,
+ * for the B*L rows r of the logits (c = r / L), computed in fp32 on the
+ * matrix cores (products and sums in fp32, summation order unspecified); with
+ * d = 30 at V = 262144 the embedding holds 7,864,320 parameters.
+ *   logits, dtype, row_stride  as for dg_canvas_stats
+ *   temperature  device float [B], each > 0
+ *   argmax       device int32 [B*L]: the row's largest-logit id, as
+ *                dg_canvas_stats writes it (the softmax is taken relative to
+ *                that logit; another id gives wrong values, never a fault)
+ *   embed        device fp32 [V, d], row-major, 4-byte aligned
+ *   d            1..31
+ *   out          device fp32 [B*L, d], written
+ * Uses the context's scratch for partial sums when the batch is small; calls
+ * on one context must not overlap. Asynchronous on `stream`. */
+dg_status dg_self_condition(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype, int64_t row_stride,
+                           const float* temperature, const int32_t* argmax, const float* embed, int32_t d,
+                           float* out, void* stream);
+
 /* Tokens per forward pass of finished dg_generate streams (boxwrench.dev,
  * "Finding", hardware paragraph: TPF counts the extra forward pass that
  * updates the cache; throughput is TPS = TPF / t_fwd). A stream's forwards

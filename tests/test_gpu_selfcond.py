@@ -1,0 +1,125 @@
+"""GPU parity of the self-conditioning matmul (dg_self_condition) against the
+oracle (oracle/selfcond.py).
+
+Tolerance (derived from the arithmetic; the pages fix none): each term
+e_v * E[v, n] is formed in fp32 from e_v = 2^(z c - zmax c); rounding the
+exponent argument (|t| <= about 40 on these inputs) costs at most 40 * 2^-24,
+about 2.4e-6 of the term, after a common factor that the normaliser cancels.
+Sums run in fp32 along chains of at most n = 8192 matrix-core updates per
+accumulator plus one addition per vocabulary slice (n <= 8200 for every
+launch shape at V <= 262144), so the numerator and the normaliser are each
+within (n * 2^-24 + 2.4e-6) of the sum of their terms' magnitudes, and the
+ratio within twice that: |gpu - oracle| <= 1.0e-3 * sum_v p_v |E[v, n]|.
+That is the worst case; the observed maximum is printed and, being a sum of
+independent roundings, sits orders of magnitude below it (checked at 2e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+from canvas_sampler_amd import binding as B
+from canvas_sampler_amd import synth
+from oracle import selfcond as SC
+
+from gpu_util import gpu, host_values, require_gpu, seeds_tensor
+
+pytestmark = gpu
+
+TOL_BOUND = 1.0e-3
+TOL_TYPICAL = 2.0e-5
+
+
+def _run(L, V, Bn, dtype, d, temps, gen=31, m_max=8.0, rows_check=None, stride=None):
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=Bn)
+    z = torch.cat([synth.margin_logits(gen + c, L, V, m_max=m_max, dtype=dtype, device="cuda")
+                   for c in range(Bn)])
+    if stride is None and V % 8:
+        stride = (V + 7) // 8 * 8   # rows must start on 16-byte boundaries
+    if stride is not None:
+        buf = torch.full((z.shape[0], stride), 3.0, dtype=dtype, device="cuda")
+        buf[:, :V] = z
+        z_in = buf
+    else:
+        z_in = z
+    E = synth.selfcond_embedding(5, V, d, device="cuda")
+    rows = Bn * L
+    t = torch.tensor(temps, dtype=torch.float32, device="cuda")
+    h = torch.empty(rows, device="cuda")
+    am = torch.empty(rows, dtype=torch.int32, device="cuda")
+    smp = torch.empty(rows, dtype=torch.int32, device="cuda")
+    ctx.dg_canvas_stats(z_in, t, 0, seeds_tensor(list(range(Bn))), h, am, smp, batch=Bn)
+    out = torch.full((rows, d), float("nan"), device="cuda")
+    ctx.dg_self_condition(z_in, t, am, E, out, batch=Bn)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().astype(np.float64)
+    Eh = E.cpu().numpy().astype(np.float64)
+    sel = np.arange(rows) if rows_check is None else np.asarray(sorted(rows_check))
+    worst = 0.0
+    for i in range(0, len(sel), 64):
+        rr = sel[i:i + 64]
+        zh = host_values(z[torch.as_tensor(rr, device="cuda")])
+        for c in np.unique(rr // L):
+            m = (rr // L) == c
+            T = np.float32(temps[c])
+            want = SC.self_condition(zh[m], T, Eh)
+            mag = SC.magnitude(zh[m], T, Eh)
+            ratio = np.abs(g[rr[m]] - want) / mag
+            assert np.all(np.isfinite(g[rr[m]]))
+            assert np.all(ratio <= TOL_BOUND), f"rows {rr[m][np.any(ratio > TOL_BOUND, axis=1)]}"
+            worst = max(worst, float(ratio.max()))
+    assert worst <= TOL_TYPICAL, worst
+    print(f"L={L} V={V} B={Bn} {dtype} d={d}: max |err| / sum p|E| = {worst:.2e} over {len(sel)} rows")
+    return g
+
+
+@pytest.mark.parametrize("V", [2, 100, 1000, 4096, 4100, 70001])
+def test_small_and_ragged_vocabularies(V):
+    _run(256, V, 1, torch.float32, 30, [0.8])
+
+
+@pytest.mark.parametrize("d", [1, 7, 30, 31])
+def test_widths(d):
+    _run(100, 4096, 3, torch.bfloat16, d, [0.8, 0.4, 1.7])
+
+
+def test_full_vocabulary_single_canvas_bf16():
+    # the sampling stage of the benchmark step: 256 x 262144 bf16, d = 30
+    _run(256, 262144, 1, torch.bfloat16, 30, [0.8], m_max=6.0)
+
+
+def test_full_vocabulary_batch_fp32_sampled_rows():
+    rows = {0, 1, 255, 256, 511, 700, 1023}
+    _run(256, 262144, 4, torch.float32, 30, [0.8, 0.6, 0.5, 0.4], rows_check=rows)
+
+
+def test_one_slice_per_tile_batch():
+    # 260 canvases of 256 rows: the row tiles alone fill the grid, so each
+    # workgroup covers the whole vocabulary and divides by its own normaliser
+    n = 260 * 256
+    rows = set(range(0, n, 1021)) | {n - 1}
+    _run(256, 4096, 260, torch.bfloat16, 30, [0.4 + 0.4 * (c % 5) / 4 for c in range(260)],
+         rows_check=rows)
+
+
+def test_row_stride_padding_is_ignored():
+    _run(64, 1000, 2, torch.bfloat16, 30, [0.8, 0.5], stride=1024)
+
+
+def test_rejects_bad_arguments():
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=8, vocab=64), max_batch=1)
+    z = torch.zeros(8, 64, device="cuda")
+    t = torch.ones(1, device="cuda")
+    am = torch.zeros(8, dtype=torch.int32, device="cuda")
+    for d in (0, 32):
+        E = torch.zeros(64, max(d, 1), device="cuda")
+        out = torch.zeros(8, max(d, 1), device="cuda")
+        st = B.lib().dg_self_condition(ctx.handle, 1, z.data_ptr(), B.DG_DTYPE_F32, 64, t.data_ptr(),
+                                       am.data_ptr(), E.data_ptr(), d, out.data_ptr(), None)
+        assert st == B.DG_ERR_INVALID_ARG and "d = " in B.lib().dg_last_error(ctx.handle).decode()
+    E = torch.zeros(64, 4, device="cuda")
+    out = torch.zeros(8, 4, device="cuda")
+    with pytest.raises(B.DgError, match="argmax"):
+        ctx._chk(B.lib().dg_self_condition(ctx.handle, 1, z.data_ptr(), B.DG_DTYPE_F32, 64, t.data_ptr(),
+                                           None, E.data_ptr(), 4, out.data_ptr(), None))
