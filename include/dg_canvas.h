@@ -20,7 +20,13 @@
  *       finding: an upstream bug".
  *   "DiffusionGemma: Parallel Denoising From an Autoregressive Checkpoint"
  *       (boxwrench.dev), "Finding": Algorithm 1 (entropy-bounded acceptance,
- *       temperature annealing, adaptive stopping) and the hardware paragraph.
+ *       temperature annealing, adaptive stopping), the architecture paragraph
+ *       (canvases appended to the encoder's cache; the self-conditioning
+ *       block) and the hardware paragraph (the sampling stage; tokens per
+ *       forward pass).
+ *   "DiffusionGemma: When the LLM Stops Writing Left to Right" (LunarOps),
+ *       "What DiffusionGemma Actually Is": block-autoregressive multi-canvas
+ *       sampling.
  *
  * The pages fix the rules but not how the multinomial sample or the noise is
  * drawn. This library fixes one random protocol so that its integer outputs
@@ -29,7 +35,7 @@
  *
  *   key      = (low 32 bits of seed_c, high 32 bits of seed_c) for canvas c
  *   counter  = (c0, position l, step s, tag)
- *   tags     INIT = 0, BLOCK = 1, ELEM = 2, RENOISE = 3
+ *   tags     INIT = 0, BLOCK = 1, ELEM = 2, RENOISE = 3, CANVAS = 4
  *   uniform  U(w) = (2*(w >> 9) + 1) * 2^-24   (in (0,1), exact in fp32)
  *   Gumbel   G(w) = -ln(-ln U(w))
  *   blocks   vocabulary id v lies in block j = 64*(v >> 12) + ((v >> 3) & 63):
@@ -45,6 +51,9 @@
  *            w0 from (0, l, s, RENOISE); initial canvas: (0, l, 0, INIT).
  *   temperature at step s: (float)(T0 + (T1-T0) * min(s, S-1) / (S-1)),
  *            evaluated in double, T0 when S == 1.
+ *   seed of canvas k >= 1 of a block-autoregressive stream (dg_generate):
+ *            words 0 (low) and 1 (high) of (k, 0, 0, CANVAS = 4) under the
+ *            stream's key; canvas 0 uses the stream's seed.
  *
  * Conventions for every entry point
  *   - Device pointers are addresses in the memory of the context's device;

@@ -144,3 +144,50 @@ def test_generate_matches_oracle():
     for c in range(2):
         assert per[c] == pytest.approx(BA.tokens_per_forward(steps[:, c].tolist(), L), rel=1e-15)
     print("steps", steps.tolist(), "TPF", per, total)
+
+
+def test_argument_errors_and_callback_failures():
+    L, V = 32, 4096
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V, max_steps=6), max_batch=2)
+    logits = torch.zeros(2 * L, V, device="cuda")
+    tokens = torch.zeros(2, 3 * L, dtype=torch.int32, device="cuda")
+    steps = torch.zeros(3, 2, dtype=torch.int32, device="cuda")
+    stopped = torch.zeros(3, 2, dtype=torch.uint8, device="cuda")
+    seeds = seeds_tensor([1, 2])
+    noop = lambda *a: None
+    with pytest.raises(B.DgError, match="n_canvases"):
+        ctx.dg_generate(seeds, 0, noop, None, logits, tokens, steps, stopped)
+    with pytest.raises(B.DgError, match="check_every"):
+        ctx.dg_generate(seeds, 3, noop, None, logits, tokens, steps, stopped, check_every=-1)
+    with pytest.raises(B.DgError, match="tokens is NULL"):
+        ctx.dg_generate(seeds, 3, noop, None, logits, None, steps, stopped)
+    final = torch.zeros(2, L, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.DgError, match="check_every"):
+        ctx.dg_run_canvas_resident(seeds, noop, logits, final, steps[0], stopped[0], check_every=-2)
+
+    class Boom(RuntimeError):
+        pass
+
+    def bad_cache(k, canvas_ptr, stream):
+        if k == 1:
+            raise Boom("cache update failed")
+
+    with pytest.raises(Boom):
+        ctx.dg_generate(seeds, 3, noop, bad_cache, logits, tokens, steps, stopped, check_every=2)
+    torch.cuda.synchronize()
+    # canvas 0 and 1 ran (zero logits never stop: the 6-step cap), canvas 2 did not start
+    assert steps.cpu().numpy()[:2].tolist() == [[6, 6], [6, 6]]
+
+    def bad_denoise(k, step, canvas_ptr, active_ptr, lg, stream):
+        if k == 1 and step == 2:
+            raise Boom("denoiser failed")
+
+    with pytest.raises(Boom):
+        ctx.dg_generate(seeds, 3, bad_denoise, None, logits, tokens, steps, stopped)
+    torch.cuda.synchronize()
+    # the context stays usable
+    ctx.dg_generate(seeds, 3, noop, None, logits, tokens, steps, stopped, check_every=3)
+    assert (steps.cpu().numpy() == 6).all() and not stopped.cpu().numpy().any()
+    per, total = B.tokens_per_forward(steps.cpu().numpy(), L)
+    assert total == 3 * L / (3 * 6 + 3)
