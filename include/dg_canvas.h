@@ -320,9 +320,12 @@ dg_status dg_generate(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t n_c
  * The pages give no shapes; this library reads it as the expected token
  * embedding under the step's tempered prediction:
  *   out[r, n] = sum_v softmax(z_r / T_c)_v * embed[v, n],  n < d,
- * for the B*L rows r of the logits (c = r / L), computed in fp32 on the
- * matrix cores (products and sums in fp32, summation order unspecified); with
- * d = 30 at V = 262144 the embedding holds 7,864,320 parameters.
+ * for the B*L rows r of the logits (c = r / L), at fp32 accuracy on the
+ * matrix cores: probabilities and embedding values are fp32, each product is
+ * formed from exact three-part bf16 splits of its factors to within about
+ * one fp32 rounding, and sums run in fp32 (order unspecified but fixed, so
+ * the result is reproducible). With d = 30 at V = 262144 the embedding holds
+ * 7,864,320 parameters.
  *   logits, dtype, row_stride  as for dg_canvas_stats
  *   temperature  device float [B], each > 0
  *   argmax       device int32 [B*L]: the row's largest-logit id, as
