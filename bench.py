@@ -53,6 +53,101 @@ def _traffic(bytes_per_launch):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _oracle_canvas_worker(job):
+    """One canvas's oracle step in a fresh process (no GPU): builds its
+    logits on the CPU and returns the seconds O.step takes."""
+    os.environ["HIP_VISIBLE_DEVICES"] = ""
+    import numpy as np
+    import torch
+    torch.set_num_threads(1)
+    from canvas_sampler_amd import synth
+    from oracle import sampler as O
+    gen, seed, L, V = job
+    z = synth.sharpening_logits(gen, 0, L, V, m0_max=8.0, dtype=torch.bfloat16)
+    zh = z.to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    O.step(zh, np.float32(0.8), seed, 0)
+    return time.perf_counter() - t0
+
+
+def cpu_full_leg(workers):
+    """The oracle's rates on the host for the configurations of the scope
+    table: single steps of C1 (V = 4096 fp32), C2 (262144 bf16) and C4
+    (262144 fp32 iid N(0, 0.05)) on one thread, the full C2 run (10 steps) on
+    one thread, and one step of C3 (16 canvases of C2's shape) with one
+    canvas per process over `workers` processes. The oracle handles one canvas
+    at a time on one thread, so a single canvas gains nothing from more
+    cores. Inputs come from the CPU generators (same shapes and
+    distributions as the GPU runs)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    from canvas_sampler_amd import synth
+    from oracle import sampler as O
+
+    torch.set_num_threads(1)
+    L, V = 256, 262144
+    out = {"threads_per_process": 1}
+
+    def timed(fn, reps=1):
+        best = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+            best = dt if best is None or dt < best else best
+        return best
+
+    z1 = synth.margin_logits(1001, L, 4096, m_max=12.0).to(torch.float64).numpy()
+    t = timed(lambda: O.step(z1, np.float32(0.8), 0, 0), reps=3)
+    out["c1_step_s"], out["c1_positions_per_s"] = t, L / t
+    z2 = synth.sharpening_logits(1002, 0, L, V, m0_max=6.0, dtype=torch.bfloat16).to(torch.float64).numpy()
+    t = timed(lambda: O.step(z2, np.float32(0.8), 0, 0), reps=2)
+    out["c2_step_s"], out["c2_positions_per_s"] = t, L / t
+    z4 = synth.iid_normal_logits(1004, 0, L, V, variance=0.05).to(torch.float64).numpy()
+    t = timed(lambda: O.step(z4, np.float32(0.8), 0, 0), reps=1)
+    out["c4_step_s"], out["c4_positions_per_s"] = t, L / t
+    del z1, z2, z4
+    # the full C2 run: the sharpening denoiser's logits for every step made
+    # beforehand, so that the timed loop is the oracle's own
+    steps_z = {}
+    for s in range(48):
+        steps_z[s] = synth.sharpening_logits(1002, s, L, V, m0_max=6.0, dtype=torch.bfloat16)
+        if s >= 15:
+            break
+    n_used = [0]
+
+    def den(s, canvas):
+        n_used[0] = s + 1
+        z = steps_z.get(s)
+        if z is None:
+            z = synth.sharpening_logits(1002, s, L, V, m0_max=6.0, dtype=torch.bfloat16)
+        return z.to(torch.float64).numpy()
+
+    t0 = time.perf_counter()
+    _, n, stopped, _ = O.run(den, 0, L, V, n_sched=16)
+    out["c2_run_s"], out["c2_run_steps"], out["c2_run_stopped"] = time.perf_counter() - t0, n, bool(stopped)
+    out["c2_run_note"] = "includes widening each step's bf16 logits to fp64"
+    del steps_z
+    jobs = [((1003 << 32) | c, c, L, V) for c in range(16)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(processes=workers) as pool:
+        t0 = time.perf_counter()
+        per = pool.map(_oracle_canvas_worker, jobs)
+        wall = time.perf_counter() - t0
+    used = min(workers, len(jobs))
+    out["c3_step_workers"] = used
+    out["c3_step_oracle_s_per_canvas"] = [round(x, 3) for x in per]
+    out["c3_positions_per_s"] = len(jobs) * L / (sum(per) / used)
+    out["c3_note"] = ("one canvas per task over the worker processes, each generating its own logits; "
+                      "the rate divides the 16 canvases' positions by their summed oracle time over "
+                      "the workers")
+    out["c3_pool_wall_s"] = wall
+    return out
+
+
 def _time_graphs(graphs, k, torch):
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -461,6 +556,10 @@ def main():
     ap.add_argument("--lmhead-only", action="store_true",
                     help="only run the LM-head product and step (for counter runs)")
     ap.add_argument("--lmhead-steps", type=int, default=10)
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="only time the oracle on the host for C1-C4 single steps, the full C2 run "
+                         "and C3 over processes (a few minutes; no GPU work)")
+    ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 20 plain 128 MiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -468,6 +567,11 @@ def main():
         print("bench.py measures one GPU: the sampler has no multi-GPU path (independent "
               "canvases would shard across GPUs without any communication)", file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_full:
+        print(json.dumps({"cpu_oracle": cpu_full_leg(max(1, args.cpu_workers)),
+                          "host_cpus": os.cpu_count()}), flush=True)
+        return
 
     import numpy as np
     import torch
