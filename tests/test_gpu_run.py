@@ -454,3 +454,53 @@ def test_resident_run_graph_replays():
         assert [bool(x) for x in stopped.cpu().tolist()] == est
         assert np.array_equal(final.cpu().numpy(), ef)
     print("graph replays equal the eager runs; steps", {k: v[1] for k, v in eager.items()})
+
+
+def test_resume_from_a_checkpoint_equals_the_uninterrupted_run():
+    # the loop state between steps is the canvas, the previous argmax canvas
+    # and the step index; a run stopped after step 3, its state copied to the
+    # host, and continued on a fresh context must finish exactly like
+    # dg_run_canvas (single canvas, sharpening stand-in, V = 16384)
+    L, V, gen, seed = 256, 16384, 3002, 41
+    require_gpu()
+    params = B.params_default(canvas_len=L, vocab=V, temp_steps=16)
+    den = _sharpening_denoiser([gen], L, V, 6.0, torch.bfloat16)
+    final_ref, steps_ref, stopped_ref, _ = _run_gpu(B.Context(params, max_batch=1), [seed], den,
+                                                    torch.bfloat16)
+
+    def run_steps(ctx, canvas, prev, s0, s1):
+        """Steps s0 .. s1-1 from (canvas, prev); returns the new state and
+        (steps used, stopped) once the stop fires."""
+        logits = torch.empty(L, V, dtype=torch.bfloat16, device="cuda")
+        am = [torch.empty(L, dtype=torch.int32, device="cuda") for _ in range(2)]
+        nxt = torch.empty(L, dtype=torch.int32, device="cuda")
+        stop = torch.empty(1, dtype=torch.uint8, device="cuda")
+        for s in range(s0, s1):
+            synth.sharpening_logits(gen, s, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda",
+                                    out=logits)
+            out = ctx.step_out(nxt, argmax_out=am[s & 1], stop_out=stop)
+            t = torch.tensor([B.dg_temperature(params, s)], device="cuda")
+            ctx.dg_sampler_step(logits, t, s, seeds_tensor([seed]), out, prev_argmax=prev)
+            torch.cuda.synchronize()
+            if stop.item():
+                return nxt.clone(), am[s & 1].clone(), (s + 1, True)
+            canvas, prev = nxt.clone(), am[s & 1].clone()
+        return canvas, prev, None
+
+    ctx = B.Context(params, max_batch=1)
+    canvas = torch.empty(1, L, dtype=torch.int32, device="cuda")
+    ctx.dg_canvas_init(seeds_tensor([seed]), canvas)
+    canvas, prev, done = run_steps(ctx, canvas.view(-1), None, 0, 3)
+    assert done is None
+    saved = (canvas.cpu().numpy(), prev.cpu().numpy())
+    ctx.close()
+    del canvas, prev
+    torch.cuda.synchronize()
+    ctx2 = B.Context(params, max_batch=1)
+    canvas = torch.as_tensor(saved[0], device="cuda")
+    prev = torch.as_tensor(saved[1], device="cuda")
+    _, final, done = run_steps(ctx2, canvas, prev, 3, 48)
+    assert done is not None, "the resumed run did not stop"
+    assert done == (steps_ref[0], stopped_ref[0])
+    assert np.array_equal(final.cpu().numpy(), final_ref[0])
+    print(f"resumed after 3 steps; stops after {done[0]} steps like the uninterrupted run")
