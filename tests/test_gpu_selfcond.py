@@ -127,3 +127,43 @@ def test_rejects_bad_arguments():
     with pytest.raises(B.DgError, match="argmax"):
         ctx._chk(B.lib().dg_self_condition(ctx.handle, 1, z.data_ptr(), B.DG_DTYPE_F32, 64, t.data_ptr(),
                                            None, E.data_ptr(), 4, out.data_ptr(), None))
+
+
+def test_extreme_rows():
+    # rows with -inf logits, a near one-hot row (margin 1000), a constant row,
+    # and a very low temperature: the softmax stays exact relative to the
+    # row's maximum, so every row still matches the oracle
+    L, V, d = 64, 4096, 30
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=2)
+    z = synth.margin_logits(77, 2 * L, V, m_max=8.0, dtype=torch.float32, device="cuda")
+    z[0, ::3] = float("-inf")
+    z[1, :V - 1] = float("-inf")          # one finite logit: p is one-hot
+    z[2, 17] += 1000.0                     # near one-hot
+    z[3, :] = 0.25                         # uniform row
+    z[4, 4000:] = float("-inf")            # the tail of the row impossible
+    t = torch.tensor([0.8, 0.05], device="cuda")   # canvas 1 at a very low temperature
+    E = synth.selfcond_embedding(9, V, d, device="cuda")
+    h = torch.empty(2 * L, device="cuda")
+    am = torch.empty(2 * L, dtype=torch.int32, device="cuda")
+    smp = torch.empty(2 * L, dtype=torch.int32, device="cuda")
+    ctx.dg_canvas_stats(z, t, 0, seeds_tensor([1, 2]), h, am, smp, batch=2)
+    out = torch.empty(2 * L, d, device="cuda")
+    ctx.dg_self_condition(z, t, am, E, out, batch=2)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().astype(np.float64)
+    zh = host_values(z)
+    Eh = E.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for c in range(2):
+        rows = slice(c * L, (c + 1) * L)
+        T = np.float32(t[c].item())
+        want = SC.self_condition(zh[rows], T, Eh)
+        mag = SC.magnitude(zh[rows], T, Eh)
+        assert np.all(np.isfinite(g[rows]))
+        ratio = np.abs(g[rows] - want) / mag
+        assert np.all(ratio <= TOL_BOUND)
+        worst = max(worst, float(ratio.max()))
+    assert worst <= TOL_TYPICAL, worst
+    assert np.allclose(g[1], Eh[V - 1], rtol=0, atol=1e-6)   # one-hot row picks its embedding row
+    print(f"extreme rows: max |err| / sum p|E| = {worst:.2e}")
