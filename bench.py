@@ -459,6 +459,16 @@ def selfcond_leg(torch, B, synth, k=200, d=30):
         stats(r)
         sc(r)
 
+    canvas = torch.empty(L, dtype=torch.int32, device="cuda")
+    stop = torch.empty(1, dtype=torch.uint8, device="cuda")
+
+    def step_sc(r):
+        out = ctx.step_out(canvas, argmax_out=am[r], stop_out=stop)
+        ctx.dg_sampler_step_selfcond(logits[r], temps[r], r, seeds, E, out_sc, out,
+                                     prev_argmax=am[(r + 1) % R])
+
+    out_sc = torch.empty(L, d, device="cuda")
+
     def timed(fn):
         for i in range(20):
             fn(i % R)
@@ -477,6 +487,7 @@ def selfcond_leg(torch, B, synth, k=200, d=30):
             stats(r)
         t_sc = timed(sc)
         t_stage = timed(stage)
+        t_step_sc = timed(step_sc)
     flops = 2.0 * L * V * d
     nbytes = L * V * 2 + V * d * 4
     ctx.close()
@@ -485,7 +496,8 @@ def selfcond_leg(torch, B, synth, k=200, d=30):
             "peak_fp32_mfma_tflops": PEAK_FP32_MFMA_TFLOPS,
             "mfma_frac": flops / t_sc * 1e-6 / PEAK_FP32_MFMA_TFLOPS,
             "read_gbs": nbytes / t_sc * 1e-3, "flops_per_launch": flops, "bytes_per_launch": nbytes,
-            "stage_us": t_stage}
+            "stage_us": t_stage, "step_with_selfcond_us": t_step_sc,
+            "step_with_selfcond_per_s": 1e6 / t_step_sc}
 
 
 def lmhead_leg(args, torch, B, synth):

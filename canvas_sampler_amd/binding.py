@@ -29,7 +29,7 @@ EXPORTS = ["dg_params_default", "dg_params_check", "dg_create", "dg_destroy", "d
            "dg_get_params", "dg_temperature", "dg_set_stats_split", "dg_canvas_init",
            "dg_canvas_stats", "dg_accept_renoise", "dg_sampler_step", "dg_run_canvas",
            "dg_run_canvas_resident", "dg_generate", "dg_tokens_per_forward",
-           "dg_self_condition",
+           "dg_self_condition", "dg_sampler_step_selfcond",
            "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_version"]
 
 
@@ -93,6 +93,8 @@ def lib():
                             vp, vp, i32, vp],
             "dg_tokens_per_forward": [vp, i32, i32, i32, vp, vp],
             "dg_self_condition": [vp, i32, vp, ctypes.c_int, i64, vp, vp, vp, i32, vp, vp],
+            "dg_sampler_step_selfcond": [vp, i32, vp, ctypes.c_int, i64, vp, i32, vp, vp, vp, vp, i32, vp,
+                                         ctypes.POINTER(DgStepOut), vp],
             "dg_lmhead_logits": [vp, i32, vp, vp, i32, vp, i64, vp],
             "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp,
                                        ctypes.POINTER(DgStepOut), vp],
@@ -296,6 +298,18 @@ class Context:
         self._chk(lib().dg_self_condition(self.handle, B, _ptr(logits), _dtype_code(logits), stride,
                                           _ptr(temperature), _ptr(argmax), _ptr(embed),
                                           embed.shape[1], _ptr(out), _stream(stream)))
+
+    def dg_sampler_step_selfcond(self, logits, temperature, step, seeds, embed, selfcond_out, out,
+                                 prev_argmax=None, active=None, batch=None, row_stride=None,
+                                 stream=None):
+        """dg_sampler_step with the self-conditioning matmul (embed [V, d]
+        fp32 -> selfcond_out [B*L, d] fp32) after the statistics pass."""
+        B = batch if batch is not None else seeds.shape[0]
+        stride = row_stride if row_stride is not None else logits.stride(0)
+        self._chk(lib().dg_sampler_step_selfcond(
+            self.handle, B, _ptr(logits), _dtype_code(logits), stride, _ptr(temperature), step,
+            _ptr(seeds), _ptr(prev_argmax), _ptr(active), _ptr(embed), embed.shape[1],
+            _ptr(selfcond_out), ctypes.byref(out), _stream(stream)))
 
     def dg_generate(self, seeds, n_canvases, denoise, cache_update, logits_scratch, tokens,
                     steps_used, stopped, check_every=0, stream=None):

@@ -569,6 +569,39 @@ dg_status check_run(dg_ctx* ctx, int32_t B, const uint64_t* seeds, bool has_deno
   return DG_OK;
 }
 
+dg_status check_selfcond(dg_ctx* ctx, const float* embed, int32_t d, const float* out) {
+  if (!embed) return set_err(ctx, DG_ERR_INVALID_ARG, "embed is NULL");
+  if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "selfcond output is NULL");
+  if (d < 1 || d > 31) return set_err(ctx, DG_ERR_INVALID_ARG, "d = %d is outside 1..31", d);
+  if ((reinterpret_cast<uintptr_t>(embed) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "embed and the selfcond output must be 4-byte aligned");
+  return DG_OK;
+}
+
+dg_status enqueue_selfcond(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype, int64_t row_stride,
+                           const float* temperature, const int32_t* argmax, const uint8_t* active,
+                           const float* embed, int32_t d, float* out, hipStream_t s) {
+  dg::SelfCondArgs a{};
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = ctx->p.vocab;
+  a.canvas_len = ctx->p.canvas_len;
+  a.rows = B * ctx->p.canvas_len;
+  a.temperature = temperature;
+  a.argmax = argmax;
+  a.active = active;
+  a.embed = embed;
+  a.d = d;
+  a.out = out;
+  dg::choose_self_cond_slices(a.rows, a.vocab, &a.nslice, &a.kslice);
+  a.rows_pad = (a.rows + dg::kScRowTile - 1) / dg::kScRowTile * dg::kScRowTile;
+  a.partials = ctx->sc_partials;
+  if (a.nslice > 1 && static_cast<int64_t>(a.nslice) * a.rows_pad * 32 > ctx->sc_partial_floats)
+    return set_err(ctx, DG_ERR_DEVICE, "self-conditioning scratch too small (internal error)");
+  DG_CHECK_HIP(ctx, dg::launch_self_cond(a, dtype == DG_DTYPE_BF16, s));
+  return DG_OK;
+}
+
 // The device-resident loop over the steps of B canvases: state initialised on
 // the device, then per step the denoiser (denoise(step)), the statistics pass
 // and the acceptance kernel, which advances the loop state itself. With
@@ -737,30 +770,38 @@ dg_status dg_self_condition(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype
   if ((st = check_logits(ctx, logits, dtype, row_stride)) != DG_OK) return st;
   if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
   if (!argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "argmax is NULL");
-  if (!embed) return set_err(ctx, DG_ERR_INVALID_ARG, "embed is NULL");
-  if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
-  if (d < 1 || d > 31) return set_err(ctx, DG_ERR_INVALID_ARG, "d = %d is outside 1..31", d);
-  if ((reinterpret_cast<uintptr_t>(embed) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
-    return set_err(ctx, DG_ERR_UNSUPPORTED, "embed and out must be 4-byte aligned");
-  dg::SelfCondArgs a{};
-  a.logits = logits;
-  a.row_stride = row_stride;
-  a.vocab = ctx->p.vocab;
-  a.canvas_len = ctx->p.canvas_len;
-  a.rows = B * ctx->p.canvas_len;
-  a.temperature = temperature;
-  a.argmax = argmax;
-  a.embed = embed;
-  a.d = d;
-  a.out = out;
-  dg::choose_self_cond_slices(a.rows, a.vocab, &a.nslice, &a.kslice);
-  a.rows_pad = (a.rows + dg::kScRowTile - 1) / dg::kScRowTile * dg::kScRowTile;
-  a.partials = ctx->sc_partials;
-  if (a.nslice > 1 && static_cast<int64_t>(a.nslice) * a.rows_pad * 32 > ctx->sc_partial_floats)
-    return set_err(ctx, DG_ERR_DEVICE, "self-conditioning scratch too small (internal error)");
+  if ((st = check_selfcond(ctx, embed, d, out)) != DG_OK) return st;
   DeviceGuard guard(ctx->device);
-  DG_CHECK_HIP(ctx, dg::launch_self_cond(a, dtype == DG_DTYPE_BF16, static_cast<hipStream_t>(stream)));
-  return DG_OK;
+  return enqueue_selfcond(ctx, B, logits, dtype, row_stride, temperature, argmax, nullptr, embed, d, out,
+                          static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_sampler_step_selfcond(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                                   int64_t row_stride, const float* temperature, int32_t step,
+                                   const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                                   const float* embed, int32_t d, float* selfcond_out, const dg_step_out* out,
+                                   void* stream) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_batch(ctx, B);
+  if (st != DG_OK) return st;
+  if ((st = check_logits(ctx, logits, dtype, row_stride)) != DG_OK) return st;
+  if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
+  if (step < 0) return set_err(ctx, DG_ERR_INVALID_ARG, "step = %d is negative", step);
+  if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
+  if (!out->canvas_out) return set_err(ctx, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
+  if ((st = check_selfcond(ctx, embed, d, selfcond_out)) != DG_OK) return st;
+  DeviceGuard guard(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;
+  int32_t* am = out->argmax_out ? out->argmax_out : ctx->argmax[0];
+  int32_t* smp = out->sample_out ? out->sample_out : ctx->sample;
+  st = enqueue_stats(ctx, B, logits, dtype, row_stride, temperature, step, nullptr, seeds, active, ent, am,
+                     smp, s);
+  if (st != DG_OK) return st;
+  st = enqueue_selfcond(ctx, B, logits, dtype, row_stride, temperature, am, active, embed, d, selfcond_out, s);
+  if (st != DG_OK) return st;
+  return enqueue_accept(ctx, B, ent, am, smp, step, nullptr, seeds, prev_argmax, active, out, false, s);
 }
 
 dg_status dg_tokens_per_forward(const int32_t* steps_used, int32_t n_canvases, int32_t B,

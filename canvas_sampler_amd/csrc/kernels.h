@@ -97,6 +97,7 @@ struct SelfCondArgs {
   int32_t rows;
   const float* temperature;  // [rows / canvas_len]
   const int32_t* argmax;   // [rows]: id of each row's largest logit
+  const uint8_t* active;   // [rows / canvas_len] or null: rows of inactive canvases are skipped
   const float* embed;      // fp32 [vocab, d]
   int32_t d;               // 1..31
   float* out;              // fp32 [rows, d]

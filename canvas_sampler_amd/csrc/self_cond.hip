@@ -72,12 +72,17 @@ struct ZTile {
 
 // This thread's pieces of a chunk, loaded with whole lines per row: piece
 // p = tid + kScThreads * i is 16-byte piece p % kPiecesPerRow of tile row
-// p / kPiecesPerRow. Rows past the batch and ids at or past `end` read as
+// p / kPiecesPerRow. Rows past the batch or of inactive canvases, and ids at or past `end`, read as
 // -inf, so their probability is exactly 0 and no later step needs a bound
 // check; only a piece that straddles `end` (V not a multiple of the piece) is
 // masked element by element. Pieces never cross the row's padded end: the row
 // stride is a multiple of 16 bytes and every piece that is read starts below
 // `end` <= V.
+// Whether `row` takes part: inside the batch and of an active canvas.
+__device__ __forceinline__ bool row_live(const SelfCondArgs& a, int32_t row) {
+  return row < a.rows && (a.active == nullptr || a.active[row / a.canvas_len] != 0);
+}
+
 template <bool kBf16>
 struct Raw {
   uint4 q[ZTile<kBf16>::kPieces];
@@ -94,7 +99,7 @@ __device__ __forceinline__ void load_chunk(const SelfCondArgs& a, int32_t row0, 
     const int32_t row = row0 + piece / G::kPiecesPerRow;
     const int64_t id = kc + static_cast<int64_t>(piece % G::kPiecesPerRow) * G::kPerPiece;
     uint4 w = make_uint4(kNegInf2, kNegInf2, kNegInf2, kNegInf2);
-    if (row < a.rows && id < end) {
+    if (row_live(a, row) && id < end) {
       const int64_t off = static_cast<int64_t>(row) * a.row_stride + id;
       if constexpr (kBf16)
         w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.logits) + off);
@@ -204,10 +209,10 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
   const int trow = wave * 32 + (lane & 31);  // this lane's row in the tile
   const int32_t row = row0 + trow;
 
-  // rows past the batch are all -inf in the tile: with c = 1 and zmax*c = 0
-  // their probabilities are exactly 0
+  // rows past the batch or of inactive canvases are all -inf in the tile:
+  // with c = 1 and zmax*c = 0 their probabilities are exactly 0
   float c = 1.0f, mc = 0.0f;
-  if (row < a.rows) {
+  if (row_live(a, row)) {
     const int64_t off = static_cast<int64_t>(row) * a.row_stride;
     int32_t am = a.argmax[row];
     am = am < 0 ? 0 : (am >= a.vocab ? a.vocab - 1 : am);
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
     for (int r = 0; r < 16; ++r) {
       const float s = __shfl(acc[r], (lane & 32) | a.d);  // the normaliser of this row
       const int32_t gr = wrow0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (gr < a.rows && n < a.d) a.out[static_cast<int64_t>(gr) * a.d + n] = acc[r] / s;
+      if (n < a.d && row_live(a, gr)) a.out[static_cast<int64_t>(gr) * a.d + n] = acc[r] / s;
     }
   } else {
     float* part = a.partials + static_cast<int64_t>(slice) * a.rows_pad * 32;
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
 __global__ __launch_bounds__(256) void self_cond_reduce_kernel(SelfCondArgs a) {
   __shared__ float4 s_part[32][8];
   const int32_t r = static_cast<int32_t>(blockIdx.x);
+  if (a.active != nullptr && a.active[r / a.canvas_len] == 0) return;  // uniform over the workgroup
   const int t = threadIdx.x, quad = t & 7, group = t >> 3;
   const int64_t stride = static_cast<int64_t>(a.rows_pad) * 32;
   const float* base = a.partials + static_cast<int64_t>(r) * 32 + 4 * quad;

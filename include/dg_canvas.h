@@ -340,6 +340,18 @@ dg_status dg_self_condition(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype
                            const float* temperature, const int32_t* argmax, const float* embed, int32_t d,
                            float* out, void* stream);
 
+/* The sampling stage of one step with the self-conditioning matmul fused
+ * after the statistics pass (boxwrench.dev, hardware paragraph: the stage runs
+ * the full-vocabulary softmax and the self-conditioning matmul together):
+ * dg_canvas_stats, then dg_self_condition on its argmax (selfcond_out
+ * [B*L, d] fp32, written for the rows of active canvases only), then
+ * dg_accept_renoise. Arguments as for dg_sampler_step and dg_self_condition. */
+dg_status dg_sampler_step_selfcond(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
+                                   int64_t row_stride, const float* temperature, int32_t step,
+                                   const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                                   const float* embed, int32_t d, float* selfcond_out, const dg_step_out* out,
+                                   void* stream);
+
 /* Tokens per forward pass of finished dg_generate streams (boxwrench.dev,
  * "Finding", hardware paragraph: TPF counts the extra forward pass that
  * updates the cache; throughput is TPS = TPF / t_fwd). A stream's forwards

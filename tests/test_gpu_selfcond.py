@@ -167,3 +167,56 @@ def test_extreme_rows():
     assert worst <= TOL_TYPICAL, worst
     assert np.allclose(g[1], Eh[V - 1], rtol=0, atol=1e-6)   # one-hot row picks its embedding row
     print(f"extreme rows: max |err| / sum p|E| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("Bn,V", [(3, 4096), (520, 1024)])
+def test_step_with_selfcond_matches_separate_calls_and_skips_inactive(Bn, V):
+    # dg_sampler_step_selfcond = statistics, self-conditioning on their
+    # argmax, acceptance: the step outputs equal dg_sampler_step's bit for bit;
+    # rows of inactive canvases keep their previous self-conditioning values;
+    # active rows match the oracle. B = 520 fills the grid with row tiles, so
+    # each workgroup divides in place (no partial tiles).
+    L, d = 256, 30
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=Bn)
+    z = torch.cat([synth.margin_logits(300 + c, L, V, m_max=8.0, dtype=torch.bfloat16, device="cuda")
+                   for c in range(Bn)])
+    E = synth.selfcond_embedding(11, V, d, device="cuda")
+    t = torch.tensor([0.8 - 0.3 * (c % 3) / 2 for c in range(Bn)], device="cuda")
+    seeds = seeds_tensor(list(range(Bn)))
+    active = torch.tensor([0 if c % 3 == 1 else 1 for c in range(Bn)], dtype=torch.uint8, device="cuda")
+    prev = torch.zeros(Bn * L, dtype=torch.int32, device="cuda")
+
+    def outs():
+        return dict(canvas_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    argmax_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    sample_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    entropy_out=torch.full((Bn * L,), -1.0, device="cuda"),
+                    accept_out=torch.full((Bn * L,), 9, dtype=torch.uint8, device="cuda"),
+                    n_accept_out=torch.full((Bn,), -1, dtype=torch.int32, device="cuda"),
+                    stop_out=torch.full((Bn,), 9, dtype=torch.uint8, device="cuda"))
+
+    a, b = outs(), outs()
+    ctx.dg_sampler_step(z, t, 2, seeds, ctx.step_out(**a), prev_argmax=prev, active=active)
+    sc = torch.full((Bn * L, d), 7.0, device="cuda")
+    ctx.dg_sampler_step_selfcond(z, t, 2, seeds, E, sc, ctx.step_out(**b), prev_argmax=prev, active=active)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    g = sc.cpu().numpy().astype(np.float64)
+    act = active.cpu().numpy()
+    for c in range(Bn):
+        rows = slice(c * L, (c + 1) * L)
+        if not act[c]:
+            assert np.all(g[rows] == 7.0), f"inactive canvas {c} was written"
+    check = [c for c in range(Bn) if act[c]][:4]
+    Eh = E.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for c in check:
+        rows = slice(c * L, (c + 1) * L)
+        zh = host_values(z[rows])
+        T = np.float32(t[c].item())
+        ratio = np.abs(g[rows] - SC.self_condition(zh, T, Eh)) / SC.magnitude(zh, T, Eh)
+        worst = max(worst, float(ratio.max()))
+    assert worst <= TOL_TYPICAL, worst
+    print(f"B={Bn} V={V}: step outputs identical; active rows max |err| / sum p|E| = {worst:.2e}")
