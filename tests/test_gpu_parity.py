@@ -277,3 +277,31 @@ def test_sampler_step_full_outputs_match_oracle_c1():
                              g["argmax_out"], float(np.float32(0.1)), float(np.float32(0.005)))
     assert g["stop_out"][0] == 0
     print("C1 step: n_accept", k, "max dH", dh)
+
+
+def test_split_rows_repeatable_over_many_launches():
+    # rows split over several workgroups are finished by the last of them,
+    # which reads the others' partials after a release/acquire hand-off; a
+    # missing ordering would show up as a run whose integers or entropies
+    # differ from the others. 600 launches, bit for bit.
+    L, V = 256, 262144
+    ctx = _ctx(L, V)
+    zs = [synth.sharpening_logits(1002, s, L, V, m0_max=6.0, dtype=torch.bfloat16, device="cuda")
+          for s in (0, 5)]
+    t = torch.tensor([0.7], device="cuda")
+    seeds = seeds_tensor([3])
+    n = 300
+    for nsplit in (2, 4):
+        ctx.set_stats_split(nsplit)
+        h = torch.empty(n, L, device="cuda")
+        am = torch.empty(n, L, dtype=torch.int32, device="cuda")
+        smp = torch.empty(n, L, dtype=torch.int32, device="cuda")
+        for i in range(n):
+            ctx.dg_canvas_stats(zs[i & 1], t, 1, seeds, h[i], am[i], smp[i])
+        torch.cuda.synchronize()
+        for par in (0, 1):
+            idx = torch.arange(par, n, 2, device="cuda")
+            for x in (h, am, smp):
+                sel = x[idx]
+                assert torch.equal(sel, sel[:1].expand_as(sel)), f"nsplit {nsplit}: launches differ"
+    ctx.set_stats_split(0)
