@@ -119,3 +119,21 @@ def test_tokens_per_forward_matches_oracle():
         B.tokens_per_forward(np.array([[3, -1]]), 256)
     st = B.lib().dg_tokens_per_forward(None, 1, 1, 256, None, None)
     assert st == B.DG_ERR_INVALID_ARG and "steps_used" in B.lib().dg_last_error(None).decode()
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # the product path has no fallback: without the built library, loading it
+    # raises (checked in a fresh interpreter whose library path points nowhere)
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from canvas_sampler_amd import binding as B\n"
+        "B._LIB_PATH = %r\n"
+        "try:\n"
+        "    B.lib()\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "else:\n"
+        "    print('loaded')\n" % (ROOT, str(tmp_path / "libdgcanvas.so")))
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "no fallback" in r.stdout
