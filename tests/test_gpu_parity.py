@@ -305,3 +305,46 @@ def test_split_rows_repeatable_over_many_launches():
                 sel = x[idx]
                 assert torch.equal(sel, sel[:1].expand_as(sel)), f"nsplit {nsplit}: launches differ"
     ctx.set_stats_split(0)
+
+
+def test_c3_sixteen_canvases_step_matches_oracle():
+    # C3 at its full size (16 canvases x 256 positions x 262144 bf16, the
+    # sharpening stand-in with m0 ~ U[0, 8] and per-canvas generator seeds,
+    # sampler seeds c): one whole step through the persistent row loop, the
+    # launch the benchmark's B = 16 line times. Sampled rows of every canvas
+    # against the oracle; each canvas's commits and stop against the rules.
+    L, V, Bn = 256, 262144, 16
+    ctx = _ctx(L, V, max_batch=Bn)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert Bn * L > cu
+    step = 6  # margins m0 + 9: a mix of confident and open positions
+    z = torch.cat([synth.sharpening_logits((1003 << 32) | c, step, L, V, m0_max=8.0, dtype=torch.bfloat16,
+                                           device="cuda") for c in range(Bn)])
+    t = B.dg_temperature(B.params_default(canvas_len=L, vocab=V), step)
+    temps = torch.full((Bn,), t, device="cuda")
+    seeds = list(range(Bn))
+    bufs = dict(canvas_out=torch.empty(Bn * L, dtype=torch.int32, device="cuda"),
+                argmax_out=torch.empty(Bn * L, dtype=torch.int32, device="cuda"),
+                sample_out=torch.empty(Bn * L, dtype=torch.int32, device="cuda"),
+                accept_out=torch.empty(Bn * L, dtype=torch.uint8, device="cuda"),
+                entropy_out=torch.empty(Bn * L, device="cuda"),
+                n_accept_out=torch.empty(Bn, dtype=torch.int32, device="cuda"),
+                mean_entropy_out=torch.empty(Bn, device="cuda"),
+                stop_out=torch.empty(Bn, dtype=torch.uint8, device="cuda"))
+    ctx.dg_sampler_step(z, temps, step, seeds_tensor(seeds), ctx.step_out(**bufs))
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in bufs.items()}
+    for c in range(Bn):
+        rows = np.array([0, 37, 128, 255]) + (c * 7) % 200
+        rows = np.unique(np.clip(rows, 0, L - 1))
+        at = c * L + rows
+        zh = host_values(z[torch.as_tensor(at, device="cuda")])
+        compare_stats(zh, np.float32(t), seeds[c], rows, step, g["entropy_out"][at], g["argmax_out"][at],
+                      g["sample_out"][at])
+        sl = slice(c * L, (c + 1) * L)
+        ren = O.uniform_tokens(seeds[c], L, step, V, OP.TAG_RENOISE)
+        check_decision_rules(g["entropy_out"][sl], g["accept_out"][sl].astype(bool), g["n_accept_out"][c],
+                             g["sample_out"][sl], g["canvas_out"][sl], ren, g["mean_entropy_out"][c],
+                             g["stop_out"][c], None, g["argmax_out"][sl], float(np.float32(0.1)),
+                             float(np.float32(0.005)))
+    print("C3 step: 16 canvases, commits", g["n_accept_out"].tolist())
