@@ -444,18 +444,16 @@ struct WaveResult {
   int64_t best_base = 0;
 };
 
-// The Philox call behind the Gumbels of the lane's current group of four
-// blocks: blocks that differ only in bits 9-10 of j (chunks 8 apart, so four
-// consecutive blocks of a wave whose first chunk is a multiple of 32 chunks
-// away from the split's start) share the call with counter c0 = j with those
-// bits cleared, block j taking word (j >> 9) & 3. The words are kept as a
-// shift register: the wave's block i takes w0 (a call at i % 4 == 0 refills
-// it), so no word is picked by a runtime index.
+// The Philox call behind a block's Gumbel: blocks that differ only in bits
+// 9-10 of j (chunks 8 apart: chunk c lies in the group of four chunks
+// c & ~24) share the call with counter c0 = j with those bits cleared, block
+// j taking word (j >> 9) & 3.
 constexpr int32_t kDrawGroupChunks = 32;  // chunks spanned by one group of four block draws
 
-struct BlockWords {
-  uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-};
+// Share of a SIMD pair's chunks that its younger wave streams, in
+// sixteenths (measured at 256 x 262144 bf16: 8/16 27.4 us, 6/16 26.7 us,
+// 5/16 26.7 us, 4/16 27.4 us).
+constexpr int32_t kYoungShare16 = 6;
 
 // Per-row constants of a pass.
 struct RowConsts {
@@ -466,15 +464,96 @@ struct RowConsts {
   float inv_t;      // 1 / T: z/T as z * (1/T), within an ulp of the quotient
 };
 
+__device__ __forceinline__ Words4 group_words(int32_t group_chunk, int lane, const RowConsts& rc) {
+  return philox4x32_10(static_cast<uint32_t>(group_chunk * kSlots + lane), static_cast<uint32_t>(rc.pos),
+                       static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
+}
+
+// Block words for a wave whose blocks are chunks 8 apart, four to a group
+// (block i % 4 == 0 starts a group): a shift register, so that block i takes
+// w0 and no word is picked by a runtime index.
+struct ShiftWords {
+  uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+  __device__ __forceinline__ uint32_t take(int32_t chunk, int32_t i, int lane, const RowConsts& rc) {
+    if ((i & 3) == 0) {  // chunk & 24 == 0
+      const Words4 rw = group_words(chunk, lane, rc);
+      w0 = rw.w[0];
+      w1 = rw.w[1];
+      w2 = rw.w[2];
+      w3 = rw.w[3];
+    }
+    const uint32_t word = w0;
+    w0 = w1;
+    w1 = w2;
+    w2 = w3;
+    return word;
+  }
+};
+
+// Block words for the blocks of one wave of a SIMD pair, taken in increasing
+// k (chunk c_begin + p + 4 k): the blocks of either parity of k form a run
+// of consecutive words of consecutive groups (word (k >> 1) & 3 of group
+// c & ~24), so each parity keeps a shift register as above. A parity's run
+// may start in the middle of a group; its first block then skips the words
+// before its own.
+struct PairWords {
+  uint32_t e0 = 0, e1 = 0, e2 = 0, e3 = 0;  // even k
+  uint32_t o0 = 0, o1 = 0, o2 = 0, o3 = 0;  // odd k
+  bool e_live = false, o_live = false;
+  __device__ __forceinline__ uint32_t take(int32_t chunk, int32_t k, int lane, const RowConsts& rc) {
+    const int idx = (k >> 1) & 3;
+    uint32_t word;
+    if (k & 1) {
+      if (idx == 0 || !o_live) {
+        const Words4 rw = group_words(chunk & ~(3 * kChunkStripes), lane, rc);
+        o0 = rw.w[0];
+        o1 = rw.w[1];
+        o2 = rw.w[2];
+        o3 = rw.w[3];
+        for (int q = 0; q < idx; ++q) {
+          o0 = o1;
+          o1 = o2;
+          o2 = o3;
+        }
+        o_live = true;
+      }
+      word = o0;
+      o0 = o1;
+      o1 = o2;
+      o2 = o3;
+    } else {
+      if (idx == 0 || !e_live) {
+        const Words4 rw = group_words(chunk & ~(3 * kChunkStripes), lane, rc);
+        e0 = rw.w[0];
+        e1 = rw.w[1];
+        e2 = rw.w[2];
+        e3 = rw.w[3];
+        for (int q = 0; q < idx; ++q) {
+          e0 = e1;
+          e1 = e2;
+          e2 = e3;
+        }
+        e_live = true;
+      }
+      word = e0;
+      e0 = e1;
+      e1 = e2;
+      e2 = e3;
+    }
+    return word;
+  }
+};
+
 template <bool kBf16, int NB>
 using Ring = uint4[2][kChunkStripes / NB][NB * Geometry<kBf16>::kLoadsPerStripe];
 
 // Block j (first id base, its 64 logits per lane in ring slot H) ends; bmax
 // is the lane's maximum over them below V.
-template <bool kBf16, int NB, int H>
-__device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t j, int32_t i,
+// seq is the block's place in the wave's sequence, as its word source counts it.
+template <bool kBf16, int NB, int H, class Words>
+__device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t j, int32_t seq,
                                             float bmax, int32_t vocab, const RowConsts& rc, LaneState& st,
-                                            WaveResult& wr, BlockWords& bw, uint4* park_best, uint4* park_max,
+                                            WaveResult& wr, Words& bw, uint4* park_best, uint4* park_max,
                                             int lane) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
   // ---- argmax: the wave maximum rises. Blocks come in increasing id order,
@@ -511,18 +590,7 @@ __device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t 
   }
 
   // ---- its score is its log-sum-exp plus its Gumbel
-  if ((i & 3) == 0) {  // (j >> 9) & 3 == 0
-    const Words4 rw = philox4x32_10(static_cast<uint32_t>(j), static_cast<uint32_t>(rc.pos),
-                                    static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
-    bw.w0 = rw.w[0];
-    bw.w1 = rw.w[1];
-    bw.w2 = rw.w[2];
-    bw.w3 = rw.w[3];
-  }
-  const uint32_t word = bw.w0;
-  bw.w0 = bw.w1;
-  bw.w1 = bw.w2;
-  bw.w2 = bw.w3;
+  const uint32_t word = bw.take(static_cast<int32_t>(base / kChunkIds), seq, lane, rc);
   float score = kNegInf;
   if (st.sb > 0.f) score = st.ref + __log2f(st.sb) + kLog2e * gumbel(word);
   st.s += static_cast<double>(st.sb);
@@ -672,16 +740,27 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
 
   // The split's chunks [c_begin, c_end), split at multiples of 32 chunks so
-  // that the block draws' groups of four stay within a split; wave w takes
-  // chunks c_begin + w, c_begin + w + 8, ...: its i-th block. Only the row's
-  // last chunk can be partial.
+  // that the block draws' groups of four stay within a split. Waves w and
+  // w + 4 share a SIMD, and the SIMD's arbiter favours the older one (w < 4):
+  // with equal shares the younger wave streams on alone for the last few
+  // microseconds. So the pair's chunks c_begin + p + 4k (p = w mod 4) are
+  // split unevenly: the older wave takes k < npair - n_young, the younger
+  // one the rest. Each wave visits its chunks in increasing order (block i is
+  // k = k0 + i); only the row's last chunk can be partial, and it is the last
+  // block of the wave that holds it.
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
   const int32_t ngroup = (nchunk + kDrawGroupChunks - 1) / kDrawGroupChunks;
   const int32_t c_begin = static_cast<int32_t>((static_cast<int64_t>(split) * ngroup) / a.nsplit) * kDrawGroupChunks;
   const int32_t c_end = min(static_cast<int32_t>((static_cast<int64_t>(split + 1) * ngroup) / a.nsplit) *
                             kDrawGroupChunks, nchunk);
-  const int32_t nblk = c_end - c_begin > wave ? (c_end - c_begin - wave + kWaves - 1) / kWaves : 0;
-  auto chunk_of = [&](int32_t i) { return c_begin + wave + kWaves * i; };
+  const int pair = wave & 3;
+  const bool young = wave >= 4;
+  const int32_t npair = c_end - c_begin > pair ? (c_end - c_begin - pair + 3) / 4 : 0;
+  const int32_t n_young = min(npair / 2, (npair * kYoungShare16 + 8) / 16);
+  const int32_t nblk = young ? n_young : npair - n_young;
+  const int32_t k0 = young ? npair - n_young : 0;
+  auto k_of = [&](int32_t i) { return k0 + i; };
+  auto chunk_of = [&](int32_t i) { return c_begin + pair + 4 * k_of(i); };
   auto base_of = [&](int32_t i) { return static_cast<int64_t>(chunk_of(i)) * kChunkIds; };
   // Block i's byte offset for this lane; batches wholly past V point beyond
   // the resource, where buffer loads return zero without touching memory, so
@@ -706,13 +785,13 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const RowConsts rc = row_consts(a, r);
   LaneState st;
   WaveResult wr;
-  BlockWords bw;
+  PairWords bw;
 
   // Full blocks: reduce, close, and refill the ring slot with block i + 2.
   auto run_block = [&](auto slot, int32_t i) {
     constexpr int H = decltype(slot)::value;
     const float bmax = reduce_block<kBf16, NB, H>(buf, base_of(i), vocab, rc.c, st, lane);
-    close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, i, bmax, vocab, rc, st, wr, bw,
+    close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, k_of(i), bmax, vocab, rc, st, wr, bw,
                               s_blk[wave], s_amx[wave], lane);
 #pragma unroll
     for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[H][t], rsrc, batch_byte(i + 2, t));
@@ -737,7 +816,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
       const int64_t f = base_of(i) + t * NB * kStripeIds;
       if (f < vocab) bmax = fmaxf(bmax, tail_batch<kBf16, NB>(buf[0][t], f + lane * kSlotIds, vocab, rc.c, st));
     }
-    close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, i, bmax, vocab, rc, st, wr, bw,
+    close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, k_of(i), bmax, vocab, rc, st, wr, bw,
                               s_blk[wave], s_amx[wave], lane);
   }
 
@@ -812,7 +891,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
     const RowConsts rc = row_consts(a, r);
     LaneState st;
     WaveResult wr;
-    BlockWords bw;
+    ShiftWords bw;
     auto run_block = [&](auto slot, int32_t i) {
       constexpr int H = decltype(slot)::value;
       const int64_t base = static_cast<int64_t>(wave + kWaves * i) * kChunkIds;
