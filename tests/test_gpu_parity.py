@@ -69,6 +69,30 @@ def test_ragged_vocab(dtype, V):
     compare_stats(host_values(z), np.float32(0.7), V * 31 + 5, np.arange(L), 3, h, am, smp)
 
 
+# The one-row-per-workgroup kernel splits each SIMD pair's chunks p + 4k
+# unevenly between its older and younger wave (the younger takes the last
+# ~6/16 of k), and each wave draws its block words from two runs (even and
+# odd k) that may start mid-group. Chunk counts that leave a pair with one
+# or two chunks, a ragged last chunk, and splits of 32 chunks with a short
+# last split.
+@pytest.mark.parametrize("V,nsplit,dtype", [
+    (5 * 4096, 1, torch.bfloat16),         # pairs of 2, 1, 1, 1 chunks
+    (14 * 4096 - 9, 1, torch.bfloat16),    # pairs of 4, 4, 3, 3; the last chunk ragged
+    (14 * 4096 - 9, 1, torch.float32),
+    (33 * 4096, 2, torch.bfloat16),        # splits of 32 and 1 chunks
+    (64 * 4096 + 100, 3, torch.bfloat16),  # splits of 32, 32 and 1 (ragged) chunks
+])
+def test_simd_pair_shares_match_oracle(V, nsplit, dtype):
+    L = 16
+    ctx = _ctx(L, V)
+    per16 = 8 if dtype == torch.bfloat16 else 4
+    stride = -(-V // per16) * per16
+    z = synth.margin_logits(V + 17, L, V, m_max=3.0, dtype=dtype, device="cuda")
+    zp = _padded(z, stride)
+    h, am, smp = _stats(ctx, zp, [0.9], [V * 7 + 1], 5, 1, nsplit=nsplit)
+    compare_stats(host_values(z), np.float32(0.9), V * 7 + 1, np.arange(L), 5, h, am, smp)
+
+
 # Shapes that take the persistent row loop (more rows than compute units, V a
 # multiple of 4096, no active mask): each workgroup handles rows b, b + grid,
 # ..., and the register ring runs on into the next row. Rows are sampled at
