@@ -16,15 +16,18 @@
 //     the best block j* with the largest z/T + element Gumbel.
 //
 // Layout and schedule (gfx950, wave64): rows are V-contiguous. A workgroup of
-// eight waves handles a row (or one split of it); wave w takes the split's
-// chunks w, w + 8, ..., so that the workgroup streams 32 KiB (bf16) of
-// consecutive memory at a time. Each lane issues one 16-byte load per 512-id
+// eight waves handles a row (or one split of it). Waves w and w + 4 share a
+// SIMD and split the chunks p + 4k (p = w mod 4) between them, the older wave
+// taking the first 10/16 of k (the SIMD's arbiter favours it); in the
+// persistent row loop wave w takes chunks w, w + 8, ... Either way the
+// workgroup streams a few stretches of consecutive memory at a time, one
+// 4096-id chunk per wave. Each lane issues one 16-byte load per 512-id
 // stripe (bf16; two for fp32); a batch is 4 stripes and a block 2 batches,
 // and a register ring holds two blocks: one is reduced while the other is in
 // flight. Loads are raw buffer loads on a per-row resource (hardware range
 // check, no branches), marked non-temporal. Per element the loop costs one
 // convert, half a max, one fma, one v_exp_f32, one add and one fma; per four
-// blocks (256 ids per lane) one Philox call. When a block ends its logits are
+// blocks of a group (256 ids per lane) one Philox call. When a block ends its logits are
 // still in registers, so nothing is read twice: if the block beats the wave's
 // best block, or a lane of it holds a new wave maximum, that lane parks the
 // block's 64 logits in LDS, and after its stream the wave draws the sample in
