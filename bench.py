@@ -9,7 +9,8 @@ accept/renoise/stop kernel. Workload: one canvas of 256 positions, a
 rotate over several 128 MiB buffers so that each step reads from HBM rather
 than from the 256 MB last-level cache. Steps are launched back to back on one
 stream (the host enqueues faster than the GPU drains, so host launch cost is
-hidden); the same steps replayed from captured HIP graphs are reported too.
+hidden); the same steps replayed from captured HIP graphs (one step per graph,
+and one graph holding a step on each buffer) are reported too.
 
 Prints one JSON line: steps/s (value), positions/s, the statistics kernel's
 achieved HBM bandwidth against the 8 TB/s peak (HIP events on the launch
@@ -646,6 +647,15 @@ def main():
         return graphs
 
     step_graphs = capture(full_step)
+    # one graph holding a step on each of the R buffers, so that the graph
+    # launch is paid once per R steps
+    multi_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(multi_graph, stream=stream):
+            for r in range(R):
+                full_step(r)
+    torch.cuda.synchronize()
 
     def time_eager(fn, k):
         """HIP events on the launch stream around k back-to-back launches."""
@@ -667,6 +677,9 @@ def main():
         # the same steps replayed from captured HIP graphs, for reference
         _time_graphs(step_graphs, args.warmup, torch)
         t_graph = _time_graphs(step_graphs, args.steps, torch)
+        n_multi = max(1, args.steps // R)
+        _time_graphs([multi_graph], max(1, args.warmup // R), torch)
+        t_graph_multi = _time_graphs([multi_graph], n_multi, torch)
 
     read_ceiling = read_ceiling_leg(torch, logits, stream, args.steps)
     steps_per_s = args.steps / t_step
@@ -700,6 +713,8 @@ def main():
                    "temperature": "0.8->0.4 over 16 steps"},
         "positions_per_s": steps_per_s * Bn * L,
         "graph_steps_per_s": args.steps / t_graph,
+        "graph_multi_steps_per_s": n_multi * R / t_graph_multi,
+        "graph_multi_steps_per_graph": R,
         "roofline": {"bound": "hbm", "kernel": "canvas_stats_kernel", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic, "avg_kernel_us": stats_s * 1e6,
