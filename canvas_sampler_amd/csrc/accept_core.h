@@ -59,13 +59,37 @@ __device__ __forceinline__ double read_lane_f64(double v, int lane) {
 
 }  // namespace accept_detail
 
+// Per-thread inputs of accept_canvas, loaded by the caller up front so that
+// every load of the kernel is in flight at once: position t's entropy,
+// argmax, sample and previous argmax (t < L), and the canvas's seed and step.
+struct AcceptInputs {
+  float h = 0.0f;
+  int32_t am = 0, smp = 0, prev = 0;
+  uint64_t seed = 0;
+  int32_t step = 0;
+};
+
+// Issues every load accept_canvas needs for thread t of `canvas`.
+__device__ __forceinline__ AcceptInputs load_accept_inputs(const AcceptArgs& a, int32_t canvas, int t) {
+  AcceptInputs in;
+  if (t < a.canvas_len) {
+    const int64_t at = static_cast<int64_t>(canvas) * a.canvas_len + t;
+    in.h = a.entropy[at];
+    in.am = a.argmax[at];
+    in.smp = a.sample[at];
+    if (a.prev_argmax != nullptr) in.prev = a.prev_argmax[at];
+  }
+  in.seed = a.seeds[canvas];
+  in.step = a.steps != nullptr ? a.steps[canvas] : a.step;
+  return in;
+}
+
 // Runs the acceptance of `canvas` on a workgroup of NT threads (NT a multiple
 // of 64, at least kAcceptThreads); threads from kAcceptThreads on only join
-// the barriers. Every thread of the workgroup must call it; thread t < L
-// passes position t's entropy h, argmax am and sample smp.
+// the barriers. Every thread of the workgroup must call it, with its inputs
+// from load_accept_inputs.
 template <int NT>
-__device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canvas, float h, int32_t am,
-                                              int32_t smp) {
+__device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canvas, const AcceptInputs& in) {
   using namespace accept_detail;
   static_assert(NT % kWave == 0 && NT >= kAcceptThreads, "accept_canvas: bad workgroup size");
   __shared__ uint64_t s_key[kAcceptThreads];
@@ -82,13 +106,15 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   const int32_t L = a.canvas_len;
   const int64_t base = static_cast<int64_t>(canvas) * L;
   const bool valid = tid < L;
+  const float h = in.h;
+  const int32_t am = in.am, smp = in.smp;
 
   // Independent of the order: mean entropy (fp64, in position order), argmax
   // stability and the renoise token. Formed before the sort so that they
   // overlap it; the per-wave parts are published by the sort's LDS barriers.
   double hsum = valid ? static_cast<double>(h) : 0.0;
   hsum = wave_sum(hsum);
-  const bool same = !valid || (a.prev_argmax != nullptr && a.prev_argmax[base + tid] == am);
+  const bool same = !valid || (a.prev_argmax != nullptr && in.prev == am);
   const bool wave_same = __builtin_amdgcn_ballot_w64(!same) == 0;
   if (part && lane == 0) {
     s_hsum[wave] = hsum;
@@ -96,11 +122,9 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   }
   int32_t renoise = 0;
   if (valid) {
-    const uint64_t seed = a.seeds[canvas];
-    const int32_t step = a.steps != nullptr ? a.steps[canvas] : a.step;
-    const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(step),
-                                    kTagRenoise, static_cast<uint32_t>(seed),
-                                    static_cast<uint32_t>(seed >> 32));
+    const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(in.step),
+                                    kTagRenoise, static_cast<uint32_t>(in.seed),
+                                    static_cast<uint32_t>(in.seed >> 32));
     renoise = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
   }
   // bitonic sort of 256 keys, ascending. Compare-exchange partners closer

@@ -10,17 +10,11 @@ namespace {
 
 __global__ __launch_bounds__(kAcceptThreads) void accept_renoise_kernel(AcceptArgs a) {
   const int32_t canvas = blockIdx.x;
+  // every load goes out before the first is used (the active flag included:
+  // an inactive canvas's inputs are valid memory, only unused)
+  const AcceptInputs in = load_accept_inputs(a, canvas, threadIdx.x);
   if (a.active != nullptr && a.active[canvas] == 0) return;
-  const int tid = threadIdx.x;
-  float h = 0.0f;
-  int32_t am = 0, smp = 0;
-  if (tid < a.canvas_len) {
-    const int64_t at = static_cast<int64_t>(canvas) * a.canvas_len + tid;
-    h = a.entropy[at];
-    am = a.argmax[at];
-    smp = a.sample[at];
-  }
-  accept_canvas<kAcceptThreads>(a, canvas, h, am, smp);
+  accept_canvas<kAcceptThreads>(a, canvas, in);
 }
 
 // Initial canvas: position l of canvas c gets floor(w0 * V / 2^32) with w0
