@@ -927,10 +927,14 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
 
 int32_t choose_nsplit(int32_t rows, int32_t vocab) {
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
-  // aim for >= 2048 waves in flight (256 CUs x 8), at most one split per 32
-  // chunks: splits start at multiples of 32 chunks, where the groups of four
-  // block draws start
-  int32_t want = (2048 / kWaves + rows - 1) / rows;
+  // Split only while the split workgroups stay within about half of the 256
+  // CUs: the agent-scope fences of the merge cost a few microseconds per
+  // workgroup, and a workgroup streams a row at a bounded rate. Measured at
+  // V = 262144 bf16 (one / two workgroups per row): L = 16 20.4 / 16.5 us,
+  // L = 64 22.1 / 20.3 us, L = 96 22.3 / 23.4 us, L = 128 22.5 / 27.5 us.
+  // At most one split per 32 chunks: splits start at multiples of 32 chunks,
+  // where the groups of four block draws start.
+  int32_t want = 128 / rows;
   int32_t cap = nchunk / kDrawGroupChunks;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
