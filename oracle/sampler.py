@@ -10,8 +10,8 @@ Rules, as the pages state them:
     item 3  stop when the argmax canvas is unchanged from the previous step
             and the mean entropy is below 0.005;
     item 4  temperature goes linearly from 0.8 to 0.4 across steps;
-    item 5  the output is the argmax canvas; the multinomial sample is what the
-            committed positions receive.
+    item 5  (garbled on the page) read as: a run returns its argmax canvas,
+            and a committed position takes that step's multinomial draw.
   "DiffusionGemma: Parallel Denoising From an Autoregressive Checkpoint"
   (boxwrench.dev), "Finding", Algorithm 1: multinomial (uniform-noise)
   diffusion; the non-accepted remainder is renoised uniformly; the budget is
@@ -218,28 +218,46 @@ def stop_test(argmax, prev_argmax, mean_h, threshold):
     return stable and bool(mean_h < np.float64(threshold))
 
 
+def row_statistics(z, temp, seed, positions, step_index):
+    """Per-row statistics of one step for rows z ([rows, V], any float dtype,
+    widened exactly to fp64) at canvas positions `positions`: entropy, raw
+    argmax and the two-level sample, with the sample's winning scores and
+    margins at both levels (see sample_two_level_detail)."""
+    z = np.asarray(z, dtype=np.float64)
+    smp, bbest, bgap, ebest, egap = sample_two_level_detail(z, temp, seed, positions, step_index)
+    return dict(entropy=entropy(z, temp), argmax=argmax_raw(z), sample=smp,
+                block_best=bbest, block_gap=bgap, elem_best=ebest, elem_gap=egap)
+
+
+def decide(h, am, smp, seed, step_index, vocab, prev_argmax=None, bound=np.float32(0.1),
+           stop_threshold=np.float32(0.005)):
+    """The per-canvas decisions of one step from its rows' entropies h,
+    argmaxes am and samples smp ([L] each): acceptance, the new canvas
+    (accepted positions take the sample, the rest a fresh uniform token), the
+    mean entropy and the stop."""
+    h = np.asarray(h, dtype=np.float64)
+    mask, k = accept(h, bound)
+    renoise = uniform_tokens(seed, h.shape[0], step_index, vocab, TAG_RENOISE)
+    canvas = np.where(mask, smp, renoise)
+    mean_h = float(np.mean(h))
+    stop = stop_test(am, prev_argmax, mean_h, stop_threshold)
+    return dict(accept=mask, n_accept=k, canvas=canvas, renoise=renoise, mean_entropy=mean_h,
+                stop=stop)
+
+
 def step(z, temp, seed, step_index, prev_argmax=None, bound=np.float32(0.1),
          stop_threshold=np.float32(0.005), rows_per_chunk=16):
     """One sampler step over one canvas. z: [L, V] logits (any float dtype,
     widened exactly to fp64). Returns a dict of every step output."""
     z = np.asarray(z)
     L, vocab = z.shape
-    h = np.empty(L)
-    am = np.empty(L, dtype=np.int64)
-    smp = np.empty(L, dtype=np.int64)
-    for r0 in range(0, L, rows_per_chunk):
-        zz = z[r0:r0 + rows_per_chunk].astype(np.float64)
-        pos = np.arange(r0, r0 + zz.shape[0])
-        h[r0:r0 + zz.shape[0]] = entropy(zz, temp)
-        am[r0:r0 + zz.shape[0]] = argmax_raw(zz)
-        smp[r0:r0 + zz.shape[0]] = sample_two_level(zz, temp, seed, pos, step_index)
-    mask, k = accept(h, bound)
-    renoise = uniform_tokens(seed, L, step_index, vocab, TAG_RENOISE)
-    canvas = np.where(mask, smp, renoise)
-    mean_h = float(np.mean(h))
-    stop = stop_test(am, prev_argmax, mean_h, stop_threshold)
-    return dict(entropy=h, argmax=am, sample=smp, accept=mask, n_accept=k,
-                canvas=canvas, mean_entropy=mean_h, stop=stop)
+    parts = [row_statistics(z[r0:r0 + rows_per_chunk], temp, seed,
+                            np.arange(r0, min(r0 + rows_per_chunk, L)), step_index)
+             for r0 in range(0, L, rows_per_chunk)]
+    out = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+    out.update(decide(out["entropy"], out["argmax"], out["sample"], seed, step_index, vocab,
+                      prev_argmax, bound, stop_threshold))
+    return out
 
 
 def run(denoise, seed, canvas_len, vocab, t_start=0.8, t_end=0.4, n_sched=48,

@@ -8,10 +8,13 @@ Comparison policy:
   - sample: bit-exact except near-ties, i.e. rows where the oracle's two best
     Gumbel-perturbed scores (block level or in-block level) differ by less
     than 1e-6 * max(1, |score|); such rows are counted and reported;
-  - acceptance/stop against the oracle's: exact except when an entropy gap or
-    the bound slack at the acceptance boundary is below the measured entropy
-    error; in addition the GPU's decisions must obey the rules as properties
-    of the GPU's own outputs (check_decision_rules, which uses no oracle code);
+  - acceptance/stop against the oracle's: exact except at a near-tie that the
+    measured entropy error can flip (accept_tie_clause, stop_tie_clause:
+    the bound slack within k * max|dH|, a boundary gap within 2 max|dH|, the
+    mean entropy within max|dH| of the threshold; each capped at 1e-4), which
+    is counted and named; in addition the GPU's decisions must obey the rules
+    as properties of the GPU's own outputs (check_decision_rules, which uses
+    no oracle code);
   - logits from the LM head (fp32 accumulation) differ from the oracle's
     exact products by a measured per-row error e; an argmax or sample mismatch
     is then a near-tie when the oracle's competing scores are within 2e/T of
@@ -86,21 +89,63 @@ def compare_stats(z_host, temp, seed, positions, step, h_gpu, am_gpu, smp_gpu, r
     return out
 
 
-def accept_near_tie(h_oracle, bound, tol):
-    """True when the acceptance decision of the oracle's entropies could flip
-    under entropy errors up to tol: an entropy gap at the boundary or the bound
-    slack of the boundary prefix sums is within the error."""
-    L = len(h_oracle)
-    order = np.lexsort((np.arange(L), h_oracle))
-    hs = h_oracle[order]
-    _, k = O.accept(h_oracle, bound)
-    ex = np.concatenate([[0.0], np.cumsum(hs)])[:-1]
-    slack_tol = max(1e-6, 4 * L * tol)
-    near = False
+# A slack or gap larger than this never excuses a difference, however large
+# the measured entropy error (it stays well below it in every configuration).
+ACCEPT_SLACK_CAP = 1e-4
+
+
+def _fp64_prefix_rounding(n, total):
+    """Bound on the rounding of an n-term fp64 sum of non-negative terms that
+    add up to `total` (either side's prefix sums)."""
+    return 2.0 * n * 2.0 ** -53 * max(float(total), 0.0) + 1e-300
+
+
+def accept_tie_clause(h_oracle, bound, dh):
+    """Names the near-tie through which entropies within dh of the oracle's
+    (per row) can change the oracle's acceptance, or returns None.
+
+    With pi the (H, position) order, EX_i the sum of the i smallest entropies
+    and k the oracle's count (EX_i <= b exactly for i < k): entropies off by
+    at most dh move each sorted value by at most dh and EX_i by at most
+    i * dh. So the count can change only when EX_k - b <= k * dh (one more
+    position fits) or b - EX_{k-1} < (k - 1) * dh (the last accepted one no
+    longer fits), and the accepted set can change at an equal count only when
+    H_pi(k) - H_pi(k-1) <= 2 * dh (the two boundary positions trade places).
+    Every slack also allows both sides' fp64 rounding of the prefix sums and
+    is capped at ACCEPT_SLACK_CAP."""
+    h = np.asarray(h_oracle, dtype=np.float64)
+    L = len(h)
+    order = np.lexsort((np.arange(L), h))
+    hs = h[order]
+    _, k = O.accept(h, bound)
+    ex = np.concatenate([[0.0], np.cumsum(hs)])
+    cap = ACCEPT_SLACK_CAP
     if k < L:
-        near |= abs(ex[k] - bound) < slack_tol or abs(hs[k] - hs[k - 1]) < max(1e-6, 4 * tol)
-    near |= abs(ex[k - 1] - bound) < slack_tol
-    return near
+        slack = ex[k] - bound
+        tol = min(k * dh + _fp64_prefix_rounding(k, ex[k]), cap)
+        if slack <= tol:
+            return f"one more position fits: EX_k - b = {slack:.3g} <= k*dH = {tol:.3g} (k = {k})"
+        gap = hs[k] - hs[k - 1]
+        tol = min(2 * dh, cap)
+        if gap <= tol:
+            return f"boundary positions trade places: H gap {gap:.3g} <= 2 dH = {tol:.3g} (k = {k})"
+    if k > 1:
+        slack = bound - ex[k - 1]
+        tol = min((k - 1) * dh + _fp64_prefix_rounding(k - 1, ex[k - 1]), cap)
+        if slack < tol:
+            return f"last position no longer fits: b - EX_(k-1) = {slack:.3g} < (k-1)*dH = {tol:.3g} (k = {k})"
+    return None
+
+
+def stop_tie_clause(mean_h_oracle, threshold, dh):
+    """Names the near-tie through which a mean entropy off by at most dh (plus
+    fp32 rounding of the GPU's mean) can flip the strict test mean < threshold,
+    or returns None."""
+    m = float(mean_h_oracle)
+    tol = min(dh + 2.0 ** -23 * max(m, float(threshold)), ACCEPT_SLACK_CAP)
+    if abs(m - float(threshold)) <= tol:
+        return f"mean entropy {m:.6g} within {tol:.3g} of the stop threshold {float(threshold):.6g}"
+    return None
 
 
 def check_decision_rules(h, accept, n_accept, sample, canvas, renoise, mean_h, stop, prev_argmax,

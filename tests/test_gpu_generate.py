@@ -11,8 +11,8 @@ from canvas_sampler_amd import synth
 from oracle import blockar as BA
 from oracle import sampler as O
 
-from gpu_util import gpu, host_values, require_gpu, seeds_tensor
-from test_gpu_run import _explain_divergence
+from gpu_util import gpu, require_gpu, seeds_tensor
+from full_parity import trajectory
 
 pytestmark = gpu
 
@@ -103,7 +103,8 @@ def test_generate_matches_oracle():
     # two streams of three canvases on the chained sharpening stand-in
     # (bf16, V = 4096): each canvas is run by the oracle from the same logits
     # bits (conditioned on the GPU's previous canvas, so that a difference
-    # cannot carry over) and must agree, or part only at a near-tie; the
+    # cannot carry over) and must stop where the oracle does with the same
+    # argmax canvas, per-step differences only at counted near-ties; the
     # device loop's own variants (never waiting, waiting every 4 steps) agree
     # bit for bit
     L, V, n = 256, 4096, 3
@@ -115,31 +116,25 @@ def test_generate_matches_oracle():
     den4 = ChainedDenoiser(gens, L, V)
     t4, s4, st4 = _generate(ctx, seeds, n, den4, torch.bfloat16, 4)
     assert np.array_equal(t4, tokens) and np.array_equal(s4, steps) and np.array_equal(st4, stopped)
-    for c, (g, seed) in enumerate(zip(gens, seeds)):
-        for k in range(n):
+    for k in range(n):
+        for c in range(2):
             assert np.array_equal(tokens[c, k * L:(k + 1) * L], den.finished[k][c].cpu().numpy())
-            tgt, m0 = den.state[k][c]
-            zs = {}
 
-            def oden(s, canvas, k=k, g=g, tgt=tgt, m0=m0):
-                zs[s] = synth.chained_logits(g, k, s, tgt, m0, V, dtype=torch.bfloat16, device="cuda")
-                return host_values(zs[s])
+        # canvas k of both streams, conditioned on the GPU's finished canvas
+        # k - 1 (so that a difference cannot carry over), every row of every
+        # step against the oracle
+        def write(step, out, k=k):
+            for c, g in enumerate(gens):
+                tgt, m0 = den.state[k][c]
+                synth.chained_logits(g, k, step, tgt, m0, V, dtype=torch.bfloat16, device="cuda",
+                                     out=out[c * L:(c + 1) * L])
 
-            ofinal, osteps, ostopped, rec = O.run(oden, BA.canvas_seed(seed, k), L, V, n_sched=16,
-                                                  record=True)
-            n_cmp = min(osteps, int(steps[k, c]))
-            parted = next((s for s in range(n_cmp)
-                           if not np.array_equal(den.canvas_in[(k, s)][c].cpu().numpy(),
-                                                 rec[s]["canvas_in"])), None)
-            if parted is None:
-                assert steps[k, c] == osteps and stopped[k, c] == bool(ostopped)
-                assert np.array_equal(tokens[c, k * L:(k + 1) * L], ofinal)
-                print(f"stream {c} canvas {k}: {osteps} steps, as the oracle")
-            else:
-                why = _explain_divergence(zs[parted - 1], rec[parted - 1], BA.canvas_seed(seed, k),
-                                          parted - 1, L, V,
-                                          den.canvas_in[(k, parted)][c].cpu().numpy())
-                print(f"stream {c} canvas {k}: parts from the oracle at step {parted} ({why})")
+        tally, runs, _ = trajectory(f"generate canvas {k}", L, V, [BA.canvas_seed(sd, k) for sd in seeds],
+                                    write, torch.bfloat16, temp_steps=16, library_loop=False)
+        for c in range(2):
+            assert (int(steps[k, c]), bool(stopped[k, c])) == runs[c][:2], f"stream {c} canvas {k}"
+            assert np.array_equal(tokens[c, k * L:(k + 1) * L], runs[c][2]), f"stream {c} canvas {k}"
+        tally.report()
     per, total = B.tokens_per_forward(steps, L)
     for c in range(2):
         assert per[c] == pytest.approx(BA.tokens_per_forward(steps[:, c].tolist(), L), rel=1e-15)

@@ -15,11 +15,9 @@ import torch
 from canvas_sampler_amd import binding as B
 from canvas_sampler_amd import synth
 from oracle import lmhead as OL
-from oracle import philox as OP
 from oracle import sampler as O
 
-from gpu_util import (accept_near_tie, check_decision_rules, compare_stats, gpu, require_gpu,
-                      seeds_tensor)
+from gpu_util import check_decision_rules, compare_stats, gpu, require_gpu, seeds_tensor
 
 pytestmark = gpu
 
@@ -123,7 +121,11 @@ def test_fused_lmhead_workload_matches_oracle():
     # 64 canvases x 256 positions, hidden bf16 [16384, 2048] ~ N(0,1), weight
     # bf16 [2048, 262144] ~ N(0, 1/2048); canvas c sits at step c mod 48 of the
     # default 48-step schedule (temperature and random draws), seed c. The
-    # oracle recomputes canvases 0 and 63 completely and 8 more sampled rows.
+    # oracle recomputes eight canvases spread over the batch completely (every
+    # logit within the accumulation bound, then every row's statistics and
+    # the canvas decisions on the exact logits), plus 8 sampled rows of others.
+    from full_parity import Tally, compare_step
+    from oracle import parallel as OPAR
     require_gpu()
     L, K, V, Bn = 256, 2048, 262144, 64
     params = B.params_default(canvas_len=L, vocab=V)
@@ -141,29 +143,31 @@ def test_fused_lmhead_workload_matches_oracle():
     g = {k: v.cpu().numpy() for k, v in bufs.items()}
     wh = _f32(w)
     hh = _f32(h)
-    report = []
-    for c in (0, 63):
+    tally = Tally("C5")
+    for c in (0, 9, 18, 27, 36, 45, 54, 63):
         rows = slice(c * L, (c + 1) * L)
         t = np.float32(temps[c])
         assert t == np.float32(O.temperature(steps[c], 0.8, 0.4, 48))
-        ref = OL.step(hh[rows], wh, t, c, steps[c])
+        exact = OL.logits(hh[rows], wh)
         gz = z[c * L:(c + 1) * L].cpu().numpy()
-        _, err = _check_logits(gz, hh[rows], wh, f"canvas {c} logits", exact=ref["logits"])
-        rep = compare_stats(ref["logits"], t, c, np.arange(L), steps[c], g["entropy_out"][rows],
-                            g["argmax_out"][rows], g["sample_out"][rows], report,
-                            logit_err=err.max(axis=1))
-        dh = rep["max_dh"]
-        if not accept_near_tie(ref["entropy"], float(np.float32(0.1)), dh):
-            assert np.array_equal(g["accept_out"][rows].astype(bool), ref["accept"])
-            assert g["n_accept_out"][c] == ref["n_accept"]
-        ren = O.uniform_tokens(c, L, steps[c], V, OP.TAG_RENOISE)
+        _, err = _check_logits(gz, hh[rows], wh, f"canvas {c} logits", exact=exact)
+        o = OPAR.steps([dict(rows=lambda r0, r1: exact[r0:r1], L=L, V=V, temp=t, seed=c, step=steps[c],
+                             prev_argmax=None)])[0]
+        gc = dict(entropy=g["entropy_out"][rows], argmax=g["argmax_out"][rows], sample=g["sample_out"][rows],
+                  accept=g["accept_out"][rows], n_accept=g["n_accept_out"][c], canvas=g["canvas_out"][rows],
+                  mean_entropy=g["mean_entropy_out"][c], stop=g["stop_out"][c])
+        compare_step(gc, o, f"C5 canvas {c} (step {steps[c]})", tally, np.float32(0.1), np.float32(0.005),
+                     logit_err=err.max(axis=1), z=exact, temp=t)
         check_decision_rules(g["entropy_out"][rows], g["accept_out"][rows], g["n_accept_out"][c],
-                             g["sample_out"][rows], g["canvas_out"][rows], ren,
+                             g["sample_out"][rows], g["canvas_out"][rows], o["renoise"],
                              g["mean_entropy_out"][c], g["stop_out"][c], None, g["argmax_out"][rows],
                              float(np.float32(0.1)), float(np.float32(0.005)))
         assert g["stop_out"][c] == 0
         print(f"canvas {c}: step {steps[c]} T {t:.4f} n_accept {g['n_accept_out'][c]} "
-              f"(oracle {ref['n_accept']}), max dH {dh:.2e}, near-ties {rep}")
+              f"(oracle {o['n_accept']})")
+        del exact, err
+    tally.report()
+    report = []
     rng = np.random.default_rng(5)
     for r in rng.choice(np.arange(L, 63 * L), size=8, replace=False):
         c, pos = divmod(int(r), L)
@@ -173,7 +177,7 @@ def test_fused_lmhead_workload_matches_oracle():
         compare_stats(zr, t, c, np.array([pos]), steps[c], g["entropy_out"][r:r + 1],
                       g["argmax_out"][r:r + 1], g["sample_out"][r:r + 1], report,
                       logit_err=err.max(axis=1))
-    print("fused LM-head workload:", report)
+    print("sampled rows of other canvases:", report)
 
 
 def test_lmhead_validation_rejects_before_launch():

@@ -137,3 +137,30 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run(["python", "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("raised:") and "no fallback" in r.stdout
+
+
+def test_acceptance_near_tie_clauses():
+    # the comparison policy of the GPU tests: a difference in acceptance is
+    # excused only when the oracle's entropies sit within the measured error
+    # of a decision boundary (planted cases), never far from one
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from gpu_util import accept_tie_clause, stop_tie_clause
+    b = float(np.float32(0.1))
+    # far from every boundary: 0.01 x 5 then large entropies (EX_5 = 0.05)
+    h = np.array([0.01] * 5 + [1.0] * 11)
+    assert accept_tie_clause(h, b, 1e-6) is None
+    # ten entropies of b/10 + 1e-9: EX_10 - b = 1e-8, so one more position
+    # fits once each entropy may be 1e-9 lower (10 * dH >= 1e-8)
+    h2 = np.concatenate([np.full(10, b / 10 + 1e-9), [5.0]])
+    assert accept_tie_clause(h2, b, 1e-7) is not None and "fits" in accept_tie_clause(h2, b, 1e-7)
+    assert accept_tie_clause(h2, b, 1e-10) is None
+    # boundary positions trade places: H gap 3e-7 at k = 1, dH 2e-7
+    h3 = np.array([0.5, 0.5 + 3e-7, 2.0])
+    assert "trade" in accept_tie_clause(h3, b, 2e-7)
+    assert accept_tie_clause(h3, b, 1e-7) is None
+    # the cap: a huge dH excuses nothing beyond 1e-4
+    assert accept_tie_clause(np.array([0.05, 0.06, 3.0]), b, 1.0) is None
+    assert stop_tie_clause(0.0050001, np.float32(0.005), 1e-6) is not None
+    assert stop_tie_clause(0.004, np.float32(0.005), 1e-6) is None

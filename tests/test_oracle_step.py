@@ -117,3 +117,18 @@ def test_minimum_two_steps_for_trivial_outputs():
     z[np.arange(L), np.arange(L) * 7] = 0.0
     _, n, stopped, _ = O.run(lambda s, c: z, seed=1, canvas_len=L, vocab=V)
     assert stopped and n == 2
+
+
+def test_parallel_driver_equals_step():
+    # oracle.parallel runs the oracle's own row statistics over a thread pool
+    # and its decisions per canvas: the result must be sampler.step's, key for
+    # key, for several canvases sharing one pool
+    from oracle import parallel as P
+    rng = np.random.default_rng(3)
+    zs = [rng.standard_normal((40, 700)).astype(np.float32) * s for s in (1.0, 4.0, 0.01)]
+    jobs = [dict(rows=lambda r0, r1, z=z: z[r0:r1], L=40, V=700, temp=np.float32(0.6), seed=9 + i,
+                 step=2, prev_argmax=None) for i, z in enumerate(zs)]
+    for i, (z, got) in enumerate(zip(zs, P.steps(jobs, threads=3))):
+        want = O.step(z, np.float32(0.6), 9 + i, 2)
+        for k, v in want.items():
+            assert np.array_equal(np.asarray(v), np.asarray(got[k])), k
