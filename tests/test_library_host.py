@@ -148,8 +148,9 @@ def test_acceptance_near_tie_clauses():
     sys.path.insert(0, os.path.dirname(__file__))
     from gpu_util import accept_tie_clause, stop_tie_clause
     b = float(np.float32(0.1))
-    # far from every boundary: 0.01 x 5 then large entropies (EX_5 = 0.05)
-    h = np.array([0.01] * 5 + [1.0] * 11)
+    # far from every boundary: 0.01 x 5, then distinct large entropies
+    # (EX_5 = 0.05 accepts the sixth, EX_6 > 1 stops there)
+    h = np.array([0.01] * 5 + [1.0 + 0.1 * i for i in range(11)])
     assert accept_tie_clause(h, b, 1e-6) is None
     # ten entropies of b/10 + 1e-9: EX_10 - b = 1e-8, so one more position
     # fits once each entropy may be 1e-9 lower (10 * dH >= 1e-8)
