@@ -501,7 +501,7 @@ def selfcond_leg(torch, B, synth, k=200, d=30):
             "step_with_selfcond_per_s": 1e6 / t_step_sc}
 
 
-def lmhead_leg(args, torch, B, synth):
+def lmhead_leg(args, torch, B, synth, keep=None):
     """The 64-canvas step whose logits come from the LM head: hidden bf16
     [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
     at step c mod 48 of the default schedule, seed c."""
@@ -539,6 +539,15 @@ def lmhead_leg(args, torch, B, synth):
                                                       steps=steps))
     flops = 2.0 * Bn * L * V * K
     tflops = flops / gemm_s / 1e12
+    if keep is not None:
+        # canvas 0 (step 0, T 0.8, seed 0) once more with every output, for the
+        # oracle comparison of the CPU-baseline leg
+        bufs = _step_buffers(torch, Bn, L)
+        ctx.dg_lmhead_sampler_step(hidden, weight, logits, temps, 0, seeds, ctx.step_out(**bufs), steps=steps)
+        torch.cuda.synchronize()
+        keep.update(hidden=hidden[:L].to(torch.float32).cpu().numpy(),
+                    weight=weight.to(torch.float32).cpu().numpy(), logits=logits[:L].cpu().numpy(),
+                    gpu=_host_outputs(bufs, 1, L)[0], temp=float(temps[0].item()), step=0, seed=0)
     ctx.close()
     return {"workload": "64 canvases x 256 positions, LM head bf16 [16384,2048] x [2048,262144] "
                         "-> fp32 logits -> statistics -> acceptance; per-canvas steps c mod 48",
@@ -549,13 +558,161 @@ def lmhead_leg(args, torch, B, synth):
             "positions_per_s": Bn * L / step_s, "steps_per_s": 1.0 / step_s, "timed_launches": k}
 
 
+def _step_buffers(torch, n, L):
+    """Device buffers for every output of one step of n canvases."""
+    dev = "cuda"
+    return dict(canvas_out=torch.empty(n * L, dtype=torch.int32, device=dev),
+                argmax_out=torch.empty(n * L, dtype=torch.int32, device=dev),
+                sample_out=torch.empty(n * L, dtype=torch.int32, device=dev),
+                accept_out=torch.empty(n * L, dtype=torch.uint8, device=dev),
+                entropy_out=torch.empty(n * L, device=dev),
+                n_accept_out=torch.empty(n, dtype=torch.int32, device=dev),
+                mean_entropy_out=torch.empty(n, device=dev),
+                stop_out=torch.empty(n, dtype=torch.uint8, device=dev))
+
+
+def _host_outputs(bufs, n, L):
+    """Per-canvas host dicts of one step's outputs."""
+    g = {k: v.cpu().numpy() for k, v in bufs.items()}
+    out = []
+    for c in range(n):
+        sl = slice(c * L, (c + 1) * L)
+        out.append(dict(entropy=g["entropy_out"][sl], argmax=g["argmax_out"][sl], sample=g["sample_out"][sl],
+                        accept=g["accept_out"][sl], n_accept=g["n_accept_out"][c], canvas=g["canvas_out"][sl],
+                        mean_entropy=g["mean_entropy_out"][c], stop=g["stop_out"][c]))
+    return out
+
+
+def cpu_baseline_leg(torch, B, synth, c2, c5):
+    """The oracle on the host cores, on bounded samples of each workload, and
+    its agreement with the GPU on the very same inputs.
+
+    Timing (cpu_baseline): the oracle as it stands (oracle.sampler's row
+    statistics and decisions; oracle.parallel only spreads rows over a thread
+    pool) on the benchmark's own four logits buffers (single canvas, 256 x
+    262144 bf16, steps 0-3 of the 16-step schedule), all host threads up to 16;
+    one of those steps is also timed on one thread.
+
+    Agreement (parity): each sample's GPU outputs against the oracle's under
+    the test suite's comparison policy (tests/full_parity.py compare_step:
+    |dH| <= 1e-4, bit-exact integers except counted near-ties): C1 one step;
+    C2 the four benchmark steps; C3 one step of 16 canvases (step 6, row
+    loop); C4 two steps; C5 canvas 0 of the LM-head step (its oracle logits
+    are the exact fp64 products)."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from full_parity import Tally, compare_step
+    from oracle import parallel as OPAR
+
+    L = 256
+    threads = OPAR.default_threads()
+    b32, thr32 = np.float32(0.1), np.float32(0.005)
+
+    def host(t):
+        return t.to("cpu").to(torch.float32).numpy()
+
+    def job(zc, V, temp, seed, step, prev=None):
+        return dict(rows=lambda r0, r1, zc=zc: zc[r0:r1], L=L, V=V, temp=np.float32(temp), seed=seed,
+                    step=step, prev_argmax=prev)
+
+    def compare(tally, gpu, orc, label, **kw):
+        try:
+            compare_step(gpu, orc, label, tally, b32, thr32, **kw)
+        except AssertionError as e:
+            tally.clauses.append(f"MISMATCH {e}")
+
+    def gpu_step(V, zs, temps, seeds, step, dtype, prev=None):
+        n = len(seeds)
+        ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=n)
+        z = torch.cat(zs) if len(zs) > 1 else zs[0]
+        bufs = _step_buffers(torch, n, L)
+        ctx.dg_sampler_step(z, torch.tensor(temps, device="cuda"), step,
+                            torch.tensor(seeds, dtype=torch.int64, device="cuda"), ctx.step_out(**bufs),
+                            prev_argmax=prev)
+        torch.cuda.synchronize()
+        out = _host_outputs(bufs, n, L)
+        ctx.close()
+        return out
+
+    parity = {}
+    # C2: the benchmark's buffers; steps r = 0..3 chained by the previous argmax
+    tally = Tally("C2")
+    jobs, prev = [], None
+    for r in range(len(c2["logits"])):
+        jobs.append(job(host(c2["logits"][r]), 262144, c2["temps"][r], 0, r, prev))
+        prev = c2["gpu"][r]["argmax"].astype(np.int64)
+    t0 = time.perf_counter()
+    orcs = OPAR.steps(jobs, threads=threads, bound=b32, stop_threshold=thr32)
+    t_all = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    OPAR.steps(jobs[:1], threads=1, bound=b32, stop_threshold=thr32)
+    t_one = time.perf_counter() - t0
+    for r, (g, o) in enumerate(zip(c2["gpu"], orcs)):
+        compare(tally, g, o, f"C2 step {r}")
+    parity["C2"] = tally.record()
+    cpu = {"value": len(jobs) / t_all, "unit": "steps/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(jobs)} full oracle steps of the benchmark workload (its 4 logits buffers: "
+                     f"256 rows x 262144 bf16, steps 0-3), fp64 numpy row statistics over {threads} "
+                     f"threads ({os.cpu_count()} host CPUs visible)",
+           "single_thread_steps_per_s": 1.0 / t_one, "seconds": t_all + t_one}
+    del jobs, orcs
+
+    # C1: one margin step, 256 x 4096 fp32
+    tally = Tally("C1")
+    z = synth.margin_logits(1001, L, 4096, m_max=12.0, dtype=torch.float32, device="cuda")
+    g = gpu_step(4096, [z], [0.8], [0], 0, torch.float32)[0]
+    compare(tally, g, OPAR.steps([job(host(z), 4096, 0.8, 0, 0)], threads=threads)[0], "C1")
+    parity["C1"] = tally.record()
+
+    # C3: one step of 16 canvases (step 6 of the 16-step schedule)
+    tally = Tally("C3")
+    n, step = 16, 6
+    t = B.dg_temperature(B.params_default(temp_steps=16), step)
+    zs = [synth.sharpening_logits((1003 << 32) | c, step, L, 262144, m0_max=8.0, dtype=torch.bfloat16,
+                                  device="cuda") for c in range(n)]
+    gs = gpu_step(262144, zs, [t] * n, list(range(n)), step, torch.bfloat16)
+    orcs = OPAR.steps([job(host(zs[c]), 262144, t, c, step) for c in range(n)], threads=threads)
+    for c in range(n):
+        compare(tally, gs[c], orcs[c], f"C3 canvas {c}")
+    parity["C3"] = tally.record()
+    del zs, orcs
+
+    # C4: steps 0 and 1 of the untrained stand-in (fp32 iid N(0, 0.05))
+    tally = Tally("C4")
+    prev_g, prev_o = None, None
+    params = B.params_default()
+    for step in range(2):
+        z = synth.iid_normal_logits(1004, step, L, 262144, variance=0.05, dtype=torch.float32, device="cuda")
+        t = B.dg_temperature(params, step)
+        g = gpu_step(262144, [z], [t], [0], step, torch.float32, prev=prev_g)[0]
+        o = OPAR.steps([job(host(z), 262144, t, 0, step, prev_o)], threads=threads)[0]
+        compare(tally, g, o, f"C4 step {step}")
+        prev_g = torch.as_tensor(g["argmax"], device="cuda")
+        prev_o = o["argmax"]
+    parity["C4"] = tally.record()
+
+    # C5: canvas 0 of the LM-head step against the exact products
+    if c5:
+        tally = Tally("C5")
+        from oracle import lmhead as OL
+        exact = OL.logits(c5["hidden"], c5["weight"])
+        err = np.abs(c5["logits"].astype(np.float64) - exact).max(axis=1)
+        o = OPAR.steps([job(exact, exact.shape[1], c5["temp"], c5["seed"], c5["step"])], threads=threads)[0]
+        compare(tally, c5["gpu"], o, "C5 canvas 0", logit_err=err, z=exact, temp=np.float32(c5["temp"]))
+        parity["C5"] = dict(tally.record(), max_logit_error=float(err.max()),
+                            note="canvas 0 of 64 (step 0, T 0.8); oracle logits are exact fp64 products")
+    for rec in parity.values():
+        rec["match"] = not any(c.startswith("MISMATCH") for c in rec["clauses"])
+    return cpu, parity
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--rotate", type=int, default=4, help="logits buffers (>= 4 beats the LLC)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head step")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch and dtype sweep")
@@ -688,19 +845,18 @@ def main():
     achieved = bytes_per_launch / stats_s / 1e9
     traffic = _traffic(bytes_per_launch)
 
-    cpu = None
+    # every output of one step on each benchmark buffer (steps 0..R-1, each
+    # after the previous one), for the oracle comparison
+    c2 = None
     if not args.no_cpu_baseline:
-        from oracle import sampler as O
-        z = logits[0].to("cpu").to(torch.float64).numpy()
-        temp = np.float32(temps[0].item())
-        n, t0 = 0, time.perf_counter()
-        while n == 0 or time.perf_counter() - t0 < args.cpu_seconds:
-            O.step(z, temp, 0, 0)
-            n += 1
-        dt = time.perf_counter() - t0
-        cpu = {"value": n / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n} full oracle steps of the same workload (256 rows x 262144 bf16 "
-                         f"logits, fp64 numpy, one thread) on {os.cpu_count()} host cores"}
+        c2 = {"logits": logits, "temps": [float(t.item()) for t in temps], "gpu": []}
+        prev = None
+        for r in range(R):
+            bufs = _step_buffers(torch, 1, L)
+            ctx.dg_sampler_step(logits[r], temps[r], r, seeds, ctx.step_out(**bufs), prev_argmax=prev)
+            torch.cuda.synchronize()
+            c2["gpu"].append(_host_outputs(bufs, 1, L)[0])
+            prev = bufs["argmax_out"]
 
     rec = {
         "metric": METRIC, "value": steps_per_s, "unit": "steps/s", "n_gpus": 1,
@@ -721,14 +877,18 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_per_launch,
                      "frac_of_read_ceiling": read_ceiling["GB/s"] and achieved / read_ceiling["GB/s"]},
         "read_ceiling": read_ceiling,
-        "cpu_baseline": cpu,
+        "cpu_baseline": None,
+        "parity": None,
         "sweep": None if args.no_sweep else sweep_leg(torch, B, synth),
         "exp_b": None if args.no_exp_b else exp_b_leg(torch, B, synth),
         "run_loop": None if args.no_run_loop else run_loop_leg(torch, B, synth),
         "generate": None if args.no_generate else generate_leg(torch, B, synth),
         "selfcond": None if args.no_selfcond else selfcond_leg(torch, B, synth),
-        "lmhead": None if args.no_lmhead else lmhead_leg(args, torch, B, synth),
     }
+    c5 = {} if not args.no_cpu_baseline and not args.no_lmhead else None
+    rec["lmhead"] = None if args.no_lmhead else lmhead_leg(args, torch, B, synth, keep=c5)
+    if c2 is not None:
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline_leg(torch, B, synth, c2, c5)
     print(json.dumps(rec), flush=True)
     ctx.close()
 

@@ -28,7 +28,24 @@ Pins (tests/test_oracle_*.py, run with -m "not gpu"):
                          columns exactly; power-of-two scaling is exact
   lmhead.step            zero hidden states give uniform logits: H = ln V at
                          every position and exactly one commit
-No function is parity-unpinned; the bit-level choice of random protocol is
-pinned only by agreement of the two independent implementations.
+  selfcond.self_condition one-hot rows select an embedding row; uniform rows
+                         average the embedding; a column of ones gives total
+                         probability 1; indicator columns equal brute-force
+                         probability sums; an index column gives the closed-form
+                         truncated geometric mean; linear in E, invariant to
+                         logit shifts (tests/test_oracle_selfcond.py)
+  blockar.canvas_seed    Philox words of the canvas counter (known-answer
+                         vectors via philox); blockar.tokens_per_forward and
+                         tokens_per_second: the pages' own TPS arithmetic
+                         (tests/golden/tps_worked_example_boxwrench.txt);
+  blockar.generate       a never-confident stream runs every canvas to the
+                         cap, a certain stream stops every canvas at step two
+                         and chains its targets (tests/test_oracle_blockar.py)
+  parallel.steps         equal, key for key, to sampler.step on the same rows
+                         (it only spreads sampler.row_statistics over threads)
+No function is parity-unpinned. The bit-level choice of the random protocol
+(block partition, grouping of the block words) is pinned only by agreement
+of the two independent implementations; the pages fix the sample in
+distribution only, which the chi-square tests pin.
 """
-from . import lmhead, philox, sampler  # noqa: F401
+from . import blockar, lmhead, parallel, philox, sampler, selfcond  # noqa: F401
