@@ -30,7 +30,7 @@ EXPORTS = ["dg_params_default", "dg_params_check", "dg_create", "dg_destroy", "d
            "dg_canvas_stats", "dg_accept_renoise", "dg_sampler_step", "dg_run_canvas",
            "dg_run_canvas_resident", "dg_generate", "dg_tokens_per_forward",
            "dg_self_condition", "dg_sampler_step_selfcond",
-           "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_version"]
+           "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_sampler_step_noalloc", "dg_version"]
 
 
 class DgParams(ctypes.Structure):
@@ -98,6 +98,8 @@ def lib():
             "dg_lmhead_logits": [vp, i32, vp, vp, i32, vp, i64, vp],
             "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp,
                                        ctypes.POINTER(DgStepOut), vp],
+            "dg_sampler_step_noalloc": [ctypes.POINTER(DgParams), i32, vp, ctypes.c_int, i64, vp, i32, vp, vp,
+                                        vp, ctypes.POINTER(DgStepOut), vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -377,6 +379,18 @@ class Context:
 
 
 _hip = None
+
+
+def sampler_step_noalloc(params, logits, temperature, step, seeds, out, prev_argmax=None, active=None,
+                         batch=None, row_stride=None, stream=None):
+    """dg_sampler_step_noalloc: one step with no context and no allocation
+    (static device scratch); arguments as Context.dg_sampler_step plus the
+    params of the step."""
+    B = batch if batch is not None else seeds.shape[0]
+    stride = row_stride if row_stride is not None else logits.stride(0)
+    _check(lib().dg_sampler_step_noalloc(ctypes.byref(params), B, _ptr(logits), _dtype_code(logits), stride,
+                                         _ptr(temperature), step, _ptr(seeds), _ptr(prev_argmax), _ptr(active),
+                                         ctypes.byref(out), _stream(stream)))
 
 
 def copy_from_device(dst, src_ptr, stream=None):

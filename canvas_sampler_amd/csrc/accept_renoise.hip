@@ -66,7 +66,19 @@ __global__ void place_canvas_kernel(const int32_t* __restrict__ canvas, int32_t 
   tokens[c * ld + offset + (i - c * canvas_len)] = canvas[i];
 }
 
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int32_t n, uint32_t value) {
+  const int32_t i = static_cast<int32_t>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = value;
+}
+
 }  // namespace
+
+hipError_t launch_fill_u32(uint32_t* p, int32_t n, uint32_t value, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int threads = 256;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((n + threads - 1) / threads), dim3(threads), 0, stream, p, n, value);
+  return hipGetLastError();
+}
 
 hipError_t launch_canvas_seeds(const uint64_t* seeds, int32_t batch, int32_t k, uint64_t* out,
                                hipStream_t stream) {

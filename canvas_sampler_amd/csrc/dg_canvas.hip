@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -117,22 +118,28 @@ dg_status check_batch(dg_ctx* ctx, int32_t B) {
   return DG_OK;
 }
 
+dg_status check_logits_v(dg_ctx* ctx, int32_t vocab, const void* logits, dg_dtype dtype, int64_t row_stride);
+
 dg_status check_logits(dg_ctx* ctx, const void* logits, dg_dtype dtype, int64_t row_stride) {
+  return check_logits_v(ctx, ctx->p.vocab, logits, dtype, row_stride);
+}
+
+dg_status check_logits_v(dg_ctx* ctx, int32_t vocab, const void* logits, dg_dtype dtype, int64_t row_stride) {
   if (!logits) return set_err(ctx, DG_ERR_INVALID_ARG, "logits is NULL");
   if (dtype != DG_DTYPE_F32 && dtype != DG_DTYPE_BF16)
     return set_err(ctx, DG_ERR_INVALID_ARG, "dtype = %d is not DG_DTYPE_F32 or DG_DTYPE_BF16",
                    static_cast<int>(dtype));
-  if (row_stride < ctx->p.vocab)
+  if (row_stride < vocab)
     return set_err(ctx, DG_ERR_INVALID_ARG, "row_stride = %lld is below vocab (%d)",
-                   static_cast<long long>(row_stride), ctx->p.vocab);
+                   static_cast<long long>(row_stride), vocab);
   if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0)
     return set_err(ctx, DG_ERR_UNSUPPORTED, "logits is not 16-byte aligned");
   const int64_t per16 = dtype == DG_DTYPE_BF16 ? 8 : 4;
-  const int64_t row_bytes = static_cast<int64_t>(ctx->p.vocab) * (16 / per16);
+  const int64_t row_bytes = static_cast<int64_t>(vocab) * (16 / per16);
   if (row_bytes > kMaxRowBytes)
     return set_err(ctx, DG_ERR_UNSUPPORTED,
                    "vocab = %d is too large for this dtype: a row must hold at most %lld bytes",
-                   ctx->p.vocab, static_cast<long long>(kMaxRowBytes));
+                   vocab, static_cast<long long>(kMaxRowBytes));
   if (row_stride % per16 != 0)
     return set_err(ctx, DG_ERR_UNSUPPORTED,
                    "row_stride = %lld must be a multiple of %lld elements (16 bytes)",
@@ -146,17 +153,26 @@ int32_t effective_nsplit(const dg_ctx* ctx, int32_t rows) {
   return n < 1 ? 1 : n;
 }
 
-dg::StatsArgs stats_args(const dg_ctx* ctx, int32_t B, const void* logits, int64_t row_stride,
-                         const float* temperature, int32_t step, const int32_t* steps,
-                         const uint64_t* seeds, const uint8_t* active, float* entropy, int32_t* argmax,
-                         int32_t* sample) {
+// Device resources a step's kernels work in: the context's scratch, or the
+// static scratch of dg_sampler_step_noalloc.
+struct StepScratch {
+  int32_t nsplit;
+  int32_t cu_count;
+  dg::RowPartial* partials;
+  uint32_t* tickets;
+};
+
+dg::StatsArgs make_stats_args(const dg_params& p, const StepScratch& sc, int32_t B, const void* logits,
+                              int64_t row_stride, const float* temperature, int32_t step, const int32_t* steps,
+                              const uint64_t* seeds, const uint8_t* active, float* entropy, int32_t* argmax,
+                              int32_t* sample) {
   dg::StatsArgs a{};
   a.logits = logits;
   a.row_stride = row_stride;
-  a.vocab = ctx->p.vocab;
-  a.canvas_len = ctx->p.canvas_len;
-  a.rows = B * ctx->p.canvas_len;
-  a.nsplit = effective_nsplit(ctx, a.rows);
+  a.vocab = p.vocab;
+  a.canvas_len = p.canvas_len;
+  a.rows = B * p.canvas_len;
+  a.nsplit = sc.nsplit;
   a.temperature = temperature;
   a.seeds = seeds;
   a.step = step;
@@ -165,10 +181,19 @@ dg::StatsArgs stats_args(const dg_ctx* ctx, int32_t B, const void* logits, int64
   a.entropy = entropy;
   a.argmax = argmax;
   a.sample = sample;
-  a.partials = ctx->partials;
-  a.tickets = ctx->tickets;
-  a.row_grid = dg::stats_row_grid(a.rows, a.vocab, a.nsplit, active != nullptr, ctx->cu_count);
+  a.partials = sc.partials;
+  a.tickets = sc.tickets;
+  a.row_grid = dg::stats_row_grid(a.rows, a.vocab, a.nsplit, active != nullptr, sc.cu_count);
   return a;
+}
+
+dg::StatsArgs stats_args(const dg_ctx* ctx, int32_t B, const void* logits, int64_t row_stride,
+                         const float* temperature, int32_t step, const int32_t* steps,
+                         const uint64_t* seeds, const uint8_t* active, float* entropy, int32_t* argmax,
+                         int32_t* sample) {
+  const StepScratch sc{effective_nsplit(ctx, B * ctx->p.canvas_len), ctx->cu_count, ctx->partials, ctx->tickets};
+  return make_stats_args(ctx->p, sc, B, logits, row_stride, temperature, step, steps, seeds, active, entropy,
+                         argmax, sample);
 }
 
 dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
@@ -181,10 +206,10 @@ dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dty
   return DG_OK;
 }
 
-dg::AcceptArgs accept_args(const dg_ctx* ctx, const float* entropy, const int32_t* argmax,
-                           const int32_t* sample, int32_t step, const int32_t* steps,
-                           const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
-                           const dg_step_out* out, bool copy_stats) {
+dg::AcceptArgs make_accept_args(const dg_params& p, const float* entropy, const int32_t* argmax,
+                                const int32_t* sample, int32_t step, const int32_t* steps,
+                                const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                                const dg_step_out* out, bool copy_stats) {
   dg::AcceptArgs a{};
   a.entropy = entropy;
   a.argmax = argmax;
@@ -194,10 +219,10 @@ dg::AcceptArgs accept_args(const dg_ctx* ctx, const float* entropy, const int32_
   a.active = active;
   a.step = step;
   a.steps = steps;
-  a.canvas_len = ctx->p.canvas_len;
-  a.vocab = ctx->p.vocab;
-  a.bound = ctx->p.entropy_bound;
-  a.stop_mean_entropy = ctx->p.stop_mean_entropy;
+  a.canvas_len = p.canvas_len;
+  a.vocab = p.vocab;
+  a.bound = p.entropy_bound;
+  a.stop_mean_entropy = p.stop_mean_entropy;
   a.canvas_out = out->canvas_out;
   if (copy_stats) {
     a.argmax_out = out->argmax_out;
@@ -209,6 +234,14 @@ dg::AcceptArgs accept_args(const dg_ctx* ctx, const float* entropy, const int32_
   a.mean_entropy_out = out->mean_entropy_out;
   a.stop_out = out->stop_out;
   return a;
+}
+
+dg::AcceptArgs accept_args(const dg_ctx* ctx, const float* entropy, const int32_t* argmax,
+                           const int32_t* sample, int32_t step, const int32_t* steps,
+                           const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                           const dg_step_out* out, bool copy_stats) {
+  return make_accept_args(ctx->p, entropy, argmax, sample, step, steps, seeds, prev_argmax, active, out,
+                          copy_stats);
 }
 
 dg_status enqueue_accept(dg_ctx* ctx, int32_t B, const float* entropy, const int32_t* argmax,
@@ -822,6 +855,116 @@ dg_status dg_tokens_per_forward(const int32_t* steps_used, int32_t n_canvases, i
     if (tpf) tpf[c] = static_cast<double>(n_canvases) * canvas_len / static_cast<double>(fwd);
   }
   if (tpf_all) tpf_all[0] = static_cast<double>(n_canvases) * B * canvas_len / static_cast<double>(all);
+  return DG_OK;
+}
+
+}  // extern "C"
+
+// ---- One step that allocates nothing (dg_sampler_step_noalloc) ----
+//
+// The step's intermediate statistics, split-row partials and tickets live in
+// `scratch`, a static array of device memory that every GPU the library runs
+// on holds until the process ends. Host code never passes the array's name to
+// a kernel: on the host that name is a stand-in, not a device address. Its
+// address on each device is taken once, with the device current, through
+// hipGetSymbolAddress and used from then on.
+
+namespace {
+
+constexpr int32_t kNoAllocMaxRows = 16384;     // B * L at most: 64 canvases of 256 positions
+constexpr int32_t kNoAllocMaxPartials = 256;   // split rows: rows * nsplit <= 128 when nsplit > 1
+constexpr int32_t kNoAllocMaxTickets = 256;
+constexpr size_t kNoAllocEntropyOff = 0;
+constexpr size_t kNoAllocArgmaxOff = kNoAllocEntropyOff + sizeof(float) * kNoAllocMaxRows;
+constexpr size_t kNoAllocSampleOff = kNoAllocArgmaxOff + sizeof(int32_t) * kNoAllocMaxRows;
+constexpr size_t kNoAllocPartialOff = kNoAllocSampleOff + sizeof(int32_t) * kNoAllocMaxRows;
+constexpr size_t kNoAllocTicketOff = kNoAllocPartialOff + sizeof(dg::RowPartial) * kNoAllocMaxPartials;
+constexpr size_t kNoAllocBytes = kNoAllocTicketOff + sizeof(uint32_t) * kNoAllocMaxTickets;
+static_assert(kNoAllocPartialOff % 256 == 0, "partials stay 256-byte aligned");
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+
+constexpr int kNoAllocMaxDevices = 64;
+
+struct NoAllocDevice {
+  unsigned char* base = nullptr;   // device address of `scratch` on this device
+  int32_t cu_count = 0;
+};
+
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+
+// The current device's copy of `scratch`, looked up on the first call on each
+// device (with that device current) and kept for the process.
+dg_status noalloc_device(NoAllocDevice* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return set_err(nullptr, DG_ERR_DEVICE, "no current HIP device");
+  if (dev >= kNoAllocMaxDevices)
+    return set_err(nullptr, DG_ERR_UNSUPPORTED, "device %d is beyond the %d devices supported", dev,
+                   kNoAllocMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoAllocDevice& d = g_noalloc[dev];
+  if (d.base == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_err(nullptr, DG_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cu = 0;
+    d.cu_count = cu;
+    d.base = static_cast<unsigned char*>(p);
+  }
+  *out = d;
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_sampler_step_noalloc(const dg_params* params, int32_t B, const void* logits, dg_dtype dtype,
+                                  int64_t row_stride, const float* temperature, int32_t step,
+                                  const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                                  const dg_step_out* out, void* stream) {
+  dg_status st = check_params(nullptr, params);
+  if (st != DG_OK) return st;
+  const dg_params& p = *params;
+  if (B < 1) return set_err(nullptr, DG_ERR_INVALID_ARG, "B = %d must be >= 1", B);
+  if (static_cast<int64_t>(B) * p.canvas_len > kNoAllocMaxRows)
+    return set_err(nullptr, DG_ERR_INVALID_ARG,
+                   "B * canvas_len = %lld exceeds the %d rows of the static scratch",
+                   static_cast<long long>(B) * p.canvas_len, kNoAllocMaxRows);
+  if ((st = check_logits_v(nullptr, p.vocab, logits, dtype, row_stride)) != DG_OK) return st;
+  if (!temperature) return set_err(nullptr, DG_ERR_INVALID_ARG, "temperature is NULL");
+  if (step < 0) return set_err(nullptr, DG_ERR_INVALID_ARG, "step = %d is negative", step);
+  if (!seeds) return set_err(nullptr, DG_ERR_INVALID_ARG, "seeds is NULL");
+  if (!out) return set_err(nullptr, DG_ERR_INVALID_ARG, "out is NULL");
+  if (!out->canvas_out) return set_err(nullptr, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
+  NoAllocDevice d;
+  if ((st = noalloc_device(&d)) != DG_OK) return st;
+  const int32_t rows = B * p.canvas_len;
+  int32_t nsplit = dg::choose_nsplit(rows, p.vocab);
+  if (nsplit > 1 && (static_cast<int64_t>(rows) * nsplit > kNoAllocMaxPartials || rows > kNoAllocMaxTickets))
+    return set_err(nullptr, DG_ERR_DEVICE, "split of %d rows over %d workgroups exceeds the static scratch "
+                   "(internal error)", rows, nsplit);
+  StepScratch sc{nsplit, d.cu_count, reinterpret_cast<dg::RowPartial*>(d.base + kNoAllocPartialOff),
+                 reinterpret_cast<uint32_t*>(d.base + kNoAllocTicketOff)};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ent = out->entropy_out ? out->entropy_out : reinterpret_cast<float*>(d.base + kNoAllocEntropyOff);
+  int32_t* am = out->argmax_out ? out->argmax_out : reinterpret_cast<int32_t*>(d.base + kNoAllocArgmaxOff);
+  int32_t* smp = out->sample_out ? out->sample_out : reinterpret_cast<int32_t*>(d.base + kNoAllocSampleOff);
+  // the split merge counts arrivals from zero: start every call from cleared tickets
+  if (nsplit > 1) DG_CHECK_HIP(nullptr, dg::launch_fill_u32(sc.tickets, rows, 0u, s));
+  const dg::StatsArgs a = make_stats_args(p, sc, B, logits, row_stride, temperature, step, nullptr, seeds, active,
+                                          ent, am, smp);
+  DG_CHECK_HIP(nullptr, dg::launch_canvas_stats(a, dtype == DG_DTYPE_BF16, s));
+  const dg::AcceptArgs acc = make_accept_args(p, ent, am, smp, step, nullptr, seeds, prev_argmax, active, out, false);
+  DG_CHECK_HIP(nullptr, dg::launch_accept_renoise(acc, B, s));
   return DG_OK;
 }
 

@@ -144,6 +144,8 @@ hipError_t launch_canvas_seeds(const uint64_t* seeds, int32_t batch, int32_t k, 
 // tokens[c * ld + offset + l] = canvas[c * canvas_len + l] for c < batch, l < canvas_len.
 hipError_t launch_place_canvas(const int32_t* canvas, int32_t batch, int32_t canvas_len, int32_t* tokens,
                                int64_t ld, int64_t offset, hipStream_t stream);
+// p[0..n) = value, as a kernel (so that a captured graph holds no memset node).
+hipError_t launch_fill_u32(uint32_t* p, int32_t n, uint32_t value, hipStream_t stream);
 hipError_t launch_canvas_init(const uint64_t* seeds, int32_t batch, int32_t canvas_len,
                               int32_t vocab, int32_t* canvas, hipStream_t stream);
 

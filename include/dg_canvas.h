@@ -401,6 +401,25 @@ dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, con
                                  const int32_t* prev_argmax, const uint8_t* active,
                                  const dg_step_out* out, void* stream);
 
+/* dg_sampler_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * context, no allocation of any kind. The step's intermediate statistics and
+ * split-row partials live in a static device array (about 200 KiB) that each
+ * GPU the library runs on holds until the process ends; its address is looked
+ * up once per device on the first call made with that device current.
+ *   params   host; the step's settings, as for dg_create (checked the same way)
+ *   B        1 .. 16384 / params->canvas_len (at most 16384 rows): larger
+ *            batches return DG_ERR_INVALID_ARG without writing anything
+ * The other arguments and every result are those of dg_sampler_step on the
+ * current device; the results equal dg_sampler_step's bit for bit. Every call
+ * on one GPU shares that GPU's array, and a call clears what it needs cleared,
+ * so calls that overlap on one GPU (concurrent streams) race: serialise them.
+ * Errors are reported through dg_last_error(NULL). */
+dg_status dg_sampler_step_noalloc(const dg_params* params, int32_t B, const void* logits, dg_dtype dtype,
+                                  int64_t row_stride, const float* temperature, int32_t step,
+                                  const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
+                                  const dg_step_out* out, void* stream);
+
 /* Library version string. */
 const char* dg_version(void);
 
