@@ -14,7 +14,8 @@ and one graph holding a step on each buffer) are reported too.
 
 Prints one JSON line: steps/s (value), positions/s, the statistics kernel's
 achieved HBM bandwidth against the 8 TB/s peak (HIP events on the launch
-stream), the oracle's rate on the host cores, and (under "lmhead") the step of
+stream), the oracle's rate on the host cores with the agreement of every
+configuration's sample with it ("parity"), and (under "lmhead") the step of
 64 canvases whose logits come from the bf16 LM-head product, hidden
 [16384, 2048] x weight [2048, 262144]: the product's time and matrix-core
 throughput against the 2.5 PFLOP/s dense bf16 peak, and the whole step's time.
@@ -642,8 +643,11 @@ def cpu_baseline_leg(torch, B, synth, c2, c5):
     for r in range(len(c2["logits"])):
         jobs.append(job(host(c2["logits"][r]), 262144, c2["temps"][r], 0, r, prev))
         prev = c2["gpu"][r]["argmax"].astype(np.int64)
-    t0 = time.perf_counter()
-    orcs = OPAR.steps(jobs, threads=threads, bound=b32, stop_threshold=thr32)
+    # the four steps over the thread pool, repeated for about 8 s of wall time
+    reps, t0 = 0, time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < 8.0:
+        orcs = OPAR.steps(jobs, threads=threads, bound=b32, stop_threshold=thr32)
+        reps += 1
     t_all = time.perf_counter() - t0
     t0 = time.perf_counter()
     OPAR.steps(jobs[:1], threads=1, bound=b32, stop_threshold=thr32)
@@ -651,8 +655,8 @@ def cpu_baseline_leg(torch, B, synth, c2, c5):
     for r, (g, o) in enumerate(zip(c2["gpu"], orcs)):
         compare(tally, g, o, f"C2 step {r}")
     parity["C2"] = tally.record()
-    cpu = {"value": len(jobs) / t_all, "unit": "steps/s", "cores": threads, "kind": "oracle",
-           "sample": f"{len(jobs)} full oracle steps of the benchmark workload (its 4 logits buffers: "
+    cpu = {"value": reps * len(jobs) / t_all, "unit": "steps/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} x {len(jobs)} full oracle steps of the benchmark workload (its 4 logits buffers: "
                      f"256 rows x 262144 bf16, steps 0-3), fp64 numpy row statistics over {threads} "
                      f"threads ({os.cpu_count()} host CPUs visible)",
            "single_thread_steps_per_s": 1.0 / t_one, "seconds": t_all + t_one}
