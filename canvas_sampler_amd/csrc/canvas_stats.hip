@@ -12,31 +12,34 @@
 //   - one multinomial sample (§2 item 5) by the two-level Gumbel-max protocol:
 //     a block is one 8-id slot across the 8 stripes of a 4096-id chunk; each
 //     lane forms its block's log-sum-exp on the fly and adds the block's
-//     Gumbel (one Philox call per four blocks), and the sample is the id of
-//     the best block j* with the largest z/T + element Gumbel.
+//     Gumbel, and the sample is the id of the best block j* with the largest
+//     z/T + element Gumbel.
 //
 // Layout and schedule (gfx950, wave64): rows are V-contiguous. A workgroup of
-// eight waves handles a row (or one split of it). Waves w and w + 4 share a
-// SIMD and split the chunks p + 4k (p = w mod 4) between them, the older wave
-// taking the first 10/16 of k (the SIMD's arbiter favours it); in the
-// persistent row loop wave w takes chunks w, w + 8, ... Either way the
-// workgroup streams a few stretches of consecutive memory at a time, one
-// 4096-id chunk per wave. Each lane issues one 16-byte load per 512-id
-// stripe (bf16; two for fp32); a batch is 4 stripes and a block 2 batches,
-// and a register ring holds two blocks: one is reduced while the other is in
-// flight. Loads are raw buffer loads on a per-row resource (hardware range
-// check, no branches), marked non-temporal. Per element the loop costs one
-// convert, half a max, one fma, one v_exp_f32, one add and one fma; per four
-// blocks of a group (256 ids per lane) one Philox call. When a block ends its logits are
-// still in registers, so nothing is read twice: if the block beats the wave's
-// best block, or a lane of it holds a new wave maximum, that lane parks the
-// block's 64 logits in LDS, and after its stream the wave draws the sample in
-// its best block and finds the first id of its maximum from the parked
-// logits. The workgroup then merges eight 40-byte partials. With more rows
-// than compute units a persistent grid loops over the rows, and the register
-// ring runs on into the next row. A row split over several workgroups (for
-// very short batches) is merged by the last workgroup to finish (atomic
-// ticket, release/acquire at agent scope).
+// eight waves handles a row (or one split of it); with more rows than
+// compute units a persistent grid loops over the rows. Wave w streams chunks
+// w, w + 8, ... so the workgroup reads eight consecutive 4096-id chunks at a
+// time. Each lane issues one 16-byte load per 512-id stripe (bf16; two for
+// fp32); a batch is 4 stripes and a block 2 batches, and a register ring
+// holds two blocks: one is reduced while the other is in flight. The loops
+// take the blocks in pairs so that every path into them leaves the two
+// slots' loads in the same order and a block waits for its own loads only.
+// Loads are raw buffer loads on a per-row resource (hardware range check, no
+// branches), marked non-temporal; the per-canvas inputs are scalar loads, so
+// they never wait behind the stream. Per element the loop costs one convert,
+// half a max, one fma, one v_exp_f32, one add and one fma; per block one
+// wave-uniform test for the rare cases, one log2 and two ballots. The block
+// Gumbels are not drawn in the stream: the workgroup draws those of a whole
+// segment of 64 chunks into LDS beforehand (the first while the first loads
+// are in flight, the next ones before the barrier that ends a segment or a
+// row). When a block ends its logits are still in registers, so nothing is
+// read twice: if the block beats the wave's best block, or a lane of it holds
+// a new wave maximum, that lane parks the block's 64 logits in LDS, and after
+// its stream the wave draws the sample in its best block and finds the first
+// id of its maximum from the parked logits. The workgroup then merges eight
+// 32-byte partials. A row split over several workgroups (for very short
+// batches) is merged by the last workgroup to finish (atomic ticket,
+// release/acquire at agent scope).
 #include <type_traits>
 
 #include "device_common.h"
@@ -278,32 +281,6 @@ __device__ __forceinline__ void slow_batch(const uint4 (&buf)[NB * Geometry<kBf1
   st.wb += bw;
 }
 
-// Reduces one complete batch (every id below V) into the lane state and
-// returns its maximum raw logit. The exponentials use the reference of the
-// batches before (it lags the running maximum), so each chunk is reduced as
-// soon as its load lands instead of after a batch-wide maximum; the batch
-// maximum is folded in afterwards. A lag of up to 2^64 cannot overflow fp32;
-// the rare batches that need more go to the slow path, behind a wave-uniform
-// branch.
-template <bool kBf16, int NB>
-__device__ __forceinline__ float fast_batch(const uint4 (&buf)[NB * Geometry<kBf16>::kLoadsPerStripe],
-                                            int64_t id0, int32_t vocab, float c, LaneState& st) {
-  constexpr float kMaxLag = 64.0f;
-  float bs, bw;
-  const float bm = chunked_sums<kBf16, NB>(buf, c, st.ref, bs, bw);
-  const float bref = __fmul_rn(bm, c);
-  const bool bad = !(bw == bw) || !(bref <= st.ref + kMaxLag);  // NaN, fresh lane, or a big jump
-  if (__builtin_amdgcn_ballot_w64(bad) != 0 && bad) {
-    slow_batch<kBf16, NB>(buf, id0, vocab, c, false, st);
-  } else {
-    st.sb += bs;
-    st.wb += bw;
-  }
-  const bool lift = bref > st.ref + kRefSlack;
-  if (__builtin_amdgcn_ballot_w64(lift) != 0 && lift) rebase(st, bref);
-  return bm;
-}
-
 // Reduces the batch that crosses V (ids past V masked) and returns its
 // maximum raw logit below V.
 template <bool kBf16, int NB>
@@ -447,17 +424,6 @@ struct WaveResult {
   int64_t best_base = 0;
 };
 
-// The Philox call behind a block's Gumbel: blocks that differ only in bits
-// 9-10 of j (chunks 8 apart: chunk c lies in the group of four chunks
-// c & ~24) share the call with counter c0 = j with those bits cleared, block
-// j taking word (j >> 9) & 3.
-constexpr int32_t kDrawGroupChunks = 32;  // chunks spanned by one group of four block draws
-
-// Share of a SIMD pair's chunks that its younger wave streams, in
-// sixteenths (measured at 256 x 262144 bf16: 8/16 27.4 us, 6/16 26.7 us,
-// 5/16 26.7 us, 4/16 27.4 us).
-constexpr int32_t kYoungShare16 = 6;
-
 // Per-row constants of a pass.
 struct RowConsts {
   int32_t pos;      // canvas position (counter word 1)
@@ -467,97 +433,80 @@ struct RowConsts {
   float inv_t;      // 1 / T: z/T as z * (1/T), within an ulp of the quotient
 };
 
-__device__ __forceinline__ Words4 group_words(int32_t group_chunk, int lane, const RowConsts& rc) {
-  return philox4x32_10(static_cast<uint32_t>(group_chunk * kSlots + lane), static_cast<uint32_t>(rc.pos),
-                       static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
+// Splits of a row start at multiples of 32 chunks, where the groups of four
+// block draws that share a Philox call start (see fill_gumbels).
+constexpr int32_t kDrawGroupChunks = 32;
+
+// Blocks in flight per wave (the register ring's depth). Measured at 256 x
+// 262144 (one-row kernel) and 16 x 256 x 262144 (row loop): bf16 rows 27.0
+// us with two blocks against 28.0 with one; fp32 rows 50.0 us with one
+// against 51.3 with two; the bf16 row loop 356 us with two against 384 with
+// one.
+template <bool kBf16>
+constexpr int kRowRing = kBf16 ? 2 : 1;
+constexpr int kRowsRing = 2;
+
+// A segment: 64 consecutive chunks of a row (4096 blocks; the whole row at
+// V = 262144), whose block Gumbels sit in LDS while its blocks are closed.
+constexpr int32_t kSegChunks = 64;
+constexpr int32_t kSegBlocks = kSegChunks * kSlots;
+
+
+// The block Gumbels of the chunks [cb, ce) of the segment starting at chunk
+// seg0, in log2 units: g2[(c - seg0) * 64 + slot] = log2(e) * G_j for block
+// j = 64 c + slot. One Philox call serves the four blocks whose numbers differ
+// only in bits 9-10 of j (chunks c0, c0 + 8, c0 + 16, c0 + 24 with bits 3-4 of
+// c0 clear, inside an aligned group of 32 chunks): counter word 0 is j with
+// those bits cleared and block j takes word (j >> 9) & 3. The workgroup's
+// threads share the segment's 1024 calls.
+__device__ __forceinline__ void fill_gumbels(float* g2, int32_t seg0, int32_t cb, int32_t ce, const RowConsts& rc,
+                                             int tid) {
+  for (int32_t i = tid; i < kSegBlocks / 4; i += kStatsThreads) {
+    const int32_t c0 = seg0 + 32 * (i >> 9) + ((i >> 6) & 7);
+    const int32_t slot = i & (kSlots - 1);
+    if (c0 + 24 < cb || c0 >= ce) continue;
+    const Words4 w = philox4x32_10(static_cast<uint32_t>(c0 * kSlots + slot), static_cast<uint32_t>(rc.pos),
+                                   static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int32_t c = c0 + 8 * q;
+      if (c >= cb && c < ce) g2[(c - seg0) * kSlots + slot] = kLog2e * gumbel(w.w[q]);
+    }
+  }
 }
 
-// Block words for a wave whose blocks are chunks 8 apart, four to a group
-// (block i % 4 == 0 starts a group): a shift register, so that block i takes
-// w0 and no word is picked by a runtime index.
-struct ShiftWords {
-  uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-  __device__ __forceinline__ uint32_t take(int32_t chunk, int32_t i, int lane, const RowConsts& rc) {
-    if ((i & 3) == 0) {  // chunk & 24 == 0
-      const Words4 rw = group_words(chunk, lane, rc);
-      w0 = rw.w[0];
-      w1 = rw.w[1];
-      w2 = rw.w[2];
-      w3 = rw.w[3];
+// The Gumbels of a wave's own blocks in the one-row kernel, where wave w
+// takes chunks c_begin + w + 8i (c_begin a multiple of 32): its blocks
+// 4m .. 4m + 3 are one group of the draws above, so one Philox call at block
+// 4m gives all four, kept as a shift register (block i takes g0).
+struct WaveGumbels {
+  float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f;
+  __device__ __forceinline__ float take(int32_t i, int32_t chunk, int lane, const RowConsts& rc) {
+    if ((i & 3) == 0) {
+      const Words4 w = philox4x32_10(static_cast<uint32_t>(chunk * kSlots + lane), static_cast<uint32_t>(rc.pos),
+                                     static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
+      g0 = kLog2e * gumbel(w.w[0]);
+      g1 = kLog2e * gumbel(w.w[1]);
+      g2 = kLog2e * gumbel(w.w[2]);
+      g3 = kLog2e * gumbel(w.w[3]);
     }
-    const uint32_t word = w0;
-    w0 = w1;
-    w1 = w2;
-    w2 = w3;
-    return word;
+    const float g = g0;
+    g0 = g1;
+    g1 = g2;
+    g2 = g3;
+    return g;
   }
 };
 
-// Block words for the blocks of one wave of a SIMD pair, taken in increasing
-// k (chunk c_begin + p + 4 k): the blocks of either parity of k form a run
-// of consecutive words of consecutive groups (word (k >> 1) & 3 of group
-// c & ~24), so each parity keeps a shift register as above. A parity's run
-// may start in the middle of a group; its first block then skips the words
-// before its own.
-struct PairWords {
-  uint32_t e0 = 0, e1 = 0, e2 = 0, e3 = 0;  // even k
-  uint32_t o0 = 0, o1 = 0, o2 = 0, o3 = 0;  // odd k
-  bool e_live = false, o_live = false;
-  __device__ __forceinline__ uint32_t take(int32_t chunk, int32_t k, int lane, const RowConsts& rc) {
-    const int idx = (k >> 1) & 3;
-    uint32_t word;
-    if (k & 1) {
-      if (idx == 0 || !o_live) {
-        const Words4 rw = group_words(chunk & ~(3 * kChunkStripes), lane, rc);
-        o0 = rw.w[0];
-        o1 = rw.w[1];
-        o2 = rw.w[2];
-        o3 = rw.w[3];
-        for (int q = 0; q < idx; ++q) {
-          o0 = o1;
-          o1 = o2;
-          o2 = o3;
-        }
-        o_live = true;
-      }
-      word = o0;
-      o0 = o1;
-      o1 = o2;
-      o2 = o3;
-    } else {
-      if (idx == 0 || !e_live) {
-        const Words4 rw = group_words(chunk & ~(3 * kChunkStripes), lane, rc);
-        e0 = rw.w[0];
-        e1 = rw.w[1];
-        e2 = rw.w[2];
-        e3 = rw.w[3];
-        for (int q = 0; q < idx; ++q) {
-          e0 = e1;
-          e1 = e2;
-          e2 = e3;
-        }
-        e_live = true;
-      }
-      word = e0;
-      e0 = e1;
-      e1 = e2;
-      e2 = e3;
-    }
-    return word;
-  }
-};
-
-template <bool kBf16, int NB>
-using Ring = uint4[2][kChunkStripes / NB][NB * Geometry<kBf16>::kLoadsPerStripe];
+template <bool kBf16, int NB, int R = 2>
+using Ring = uint4[R][kChunkStripes / NB][NB * Geometry<kBf16>::kLoadsPerStripe];
 
 // Block j (first id base, its 64 logits per lane in ring slot H) ends; bmax
-// is the lane's maximum over them below V.
-// seq is the block's place in the wave's sequence, as its word source counts it.
-template <bool kBf16, int NB, int H, class Words>
-__device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t j, int32_t seq,
-                                            float bmax, int32_t vocab, const RowConsts& rc, LaneState& st,
-                                            WaveResult& wr, Words& bw, uint4* park_best, uint4* park_max,
-                                            int lane) {
+// is the lane's maximum over them below V and g2 its Gumbel in log2 units.
+template <bool kBf16, int NB, int H, int R>
+__device__ __forceinline__ void close_block(const Ring<kBf16, NB, R>& buf, int64_t base, int32_t j, float bmax,
+                                            float g2, LaneState& st, WaveResult& wr, uint4* park_best,
+                                            uint4* park_max, int lane) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
   // ---- argmax: the wave maximum rises. Blocks come in increasing id order,
   // so an equal later maximum never replaces an earlier one. With one holding
@@ -593,9 +542,8 @@ __device__ __forceinline__ void close_block(const Ring<kBf16, NB>& buf, int64_t 
   }
 
   // ---- its score is its log-sum-exp plus its Gumbel
-  const uint32_t word = bw.take(static_cast<int32_t>(base / kChunkIds), seq, lane, rc);
   float score = kNegInf;
-  if (st.sb > 0.f) score = st.ref + __log2f(st.sb) + kLog2e * gumbel(word);
+  if (st.sb > 0.f) score = st.ref + __log2f(st.sb) + g2;
   st.s += static_cast<double>(st.sb);
   st.w += static_cast<double>(st.wb);
   st.sb = 0.f;
@@ -670,20 +618,52 @@ __device__ __forceinline__ RowPartial wave_partial(const LaneState& st, const Wa
   return p;
 }
 
-// Reduces the kBB batches of a full block in ring slot H; returns the lane's
-// maximum over them.
-template <bool kBf16, int NB, int H>
-__device__ __forceinline__ float reduce_block(const Ring<kBf16, NB>& buf, int64_t base, int32_t vocab, float c,
+// Reduces the batches of a full block in ring slot H into the lane state and
+// returns the lane's maximum over them. The exponentials use the reference of
+// the blocks before (it lags the running maximum), so each stripe is reduced
+// as soon as its load lands instead of after a block-wide maximum; the block
+// maximum is folded in afterwards. A lag of up to 2^64 cannot overflow fp32.
+// One wave-uniform test per block catches the rare block that needs more: a
+// lane's first finite logits, -inf logits (2^t = 0 but t*2^t = NaN), a
+// maximum beyond the lag bound (the block is reduced again on the slow path,
+// batch by batch) or above the reference's slack (the sums are rescaled).
+template <bool kBf16, int NB, int H, int R>
+__device__ __forceinline__ float reduce_block(const Ring<kBf16, NB, R>& buf, int64_t base, int32_t vocab, float c,
                                               LaneState& st, int lane) {
-  float bmax = kNegInf;
+  constexpr float kMaxLag = 64.0f;
+  float bs = 0.f, bw = 0.f, bmax = kNegInf;
 #pragma unroll
-  for (int t = 0; t < kChunkStripes / NB; ++t)
-    bmax = max_raw(bmax, fast_batch<kBf16, NB>(buf[H][t], base + t * NB * kStripeIds + lane * kSlotIds, vocab, c, st));
+  for (int t = 0; t < kChunkStripes / NB; ++t) {
+    float s, w;
+    bmax = max_raw(bmax, chunked_sums<kBf16, NB>(buf[H][t], c, st.ref, s, w));
+    bs += s;
+    bw += w;
+    // one batch's temporaries at a time: the scheduler may not interleave
+    // the batches (their exponentials would not fit the registers together)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float bref = __fmul_rn(bmax, c);
+  const bool bad = !(bw == bw) || !(bref <= st.ref + kMaxLag);  // NaN, fresh lane, or a big jump
+  const bool lift = bref > st.ref + kRefSlack;
+  if (__builtin_amdgcn_ballot_w64(bad || lift) != 0) {
+    if (bad) {
+#pragma unroll
+      for (int t = 0; t < kChunkStripes / NB; ++t)
+        slow_batch<kBf16, NB>(buf[H][t], base + t * NB * kStripeIds + lane * kSlotIds, vocab, c, false, st);
+    } else {
+      st.sb += bs;
+      st.wb += bw;
+    }
+    if (bref > st.ref + kRefSlack) rebase(st, bref);
+  } else {
+    st.sb += bs;
+    st.wb += bw;
+  }
   return bmax;
 }
 
-template <bool kBf16, int NB, int H>
-__device__ __forceinline__ void load_block(Ring<kBf16, NB>& buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte0,
+template <bool kBf16, int NB, int H, int R>
+__device__ __forceinline__ void load_block(Ring<kBf16, NB, R>& buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte0,
                                            bool live) {
 #pragma unroll
   for (int t = 0; t < kChunkStripes / NB; ++t)
@@ -702,24 +682,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const StatsArgs& a, i
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), 0, ((a.vocab * kEB + 15) / 16) * 16, 0x00020000);
 }
 
+// A read-only input read through the constant address space: a scalar load,
+// which waits on its own counter instead of behind the logits' vector loads
+// in flight (the kernel never writes these arrays).
+template <typename T>
+__device__ __forceinline__ T read_only(const T* p, int32_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 __device__ __forceinline__ RowConsts row_consts(const StatsArgs& a, int32_t r) {
   const int32_t canvas = r / a.canvas_len;
   RowConsts rc;
   rc.pos = r % a.canvas_len;
-  rc.step = a.steps != nullptr ? a.steps[canvas] : a.step;
-  const float temp = a.temperature[canvas];
+  rc.step = a.steps != nullptr ? read_only(a.steps, canvas) : a.step;
+  const float temp = read_only(a.temperature, canvas);
   rc.c = kLog2e / temp;
   rc.inv_t = 1.0f / temp;
-  const uint64_t seed = a.seeds[canvas];
+  const uint64_t seed = read_only(a.seeds, canvas);
   rc.k0 = static_cast<uint32_t>(seed);
   rc.k1 = static_cast<uint32_t>(seed >> 32);
   return rc;
 }
 
 // One workgroup per row (or per split of a row). NB stripes per batch; the
-// register ring holds two blocks (one in flight while the other is reduced;
-// deeper rings measured slower).
-template <bool kBf16, int NB>
+// register ring holds RING blocks (one is reduced while the others are in
+// flight). Wave w streams chunks c_begin + w + 8i, so the workgroup reads one
+// stretch of eight consecutive chunks at a time, and draws the Gumbels of its
+// own blocks as it goes (no barrier before the stream starts).
+template <bool kBf16, int NB, int RING>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
   constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
@@ -742,28 +732,16 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const __amdgpu_buffer_rsrc_t rsrc = row_rsrc<kBf16>(a, r);
   const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
 
-  // The split's chunks [c_begin, c_end), split at multiples of 32 chunks so
-  // that the block draws' groups of four stay within a split. Waves w and
-  // w + 4 share a SIMD, and the SIMD's arbiter favours the older one (w < 4):
-  // with equal shares the younger wave streams on alone for the last few
-  // microseconds. So the pair's chunks c_begin + p + 4k (p = w mod 4) are
-  // split unevenly: the older wave takes k < npair - n_young, the younger
-  // one the rest. Each wave visits its chunks in increasing order (block i is
-  // k = k0 + i); only the row's last chunk can be partial, and it is the last
-  // block of the wave that holds it.
+  // The split's chunks [c_begin, c_end), cut at multiples of 32 chunks. Wave
+  // w takes chunks c_begin + w + 8i in increasing order; only the row's last
+  // chunk can be partial, and it is the last block of the wave that holds it.
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
   const int32_t ngroup = (nchunk + kDrawGroupChunks - 1) / kDrawGroupChunks;
   const int32_t c_begin = static_cast<int32_t>((static_cast<int64_t>(split) * ngroup) / a.nsplit) * kDrawGroupChunks;
   const int32_t c_end = min(static_cast<int32_t>((static_cast<int64_t>(split + 1) * ngroup) / a.nsplit) *
                             kDrawGroupChunks, nchunk);
-  const int pair = wave & 3;
-  const bool young = wave >= 4;
-  const int32_t npair = c_end - c_begin > pair ? (c_end - c_begin - pair + 3) / 4 : 0;
-  const int32_t n_young = min(npair / 2, (npair * kYoungShare16 + 8) / 16);
-  const int32_t nblk = young ? n_young : npair - n_young;
-  const int32_t k0 = young ? npair - n_young : 0;
-  auto k_of = [&](int32_t i) { return k0 + i; };
-  auto chunk_of = [&](int32_t i) { return c_begin + pair + 4 * k_of(i); };
+  const int32_t nblk = c_end - c_begin > wave ? (c_end - c_begin - wave + kWaves - 1) / kWaves : 0;
+  auto chunk_of = [&](int32_t i) { return c_begin + wave + kWaves * i; };
   auto base_of = [&](int32_t i) { return static_cast<int64_t>(chunk_of(i)) * kChunkIds; };
   // Block i's byte offset for this lane; batches wholly past V point beyond
   // the resource, where buffer loads return zero without touching memory, so
@@ -777,10 +755,10 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const int32_t nblk_full =
       (nblk > 0 && base_of(nblk - 1) + kChunkIds > vocab) ? nblk - 1 : nblk;
 
-  // The ring: blocks 0 and 1 go out before the per-canvas scalars are read.
-  Ring<kBf16, NB> buf;
+  // The ring: its first blocks go out before the per-canvas scalars are read.
+  Ring<kBf16, NB, RING> buf;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < RING; ++h)
 #pragma unroll
     for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[h][t], rsrc, batch_byte(h, t));
 
@@ -788,30 +766,42 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const RowConsts rc = row_consts(a, r);
   LaneState st;
   WaveResult wr;
-  PairWords bw;
+  WaveGumbels gw;
 
-  // Full blocks: reduce, close, and refill the ring slot with block i + 2.
+  // Full blocks: reduce, close, and refill the ring slot with block i + RING.
   auto run_block = [&](auto slot, int32_t i) {
     constexpr int H = decltype(slot)::value;
     const float bmax = reduce_block<kBf16, NB, H>(buf, base_of(i), vocab, rc.c, st, lane);
-    close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, k_of(i), bmax, vocab, rc, st, wr, bw,
-                              s_blk[wave], s_amx[wave], lane);
+    const float g2 = gw.take(i, chunk_of(i), lane, rc);
+    close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, g2, st, wr, s_blk[wave],
+                              s_amx[wave], lane);
 #pragma unroll
-    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[H][t], rsrc, batch_byte(i + 2, t));
+    for (int t = 0; t < kBB; ++t) load_batch<kBf16, NB>(buf[H][t], rsrc, batch_byte(i + RING, t));
   };
-  for (int32_t i0 = 0; i0 < nblk_full; i0 += 2) {
-    run_block(std::integral_constant<int, 0>{}, i0);
-    if (i0 + 1 < nblk_full) run_block(std::integral_constant<int, 1>{}, i0 + 1);
+  // block i waits in ring slot i % RING; the loop takes the slots in turn, so
+  // that every way into it leaves their loads in the same order and each
+  // block waits for its own loads only; a last odd block follows it
+  int32_t i = 0;
+  if constexpr (RING == 1) {
+    for (; i < nblk_full; ++i) run_block(std::integral_constant<int, 0>{}, i);
+  } else {
+    for (; i + 1 < nblk_full; i += 2) {
+      run_block(std::integral_constant<int, 0>{}, i);
+      run_block(std::integral_constant<int, 1>{}, i + 1);
+    }
+    if (i < nblk_full) {
+      run_block(std::integral_constant<int, 0>{}, i);
+      ++i;
+    }
   }
   if (nblk_full < nblk) {
-    // the block holding V sits in ring slot nblk_full % 2 (moved to slot 0);
+    // the block holding V sits in ring slot i % RING (moved to slot 0);
     // batches below V are reduced with ids past V masked, the rest skipped
-    const int32_t i = nblk_full;
-    if (i & 1) {
+    if (RING > 1 && (i & 1)) {
 #pragma unroll
       for (int t = 0; t < kBB; ++t)
 #pragma unroll
-        for (int q = 0; q < NB * LPS; ++q) buf[0][t][q] = buf[1][t][q];
+        for (int q = 0; q < NB * LPS; ++q) buf[0][t][q] = buf[RING - 1][t][q];
     }
     float bmax = kNegInf;
 #pragma unroll
@@ -819,8 +809,9 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
       const int64_t f = base_of(i) + t * NB * kStripeIds;
       if (f < vocab) bmax = fmaxf(bmax, tail_batch<kBf16, NB>(buf[0][t], f + lane * kSlotIds, vocab, rc.c, st));
     }
-    close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, k_of(i), bmax, vocab, rc, st, wr, bw,
-                              s_blk[wave], s_amx[wave], lane);
+    const float g2 = gw.take(i, chunk_of(i), lane, rc);
+    close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, g2, st, wr, s_blk[wave],
+                              s_amx[wave], lane);
   }
 
   const RowPartial wp = wave_partial<kBf16>(st, wr, vocab, rc, s_blk[wave], s_amx[wave], lane);
@@ -848,16 +839,20 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
 
 // Row loop: a persistent grid of workgroups, workgroup b taking rows b,
 // b + grid, ... (V a multiple of 4096, one workgroup per row, no active
-// mask). Each wave's blocks of all its rows form one sequence g = 0, 1, ...;
-// the ring refills slot g % 2 with block g + 2 even when that block belongs
-// to the next row, so a row's finish and merge overlap the next row's loads.
-template <bool kBf16, int NB>
+// mask). Wave w streams chunks w, w + 8, ... of each row, and its blocks of
+// all its rows form one sequence g = 0, 1, ...; the ring refills slot g % 2
+// with block g + 2 even when that block belongs to the next row, so a row's
+// finish and merge overlap the next row's loads. The block Gumbels of each
+// segment of 64 chunks are drawn into one of two LDS tables by the waves that
+// have finished the segment before, in the barrier that ends it.
+template <bool kBf16, int NB, bool kSeg, bool kPairs, int RING>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
   constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
   __shared__ RowPartial s_part[2][kWaves];  // by row parity
   __shared__ __align__(16) uint4 s_blk[kWaves][kChunkStripes * LPS];
   __shared__ __align__(16) uint4 s_amx[kWaves][kChunkStripes * LPS];
+  __shared__ float s_g2[2][kSegBlocks];     // by segment parity
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -868,12 +863,13 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
   const int32_t first_row = static_cast<int32_t>(blockIdx.x);
   const int32_t my_rows = (a.rows - first_row + grid - 1) / grid;  // >= 1
   const int32_t nchunk = vocab / kChunkIds;
-  const int32_t nblk = nchunk > wave ? (nchunk - wave + kWaves - 1) / kWaves : 0;  // per row
+  auto blocks_below = [&](int32_t c) { return c > wave ? (c - wave + kWaves - 1) / kWaves : 0; };
+  const int32_t nblk = blocks_below(nchunk);  // per row
   const int64_t total = static_cast<int64_t>(my_rows) * nblk;
 
   // Block g of the wave's sequence is block g % nblk (chunk wave + 8 (g % nblk))
   // of row first_row + (g / nblk) * grid; past the sequence, loads read nothing.
-  Ring<kBf16, NB> buf;
+  Ring<kBf16, NB, RING> buf;
   auto fetch = [&](auto slot, int64_t g) {
     constexpr int H = decltype(slot)::value;
     int32_t r = first_row;
@@ -886,32 +882,83 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
     load_block<kBf16, NB, H>(buf, row_rsrc<kBf16>(a, r), byte0, live);
   };
   fetch(std::integral_constant<int, 0>{}, 0);
-  fetch(std::integral_constant<int, 1>{}, 1);
+  if constexpr (RING > 1) fetch(std::integral_constant<int, RING - 1>{}, 1);
 
+  RowConsts rc = row_consts(a, first_row);
+  fill_gumbels(s_g2[0], 0, 0, min(nchunk, kSegChunks), rc, tid);
+  __syncthreads();
+  int tp = 0;  // table in use
   int64_t g = 0;
   for (int32_t k = 0; k < my_rows; ++k) {
     const int32_t r = first_row + k * grid;
-    const RowConsts rc = row_consts(a, r);
     LaneState st;
     WaveResult wr;
-    ShiftWords bw;
-    auto run_block = [&](auto slot, int32_t i) {
+    const RowConsts rc_next = k + 1 < my_rows ? row_consts(a, r + grid) : rc;
+    // block i of the row, block gi of the wave's sequence, in ring slot gi % 2
+    auto run_block = [&](auto slot, int32_t i, int64_t gi, int32_t seg0) {
       constexpr int H = decltype(slot)::value;
-      const int64_t base = static_cast<int64_t>(wave + kWaves * i) * kChunkIds;
+      const int32_t chunk = wave + kWaves * i;
+      const float gv = s_g2[tp][(chunk - seg0) * kSlots + lane];
+      const int64_t base = static_cast<int64_t>(chunk) * kChunkIds;
       const float bmax = reduce_block<kBf16, NB, H>(buf, base, vocab, rc.c, st, lane);
-      close_block<kBf16, NB, H>(buf, base, (wave + kWaves * i) * kSlots + lane, i, bmax, vocab, rc, st, wr, bw,
-                                s_blk[wave], s_amx[wave], lane);
-      fetch(slot, g + 2);
+      close_block<kBf16, NB, H>(buf, base, chunk * kSlots + lane, bmax, gv, st, wr, s_blk[wave], s_amx[wave], lane);
+      fetch(slot, gi + RING);
     };
-    for (int32_t i = 0; i < nblk; ++i, ++g) {
-      if ((g & 1) == 0)
-        run_block(std::integral_constant<int, 0>{}, i);
-      else
-        run_block(std::integral_constant<int, 1>{}, i);
+    // the end of a segment: the next segment's Gumbels (this row's next, or
+    // the next row's first) go into the other table, and at the row's end
+    // the wave's partial into s_part, both published by the barrier
+    auto end_segment = [&](int32_t seg_end) {
+      const bool last_seg = seg_end >= nchunk;
+      if (!last_seg)
+        fill_gumbels(s_g2[tp ^ 1], seg_end, seg_end, min(nchunk, seg_end + kSegChunks), rc, tid);
+      else if (k + 1 < my_rows)
+        fill_gumbels(s_g2[tp ^ 1], 0, 0, min(nchunk, kSegChunks), rc_next, tid);
+      if (last_seg) {
+        const RowPartial wp = wave_partial<kBf16>(st, wr, vocab, rc, s_blk[wave], s_amx[wave], lane);
+        if (lane == 0) s_part[k & 1][wave] = wp;
+      }
+      __syncthreads();
+      tp ^= 1;
+    };
+    if constexpr (RING == 1) {
+      // one block in flight per wave, always in the ring's only slot
+      for (int32_t seg0 = 0; seg0 < nchunk; seg0 += kSegChunks) {
+        const int32_t seg_end = min(nchunk, seg0 + kSegChunks);
+        for (int32_t i = blocks_below(seg0); i < blocks_below(seg_end); ++i, ++g)
+          run_block(std::integral_constant<int, 0>{}, i, g, seg0);
+        end_segment(seg_end);
+      }
+    } else if constexpr (kPairs) {
+      // one segment per row and an even number of blocks per wave (chunks a
+      // multiple of 16): every row starts in slot 0, and a loop over pairs
+      // keeps the two slots' loads in order, so that each block waits for
+      // its own loads alone
+      for (int32_t i = 0; i < nblk; i += 2, g += 2) {
+        run_block(std::integral_constant<int, 0>{}, i, g, 0);
+        run_block(std::integral_constant<int, RING - 1>{}, i + 1, g + 1, 0);
+      }
+      end_segment(nchunk);
+    } else if constexpr (!kSeg) {
+      // one segment per row (rows of up to 262144 ids)
+      for (int32_t i = 0; i < nblk; ++i, ++g) {
+        if ((g & 1) == 0)
+          run_block(std::integral_constant<int, 0>{}, i, g, 0);
+        else
+          run_block(std::integral_constant<int, RING - 1>{}, i, g, 0);
+      }
+      end_segment(nchunk);
+    } else {
+      for (int32_t seg0 = 0; seg0 < nchunk; seg0 += kSegChunks) {
+        const int32_t seg_end = min(nchunk, seg0 + kSegChunks);
+        for (int32_t i = blocks_below(seg0); i < blocks_below(seg_end); ++i, ++g) {
+          if ((g & 1) == 0)
+            run_block(std::integral_constant<int, 0>{}, i, g, seg0);
+          else
+            run_block(std::integral_constant<int, RING - 1>{}, i, g, seg0);
+        }
+        end_segment(seg_end);
+      }
     }
-    const RowPartial wp = wave_partial<kBf16>(st, wr, vocab, rc, s_blk[wave], s_amx[wave], lane);
-    if (lane == 0) s_part[k & 1][wave] = wp;
-    __syncthreads();
     // the merge of row k falls to wave k mod 8; the other waves go on. The
     // partials are double-buffered by row parity: row k + 2 writes them only
     // after the barrier of row k + 1, which the merging wave reaches after
@@ -920,6 +967,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
       const RowPartial p = merge_waves(s_part[k & 1], lane);
       if (lane == 0) row_output(a, r, p);
     }
+    rc = rc_next;
   }
 }
 
@@ -952,19 +1000,32 @@ int32_t stats_row_grid(int32_t rows, int32_t vocab, int32_t nsplit, bool has_act
 
 hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream) {
   const dim3 block(kStatsThreads);
+  // rows of more than one segment (64 chunks, 262144 ids) take the kernels'
+  // segment loops; shorter rows the plain ones
+  const int32_t nchunk = (a.vocab + kChunkIds - 1) / kChunkIds;
+  const bool seg = nchunk > kSegChunks;
   if (a.row_grid > 0) {
     const dim3 grid(static_cast<unsigned>(a.row_grid));
+    const bool pairs = kRowsRing == 2 && !seg && nchunk % 16 == 0;
+#define DG_ROWS(BF, SEG, PAIRS) \
+  hipLaunchKernelGGL((canvas_stats_rows_kernel<BF, 4, SEG, PAIRS, kRowsRing>), grid, block, 0, stream, a)
+    if (bf16) {
+      if (pairs) DG_ROWS(true, false, true);
+      else if (seg) DG_ROWS(true, true, false);
+      else DG_ROWS(true, false, false);
+    } else {
+      if (pairs) DG_ROWS(false, false, true);
+      else if (seg) DG_ROWS(false, true, false);
+      else DG_ROWS(false, false, false);
+    }
+#undef DG_ROWS
+  } else {
+    const dim3 grid(static_cast<unsigned>(a.rows) * static_cast<unsigned>(a.nsplit));
     if (bf16)
-      hipLaunchKernelGGL((canvas_stats_rows_kernel<true, 4>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((canvas_stats_kernel<true, 4, kRowRing<true>>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((canvas_stats_rows_kernel<false, 4>), grid, block, 0, stream, a);
-    return hipGetLastError();
+      hipLaunchKernelGGL((canvas_stats_kernel<false, 4, kRowRing<false>>), grid, block, 0, stream, a);
   }
-  const dim3 grid(static_cast<unsigned>(a.rows) * static_cast<unsigned>(a.nsplit));
-  if (bf16)
-    hipLaunchKernelGGL((canvas_stats_kernel<true, 4>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((canvas_stats_kernel<false, 4>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
