@@ -505,17 +505,20 @@ def selfcond_leg(torch, B, synth, k=200, d=30):
 def lmhead_leg(args, torch, B, synth, keep=None):
     """The 64-canvas step whose logits come from the LM head: hidden bf16
     [16384, 2048] ~ N(0,1), weight bf16 [2048, 262144] ~ N(0, 1/2048), canvas c
-    at step c mod 48 of the default schedule, seed c."""
+    at step c mod 48 of the default schedule, seed c. Timed: the fused step
+    (product with the statistics epilogue, merge of the tile partials,
+    acceptance; the logits never stored) and, for comparison, the product
+    alone with its 16 GiB of fp32 logits stored."""
     L, K, V, Bn = 256, 2048, 262144, 64
     params = B.params_default(canvas_len=L, vocab=V)
     ctx = B.Context(params, max_batch=Bn)
     hidden, weight = synth.lmhead_operands(1005, Bn * L, K, V, device="cuda")
-    logits = torch.empty(Bn * L, V, device="cuda")
     steps = torch.tensor([c % 48 for c in range(Bn)], dtype=torch.int32, device="cuda")
     temps = torch.tensor([B.dg_temperature(params, c % 48) for c in range(Bn)], device="cuda")
     seeds = torch.arange(Bn, dtype=torch.int64, device="cuda")
     canvas = torch.empty(Bn * L, dtype=torch.int32, device="cuda")
     out = ctx.step_out(canvas)
+    ws = torch.empty(ctx.dg_lmhead_workspace_bytes(Bn), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.Stream()
     # the inputs were made on the default stream: let that work finish (and
     # its freed temporaries stop being in use) before launching on `stream`
@@ -535,53 +538,39 @@ def lmhead_leg(args, torch, B, synth, keep=None):
             torch.cuda.synchronize()
         return start.elapsed_time(stop) / 1e3 / k
 
-    gemm_s = timed(lambda: ctx.dg_lmhead_logits(hidden, weight, logits))
-    step_s = timed(lambda: ctx.dg_lmhead_sampler_step(hidden, weight, logits, temps, 0, seeds, out,
-                                                      steps=steps))
+    step_s = timed(lambda: ctx.dg_lmhead_sampler_step(hidden, weight, ws, temps, 0, seeds, out, steps=steps))
+    gemm_s = None
+    if not args.lmhead_no_store:
+        logits = torch.empty(Bn * L, V, device="cuda")
+        gemm_s = timed(lambda: ctx.dg_lmhead_logits(hidden, weight, logits))
+        del logits
+        torch.cuda.synchronize()
     flops = 2.0 * Bn * L * V * K
-    tflops = flops / gemm_s / 1e12
+    tflops = flops / step_s / 1e12
     if keep is not None:
-        # canvas 0 (step 0, T 0.8, seed 0) once more with every output, for the
-        # oracle comparison of the CPU-baseline leg
+        # canvas 0 (step 0, T 0.8, seed 0) once more with every output, and its
+        # rows of the product, for the oracle comparison of the CPU-baseline leg
         bufs = _step_buffers(torch, Bn, L)
-        ctx.dg_lmhead_sampler_step(hidden, weight, logits, temps, 0, seeds, ctx.step_out(**bufs), steps=steps)
+        ctx.dg_lmhead_sampler_step(hidden, weight, ws, temps, 0, seeds, ctx.step_out(**bufs), steps=steps)
+        z0 = torch.empty(L, V, device="cuda")
+        ctx.dg_lmhead_logits(hidden[:L], weight, z0)
         torch.cuda.synchronize()
         keep.update(hidden=hidden[:L].to(torch.float32).cpu().numpy(),
-                    weight=weight.to(torch.float32).cpu().numpy(), logits=logits[:L].cpu().numpy(),
+                    weight=weight.to(torch.float32).cpu().numpy(), logits=z0.cpu().numpy(),
                     gpu=_host_outputs(bufs, 1, L)[0], temp=float(temps[0].item()), step=0, seed=0)
     ctx.close()
-    return {"workload": "64 canvases x 256 positions, LM head bf16 [16384,2048] x [2048,262144] "
-                        "-> fp32 logits -> statistics -> acceptance; per-canvas steps c mod 48",
-            "gemm_kernel": "lmhead_gemm_kernel", "gemm_ms": gemm_s * 1e3, "gemm_tflops": tflops,
-            "mfma_peak_tflops": PEAK_BF16_TFLOPS, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
-            "flops_per_launch": flops, "step_ms": step_s * 1e3,
-            "stats_and_accept_ms": (step_s - gemm_s) * 1e3,
-            "positions_per_s": Bn * L / step_s, "steps_per_s": 1.0 / step_s, "timed_launches": k}
-
-
-def _step_buffers(torch, n, L):
-    """Device buffers for every output of one step of n canvases."""
-    dev = "cuda"
-    return dict(canvas_out=torch.empty(n * L, dtype=torch.int32, device=dev),
-                argmax_out=torch.empty(n * L, dtype=torch.int32, device=dev),
-                sample_out=torch.empty(n * L, dtype=torch.int32, device=dev),
-                accept_out=torch.empty(n * L, dtype=torch.uint8, device=dev),
-                entropy_out=torch.empty(n * L, device=dev),
-                n_accept_out=torch.empty(n, dtype=torch.int32, device=dev),
-                mean_entropy_out=torch.empty(n, device=dev),
-                stop_out=torch.empty(n, dtype=torch.uint8, device=dev))
-
-
-def _host_outputs(bufs, n, L):
-    """Per-canvas host dicts of one step's outputs."""
-    g = {k: v.cpu().numpy() for k, v in bufs.items()}
-    out = []
-    for c in range(n):
-        sl = slice(c * L, (c + 1) * L)
-        out.append(dict(entropy=g["entropy_out"][sl], argmax=g["argmax_out"][sl], sample=g["sample_out"][sl],
-                        accept=g["accept_out"][sl], n_accept=g["n_accept_out"][c], canvas=g["canvas_out"][sl],
-                        mean_entropy=g["mean_entropy_out"][c], stop=g["stop_out"][c]))
-    return out
+    rec = {"workload": "64 canvases x 256 positions, LM head bf16 [16384,2048] x [2048,262144] "
+                       "with the statistics in the product's epilogue (logits never stored) -> "
+                       "merge of the tile partials -> acceptance; per-canvas steps c mod 48",
+           "fused_kernel": "lmhead_gemm_kernel<statistics epilogue>", "step_ms": step_s * 1e3,
+           "step_tflops": tflops, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
+           "step_mfma_frac": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
+           "workspace_bytes": int(ws.numel()),
+           "positions_per_s": Bn * L / step_s, "steps_per_s": 1.0 / step_s, "timed_launches": k}
+    if gemm_s is not None:
+        rec.update(store_gemm_ms=gemm_s * 1e3, store_gemm_tflops=flops / gemm_s / 1e12,
+                   store_gemm_note="the same product alone, its 16 GiB of fp32 logits stored")
+    return rec
 
 
 def cpu_baseline_leg(torch, B, synth, c2, c5):
@@ -696,16 +685,21 @@ def cpu_baseline_leg(torch, B, synth, c2, c5):
         prev_o = o["argmax"]
     parity["C4"] = tally.record()
 
-    # C5: canvas 0 of the LM-head step against the exact products
+    # C5: canvas 0 of the fused LM-head step; the oracle runs on the product's
+    # own fp32 logits (the fused kernel's input bit for bit), whose distance
+    # from the exact fp64 products is reported beside it
     if c5:
         tally = Tally("C5")
         from oracle import lmhead as OL
         exact = OL.logits(c5["hidden"], c5["weight"])
-        err = np.abs(c5["logits"].astype(np.float64) - exact).max(axis=1)
-        o = OPAR.steps([job(exact, exact.shape[1], c5["temp"], c5["seed"], c5["step"])], threads=threads)[0]
-        compare(tally, c5["gpu"], o, "C5 canvas 0", logit_err=err, z=exact, temp=np.float32(c5["temp"]))
+        z0 = c5["logits"].astype(np.float64)
+        err = np.abs(z0 - exact).max(axis=1)
+        del exact
+        o = OPAR.steps([job(z0, z0.shape[1], c5["temp"], c5["seed"], c5["step"])], threads=threads)[0]
+        compare(tally, c5["gpu"], o, "C5 canvas 0")
         parity["C5"] = dict(tally.record(), max_logit_error=float(err.max()),
-                            note="canvas 0 of 64 (step 0, T 0.8); oracle logits are exact fp64 products")
+                            note="canvas 0 of 64 (step 0, T 0.8); oracle on the product's fp32 logits, "
+                                 "max_logit_error against the exact fp64 products")
     for rec in parity.values():
         rec["match"] = not any(c.startswith("MISMATCH") for c in rec["clauses"])
     return cpu, parity
@@ -730,6 +724,8 @@ def main():
     ap.add_argument("--lmhead-only", action="store_true",
                     help="only run the LM-head product and step (for counter runs)")
     ap.add_argument("--lmhead-steps", type=int, default=10)
+    ap.add_argument("--lmhead-no-store", action="store_true",
+                    help="skip timing the product alone with its logits stored")
     ap.add_argument("--cpu-full", action="store_true",
                     help="only time the oracle on the host for C1-C4 single steps, the full C2 run "
                          "and C3 over processes (a few minutes; no GPU work)")

@@ -30,7 +30,8 @@ EXPORTS = ["dg_params_default", "dg_params_check", "dg_create", "dg_destroy", "d
            "dg_canvas_stats", "dg_accept_renoise", "dg_sampler_step", "dg_run_canvas",
            "dg_run_canvas_resident", "dg_generate", "dg_tokens_per_forward",
            "dg_self_condition", "dg_sampler_step_selfcond",
-           "dg_lmhead_logits", "dg_lmhead_sampler_step", "dg_sampler_step_noalloc", "dg_version"]
+           "dg_lmhead_logits", "dg_lmhead_workspace_bytes", "dg_lmhead_sampler_step",
+           "dg_sampler_step_noalloc", "dg_version"]
 
 
 class DgParams(ctypes.Structure):
@@ -96,7 +97,8 @@ def lib():
             "dg_sampler_step_selfcond": [vp, i32, vp, ctypes.c_int, i64, vp, i32, vp, vp, vp, vp, i32, vp,
                                          ctypes.POINTER(DgStepOut), vp],
             "dg_lmhead_logits": [vp, i32, vp, vp, i32, vp, i64, vp],
-            "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp,
+            "dg_lmhead_workspace_bytes": [vp, i32, ctypes.POINTER(ctypes.c_int64)],
+            "dg_lmhead_sampler_step": [vp, i32, vp, vp, i32, vp, i64, vp, i32, vp, vp, vp, vp,
                                        ctypes.POINTER(DgStepOut), vp],
             "dg_sampler_step_noalloc": [ctypes.POINTER(DgParams), i32, vp, ctypes.c_int, i64, vp, i32, vp, vp,
                                         vp, ctypes.POINTER(DgStepOut), vp],
@@ -254,13 +256,24 @@ class Context:
         self._chk(lib().dg_lmhead_logits(self.handle, rows, _ptr(hidden), _ptr(weight), k,
                                          _ptr(logits), logits.stride(0), _stream(stream)))
 
-    def dg_lmhead_sampler_step(self, hidden, weight, logits, temperature, step, seeds, out,
-                               steps=None, prev_argmax=None, active=None, stream=None):
+    def dg_lmhead_workspace_bytes(self, B):
+        """Bytes of device workspace dg_lmhead_sampler_step needs for B canvases."""
+        n = ctypes.c_int64()
+        self._chk(lib().dg_lmhead_workspace_bytes(self.handle, B, ctypes.byref(n)))
+        return n.value
+
+    def dg_lmhead_sampler_step(self, hidden, weight, workspace, temperature, step, seeds, out,
+                               steps=None, prev_argmax=None, active=None, stream=None,
+                               workspace_bytes=None):
+        """workspace: a device tensor of at least dg_lmhead_workspace_bytes(B) bytes."""
         B = seeds.shape[0]
+        nbytes = workspace_bytes if workspace_bytes is not None else \
+            workspace.numel() * workspace.element_size()
         self._chk(lib().dg_lmhead_sampler_step(self.handle, B, _ptr(hidden), _ptr(weight),
-                                               hidden.shape[1], _ptr(logits), _ptr(temperature),
-                                               step, _ptr(steps), _ptr(seeds), _ptr(prev_argmax),
-                                               _ptr(active), ctypes.byref(out), _stream(stream)))
+                                               hidden.shape[1], _ptr(workspace), nbytes,
+                                               _ptr(temperature), step, _ptr(steps), _ptr(seeds),
+                                               _ptr(prev_argmax), _ptr(active), ctypes.byref(out),
+                                               _stream(stream)))
 
     def dg_run_canvas(self, seeds, denoise, logits_scratch, final_argmax, stream=None):
         """seeds: list of ints (host). denoise(step, canvas_ptr, active_ptr, logits, stream)

@@ -37,7 +37,7 @@
 // a new wave maximum, that lane parks the block's 64 logits in LDS, and after
 // its stream the wave draws the sample in its best block and finds the first
 // id of its maximum from the parked logits. The workgroup then merges eight
-// 32-byte partials. A row split over several workgroups (for very short
+// 40-byte partials. A row split over several workgroups (for very short
 // batches) is merged by the last workgroup to finish (atomic ticket,
 // release/acquire at agent scope).
 #include <type_traits>
@@ -971,7 +971,80 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
   }
 }
 
+// Merges the partials of the 64 lanes of a wave (lane l holds the merge of
+// its share of a row's partials): a butterfly over the maxima and best-block
+// keys, then the sums rescaled once to the largest reference and added.
+// Every lane returns the result.
+__device__ __forceinline__ RowPartial merge_lanes(const RowPartial& q) {
+  uint64_t km = argmax_key(q.m, q.argmax);
+  uint64_t kb = argmax_key(q.best, q.bestj);
+  int32_t sample = q.sample;
+  float r = q.ref;
+#define DG_MERGE_STEP(J)                                                               \
+  {                                                                                    \
+    km = max_u64(km, lane_xor64<J>(km));                                               \
+    const uint64_t ob = lane_xor64<J>(kb);                                             \
+    const int32_t os = static_cast<int32_t>(lane_xor<J>(static_cast<uint32_t>(sample))); \
+    const bool take = ob > kb;                                                         \
+    kb = take ? ob : kb;                                                               \
+    sample = take ? os : sample;                                                       \
+    r = max_raw(r, f32_of(lane_xor<J>(u32_of(r))));                                    \
+  }
+  DG_MERGE_STEP(32) DG_MERGE_STEP(16) DG_MERGE_STEP(8) DG_MERGE_STEP(4) DG_MERGE_STEP(2) DG_MERGE_STEP(1)
+#undef DG_MERGE_STEP
+  double s = 0.0, w = 0.0;
+  if (q.ref != kNegInf) {
+    const double d = static_cast<double>(q.ref) - static_cast<double>(r);
+    const double f = scale_of(d);
+    s = f * q.s;
+    w = f * (q.w + d * q.s);
+  }
+  RowPartial p;
+  argmax_unkey(km, p.m, p.argmax);
+  argmax_unkey(kb, p.best, p.bestj);
+  p.sample = sample;
+  p.ref = r;
+  p.s = wave_sum(s);
+  p.w = wave_sum(w);
+  return p;
+}
+
+constexpr int kMergeThreads = 256;
+
+// One wave per row: lane l merges the row's partials l, l + 64, ... in order,
+// then the wave merges its lanes and lane 0 writes the row's outputs. Rows of
+// inactive canvases are skipped (their outputs are not written).
+__global__ __launch_bounds__(kMergeThreads) void partials_merge_kernel(StatsArgs a, const RowPartial* parts,
+                                                                       int32_t nparts) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t r = static_cast<int32_t>(blockIdx.x) * (kMergeThreads / kWave) +
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  if (r >= a.rows) return;
+  if (a.active != nullptr && !active_flag(a.active, r / a.canvas_len)) return;
+  const RowPartial* row = parts + static_cast<int64_t>(r) * nparts;
+  RowPartial p;
+  p.s = 0.0;
+  p.w = 0.0;
+  p.ref = kNegInf;
+  p.m = kNegInf;
+  p.argmax = 0x7FFFFFFF;
+  p.best = kNegInf;
+  p.bestj = 0x7FFFFFFF;
+  p.sample = 0x7FFFFFFF;
+  for (int32_t t = lane; t < nparts; t += kWave) merge_partial(p, row[t]);
+  p = merge_lanes(p);
+  if (lane == 0) row_output(a, r, p);
+}
+
 }  // namespace
+
+hipError_t launch_partials_merge(const StatsArgs& a, const RowPartial* partials, int32_t nparts,
+                                 hipStream_t stream) {
+  constexpr int kRowsPerBlock = kMergeThreads / kWave;
+  const dim3 grid(static_cast<unsigned>((a.rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL(partials_merge_kernel, grid, dim3(kMergeThreads), 0, stream, a, partials, nparts);
+  return hipGetLastError();
+}
 
 int32_t choose_nsplit(int32_t rows, int32_t vocab) {
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;

@@ -271,25 +271,18 @@ dg_status enqueue_step(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtyp
 // Operands of the LM-head product are read through 32-bit buffer offsets.
 constexpr int64_t kMaxOperandBytes = 0x7FFF0000LL;
 
-dg_status check_lmhead(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
-                       int32_t hidden_dim, const float* logits, int64_t ld_logits) {
+// The operands of the product (shared by both LM-head entry points).
+dg_status check_lmhead_operands(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
+                                int32_t hidden_dim) {
   if (!hidden) return set_err(ctx, DG_ERR_INVALID_ARG, "hidden is NULL");
   if (!weight) return set_err(ctx, DG_ERR_INVALID_ARG, "weight is NULL");
-  if (!logits) return set_err(ctx, DG_ERR_INVALID_ARG, "logits is NULL");
   if (hidden_dim < 1) return set_err(ctx, DG_ERR_INVALID_ARG, "hidden_dim = %d must be >= 1", hidden_dim);
-  if (ld_logits < ctx->p.vocab)
-    return set_err(ctx, DG_ERR_INVALID_ARG, "ld_logits = %lld is below vocab (%d)",
-                   static_cast<long long>(ld_logits), ctx->p.vocab);
   if (hidden_dim % 64 != 0)
     return set_err(ctx, DG_ERR_UNSUPPORTED, "hidden_dim = %d must be a multiple of 64", hidden_dim);
   if (ctx->p.vocab % 8 != 0)
     return set_err(ctx, DG_ERR_UNSUPPORTED, "vocab = %d must be a multiple of 8 for the LM head", ctx->p.vocab);
-  if (ld_logits % 4 != 0)
-    return set_err(ctx, DG_ERR_UNSUPPORTED, "ld_logits = %lld must be a multiple of 4",
-                   static_cast<long long>(ld_logits));
-  if ((reinterpret_cast<uintptr_t>(hidden) & 15u) || (reinterpret_cast<uintptr_t>(weight) & 15u) ||
-      (reinterpret_cast<uintptr_t>(logits) & 15u))
-    return set_err(ctx, DG_ERR_UNSUPPORTED, "hidden, weight and logits must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(hidden) & 15u) || (reinterpret_cast<uintptr_t>(weight) & 15u))
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "hidden and weight must be 16-byte aligned");
   if (static_cast<int64_t>(rows) * hidden_dim * 2 > kMaxOperandBytes)
     return set_err(ctx, DG_ERR_UNSUPPORTED, "hidden is too large: rows * hidden_dim * 2 = %lld bytes > %lld",
                    static_cast<long long>(static_cast<int64_t>(rows) * hidden_dim * 2),
@@ -299,6 +292,35 @@ dg_status check_lmhead(dg_ctx* ctx, int32_t rows, const void* hidden, const void
                    static_cast<long long>(static_cast<int64_t>(hidden_dim) * ctx->p.vocab * 2),
                    static_cast<long long>(kMaxOperandBytes));
   return DG_OK;
+}
+
+dg_status check_lmhead(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
+                       int32_t hidden_dim, const float* logits, int64_t ld_logits) {
+  if (!hidden) return set_err(ctx, DG_ERR_INVALID_ARG, "hidden is NULL");
+  if (!weight) return set_err(ctx, DG_ERR_INVALID_ARG, "weight is NULL");
+  if (!logits) return set_err(ctx, DG_ERR_INVALID_ARG, "logits is NULL");
+  if (hidden_dim < 1) return set_err(ctx, DG_ERR_INVALID_ARG, "hidden_dim = %d must be >= 1", hidden_dim);
+  if (ld_logits < ctx->p.vocab)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "ld_logits = %lld is below vocab (%d)",
+                   static_cast<long long>(ld_logits), ctx->p.vocab);
+  const dg_status st = check_lmhead_operands(ctx, rows, hidden, weight, hidden_dim);
+  if (st != DG_OK) return st;
+  if (ld_logits % 4 != 0)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "ld_logits = %lld must be a multiple of 4",
+                   static_cast<long long>(ld_logits));
+  if (reinterpret_cast<uintptr_t>(logits) & 15u)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "logits must be 16-byte aligned");
+  return DG_OK;
+}
+
+// Workspace of the fused LM-head step: one 40-byte partial per (row, tile),
+// then one 32-bit running best score per row.
+int64_t lmhead_partials_bytes(int32_t rows, int32_t vocab) {
+  return static_cast<int64_t>(rows) * dg::lmhead_stats_tiles(vocab) * static_cast<int64_t>(sizeof(dg::RowPartial));
+}
+
+int64_t lmhead_workspace_bytes(int32_t rows, int32_t vocab) {
+  return lmhead_partials_bytes(rows, vocab) + static_cast<int64_t>(rows) * 4;
 }
 
 dg_status enqueue_lmhead(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
@@ -546,16 +568,33 @@ dg_status dg_lmhead_logits(dg_ctx* ctx, int32_t rows, const void* hidden, const 
                         static_cast<hipStream_t>(stream));
 }
 
+dg_status dg_lmhead_workspace_bytes(const dg_ctx* ctx, int32_t B, int64_t* bytes) {
+  if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_ctx* c = const_cast<dg_ctx*>(ctx);
+  const dg_status st = check_batch(c, B);
+  if (st != DG_OK) return st;
+  if (!bytes) return set_err(c, DG_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = lmhead_workspace_bytes(B * ctx->p.canvas_len, ctx->p.vocab);
+  return DG_OK;
+}
+
 dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, const void* weight,
-                                 int32_t hidden_dim, float* logits, const float* temperature,
-                                 int32_t step, const int32_t* steps, const uint64_t* seeds,
-                                 const int32_t* prev_argmax, const uint8_t* active,
+                                 int32_t hidden_dim, void* workspace, int64_t workspace_bytes,
+                                 const float* temperature, int32_t step, const int32_t* steps,
+                                 const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
                                  const dg_step_out* out, void* stream) {
   if (!ctx) return set_err(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   dg_status st = check_batch(ctx, B);
   if (st != DG_OK) return st;
   const int32_t rows = B * ctx->p.canvas_len;
-  if ((st = check_lmhead(ctx, rows, hidden, weight, hidden_dim, logits, ctx->p.vocab)) != DG_OK) return st;
+  if ((st = check_lmhead_operands(ctx, rows, hidden, weight, hidden_dim)) != DG_OK) return st;
+  if (!workspace) return set_err(ctx, DG_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u)
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  const int64_t need = lmhead_workspace_bytes(rows, ctx->p.vocab);
+  if (workspace_bytes < need)
+    return set_err(ctx, DG_ERR_INVALID_ARG, "workspace_bytes = %lld is below the %lld bytes B = %d needs",
+                   static_cast<long long>(workspace_bytes), static_cast<long long>(need), B);
   if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
   if (step < 0) return set_err(ctx, DG_ERR_INVALID_ARG, "step = %d is negative", step);
   if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
@@ -563,13 +602,30 @@ dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, con
   if (!out->canvas_out) return set_err(ctx, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
   DeviceGuard guard(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = enqueue_lmhead(ctx, rows, hidden, weight, hidden_dim, logits, ctx->p.vocab, s);
-  if (st != DG_OK) return st;
   float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;
   int32_t* am = out->argmax_out ? out->argmax_out : ctx->argmax[0];
   int32_t* smp = out->sample_out ? out->sample_out : ctx->sample;
-  return enqueue_step(ctx, B, logits, DG_DTYPE_F32, ctx->p.vocab, temperature, step, steps, seeds,
-                      prev_argmax, active, ent, am, smp, out, false, s);
+
+  dg::GemmArgs g{};
+  g.hidden = hidden;
+  g.weight = weight;
+  g.rows = rows;
+  g.hidden_dim = hidden_dim;
+  g.vocab = ctx->p.vocab;
+  g.canvas_len = ctx->p.canvas_len;
+  g.temperature = temperature;
+  g.seeds = seeds;
+  g.step = step;
+  g.steps = steps;
+  g.active = active;
+  g.partials = static_cast<dg::RowPartial*>(workspace);
+  g.hint = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + lmhead_partials_bytes(rows, ctx->p.vocab));
+  g.ntiles = dg::lmhead_stats_tiles(ctx->p.vocab);
+  DG_CHECK_HIP(ctx, dg::launch_lmhead_stats(g, s));
+  dg::StatsArgs a = stats_args(ctx, B, nullptr, ctx->p.vocab, temperature, step, steps, seeds, active, ent, am,
+                               smp);
+  DG_CHECK_HIP(ctx, dg::launch_partials_merge(a, g.partials, g.ntiles, s));
+  return enqueue_accept(ctx, B, ent, am, smp, step, steps, seeds, prev_argmax, active, out, false, s);
 }
 
 }  // extern "C"

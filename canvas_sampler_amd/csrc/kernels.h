@@ -6,7 +6,7 @@
 
 namespace dg {
 
-// Partial result of the statistics pass over part of a row (32 bytes): of a
+// Partial result of the statistics pass over part of a row (40 bytes): of a
 // wave, of a workgroup, or of a split of a row over several workgroups.
 //   s, w     sums of 2^t and t*2^t, t = z*c - ref with c = log2(e)/T and ref
 //            an fp32 value at most the part's max z*c (-inf: nothing finite)
@@ -81,11 +81,23 @@ struct StatsArgs {
 struct GemmArgs {
   const void* hidden;      // bf16 [rows, hidden_dim]
   const void* weight;      // bf16 [hidden_dim, vocab]
-  float* logits;           // fp32 [rows, ld_logits]
+  float* logits;           // fp32 [rows, ld_logits] (the product alone)
   int64_t ld_logits;
   int32_t rows;
   int32_t hidden_dim;      // multiple of 64
   int32_t vocab;           // multiple of 8
+  // The product with the statistics epilogue (logits never stored): each
+  // 256 x 256 tile holds four whole blocks of the sampling protocol and
+  // writes one RowPartial per row into partials[row * ntiles + tile].
+  int32_t canvas_len;
+  const float* temperature;   // [rows / canvas_len]
+  const uint64_t* seeds;
+  int32_t step;
+  const int32_t* steps;       // may be null: per-canvas step, else `step`
+  const uint8_t* active;      // may be null: tiles whose rows all lie in inactive canvases are skipped
+  RowPartial* partials;       // [rows, ntiles]
+  uint32_t* hint;             // [rows]: best block score so far (order-preserving bits), zero at launch
+  int32_t ntiles;             // tiles per row: 16 * ceil(vocab / 4096)
 };
 
 // Self-conditioning matmul: out[r, n] = sum_v softmax(z_r / T)_v E[v, n].
@@ -132,6 +144,13 @@ int32_t stats_row_grid(int32_t rows, int32_t vocab, int32_t nsplit, bool has_act
 hipError_t launch_canvas_stats(const StatsArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_renoise(const AcceptArgs& a, int32_t batch, hipStream_t stream);
 hipError_t launch_lmhead_gemm(const GemmArgs& g, hipStream_t stream);
+// The product with the statistics epilogue, then the merge of each row's tile
+// partials into a.entropy / a.argmax / a.sample (a: rows, vocab, canvas_len,
+// active as for the statistics pass). Tiles per row for `vocab`:
+int32_t lmhead_stats_tiles(int32_t vocab);
+hipError_t launch_lmhead_stats(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_partials_merge(const StatsArgs& a, const RowPartial* partials, int32_t nparts,
+                                 hipStream_t stream);
 // Start of a device-resident run: every canvas active, no steps used, not
 // stopped, temperature t0.
 hipError_t launch_run_state_init(int32_t batch, uint8_t* active, int32_t* steps_used,

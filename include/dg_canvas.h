@@ -386,19 +386,43 @@ dg_status dg_tokens_per_forward(const int32_t* steps_used, int32_t n_canvases, i
 dg_status dg_lmhead_logits(dg_ctx* ctx, int32_t rows, const void* hidden, const void* weight,
                            int32_t hidden_dim, float* logits, int64_t ld_logits, void* stream);
 
-/* One sampler step of B canvases whose logits come from the LM head:
- * dg_lmhead_logits into `logits` ([B*L, V] fp32, row stride V, caller-owned
- * workspace that holds the logits afterwards), then dg_sampler_step on them.
- *   temperature  device float [B]
- *   step         the step index of every canvas when `steps` is NULL
- *   steps        device int32 [B] or NULL: canvas c draws its random numbers
- *                for step steps[c] (values >= 0, not checked), so canvases at
- *                different points of their schedules share one call
- * The other arguments are those of dg_lmhead_logits and dg_sampler_step. */
+/* Device workspace, in bytes, that dg_lmhead_sampler_step needs for B
+ * canvases (1 <= B <= max_batch): 40 * B * L * 16 * ceil(V / 4096) + 4 * B * L.
+ *   bytes   host int64 out */
+dg_status dg_lmhead_workspace_bytes(const dg_ctx* ctx, int32_t B, int64_t* bytes);
+
+/* One sampler step of B canvases whose logits come from the LM head, with the
+ * logits never stored: the product of dg_lmhead_logits (the same fp32 values
+ * bit for bit) feeds the statistics of dg_sampler_step inside the product's
+ * own epilogue. Every 256 x 256 tile of the product holds four whole blocks of
+ * the sampler's two-level Gumbel-max protocol, so the tile reduces each of its
+ * rows to one partial (maximum and its first id, the entropy sums, its best
+ * block's score and the in-block draw of that block; "DiffusionGemma Lab",
+ * §2 items 2 and 5); a merge of every row's partials gives the entropy,
+ * argmax and sample, and the acceptance of dg_sampler_step follows.
+ * Argmax and acceptance inputs are those of dg_sampler_step on the
+ * dg_lmhead_logits product: the argmax is identical, the entropy agrees to
+ * fp32 rounding of the sums, and the sample is identical except where two
+ * perturbed scores lie within fp32 rounding of each other.
+ *   workspace        device, 16-byte aligned, at least
+ *                    dg_lmhead_workspace_bytes(ctx, B) bytes (else
+ *                    DG_ERR_INVALID_ARG); its contents are overwritten
+ *   temperature      device float [B]
+ *   step             the step index of every canvas when `steps` is NULL
+ *   steps            device int32 [B] or NULL: canvas c draws its random
+ *                    numbers for step steps[c] (values >= 0, not checked), so
+ *                    canvases at different points of their schedules share
+ *                    one call
+ *   active           device uint8 [B] or NULL: as for dg_sampler_step; tiles
+ *                    whose rows all lie in inactive canvases are not computed
+ * hidden, weight and hidden_dim are those of dg_lmhead_logits (the same shape
+ * limits); seeds, prev_argmax and out those of dg_sampler_step. Products that
+ * overflow fp32 (an infinite logit) give unspecified statistics. Asynchronous
+ * on `stream`. */
 dg_status dg_lmhead_sampler_step(dg_ctx* ctx, int32_t B, const void* hidden, const void* weight,
-                                 int32_t hidden_dim, float* logits, const float* temperature,
-                                 int32_t step, const int32_t* steps, const uint64_t* seeds,
-                                 const int32_t* prev_argmax, const uint8_t* active,
+                                 int32_t hidden_dim, void* workspace, int64_t workspace_bytes,
+                                 const float* temperature, int32_t step, const int32_t* steps,
+                                 const uint64_t* seeds, const int32_t* prev_argmax, const uint8_t* active,
                                  const dg_step_out* out, void* stream);
 
 /* dg_sampler_step for callers that cannot allocate device memory (code under
