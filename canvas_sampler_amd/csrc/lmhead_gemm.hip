@@ -58,6 +58,8 @@ constexpr int kTilesPerChunk = kChunkIds / kBN;   // 16: four blocks per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
+constexpr int kBlkPitch = 68;   // floats per parked block row (64 logits, padded)
+
 struct GemmLds {
   uint16_t a[2][kBM * kPitch];
   uint16_t b[2][kBN * kPitch];
@@ -76,13 +78,15 @@ struct EpiLds {
   uint32_t hint[kBM];      // the row's best block score seen when the tile started
   float hmax[2][kBM];      // largest logit of each half
   int32_t hkey[2][kBM];    // its first position key (s * 32 + u * 8 + t), or INT_MAX
-  float g2[kBM][4];        // block Gumbels, log2 units
   float hs[2][kBM][4];     // half-block sums of 2^t
   float hw[2][kBM][4];     // half-block sums of t * 2^t
   int32_t draw_u[kBM];     // block (0..3) to draw in, or -1
-  uint64_t draw[2][kBM];   // (score, id) keys of the half draws
+  int32_t sample[kBM];     // the draw's id
+  float blk[kBM][kBlkPitch];  // the 64 logits of each drawn block (-inf past V), by stripe and id
   RowPartial fin[kBM];
 };
+
+static_assert(sizeof(EpiLds) <= sizeof(GemmLds), "the epilogue's LDS overlays the operand stages");
 
 union TileLds {
   GemmLds g;
@@ -99,23 +103,17 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t lo, uint32_t hi, bool h
   return hi_half ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
 }
 
-// ---- reductions over the 16 lanes of a DPP row (one row of the tile's logits
-// for the lanes of one MFMA row group). Every lane of the row returns the same
-// bits: each step combines a lane with one partner by a commutative operation.
-
-// Largest value of the row's 16 lanes (never NaN).
-__device__ __forceinline__ float row16_max(float v) {
-  v = max_raw(v, f32_of(dpp_mov<kDppXor8>(u32_of(v))));
-  v = max_raw(v, f32_of(dpp_mov<kDppRor4>(u32_of(v))));
-  v = max_raw(v, f32_of(dpp_mov<kDppXor2>(u32_of(v))));
-  return max_raw(v, f32_of(dpp_mov<kDppXor1>(u32_of(v))));
+// Cross-lane moves inside a DPP row of 16 lanes for the reductions of the
+// statistics epilogue (every control used here has an in-row source for every
+// lane, so no lane keeps an old value).
+template <int C>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), C, 0xF, 0xF, true));
 }
 
-__device__ __forceinline__ int row16_min(int v) {
-  v = min(v, static_cast<int>(dpp_mov<kDppXor8>(static_cast<uint32_t>(v))));
-  v = min(v, static_cast<int>(dpp_mov<kDppRor4>(static_cast<uint32_t>(v))));
-  v = min(v, static_cast<int>(dpp_mov<kDppXor2>(static_cast<uint32_t>(v))));
-  return min(v, static_cast<int>(dpp_mov<kDppXor1>(static_cast<uint32_t>(v))));
+template <int C>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, C, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ uint64_t row16_max_u64(uint64_t k) {
@@ -123,24 +121,6 @@ __device__ __forceinline__ uint64_t row16_max_u64(uint64_t k) {
   k = max_u64(k, dpp_mov_u64<kDppRor4>(k));
   k = max_u64(k, dpp_mov_u64<kDppXor2>(k));
   return max_u64(k, dpp_mov_u64<kDppXor1>(k));
-}
-
-// Sum over the four lanes n, n ^ 4, n ^ 8, n ^ 12 of the row: the half of one
-// block (lane i adds lane i ^ 8, then lane (i - 4) mod 16).
-__device__ __forceinline__ float block_half_sum(float v) {
-  v += f32_of(dpp_mov<kDppXor8>(u32_of(v)));
-  return v + f32_of(dpp_mov<kDppRor4>(u32_of(v)));
-}
-
-// Over the four lanes of a quad (the four blocks of the tile).
-__device__ __forceinline__ uint64_t quad_max_u64(uint64_t k) {
-  k = max_u64(k, dpp_mov_u64<kDppXor1>(k));
-  return max_u64(k, dpp_mov_u64<kDppXor2>(k));
-}
-
-__device__ __forceinline__ double quad_sum(double v) {
-  v += dpp_mov_f64<kDppXor1>(v);
-  return v + dpp_mov_f64<kDppXor2>(v);
 }
 
 __device__ __forceinline__ uint32_t word_of(const Words4& w, int k) {
@@ -187,7 +167,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
   float rc_temp = 1.0f;
   int32_t rc_step = 0, rc_pos = 0;
   uint64_t rc_seed = 0;
-  uint32_t rc_hint = 0;
   if constexpr (kStats) {
     if (g.active != nullptr) {
       // a tile whose rows all belong to inactive canvases has nothing to do
@@ -204,7 +183,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
       rc_temp = g.temperature[canvas];
       rc_step = g.steps != nullptr ? g.steps[canvas] : g.step;
       rc_seed = g.seeds[canvas];
-      rc_hint = __hip_atomic_load(&g.hint[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -344,115 +322,173 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
       e.step[tid] = rc_step;
       e.k0[tid] = static_cast<uint32_t>(rc_seed);
       e.k1[tid] = static_cast<uint32_t>(rc_seed >> 32);
-      e.hint[tid] = rc_hint;
     }
-    // phase 1: largest logit of each half row
+    // the row's running best block score, read now (its latency hides behind
+    // phases 1 and 2) and parked for phase 3
+    uint32_t rc_hint = 0;
+    if (tid < kBM)
+      rc_hint = __hip_atomic_load(&g.hint[min(m0 + tid, g.rows - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // phase 1: largest logit of each half row. The reductions over a DPP
+    // row run step by step across all 16 row slots, so that consecutive
+    // cross-lane moves are independent.
+    {
+      float m[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float m = max3_raw(max3_raw(acc[i][0][q], acc[i][1][q], acc[i][2][q]),
-                           max3_raw(acc[i][3][q], acc[i][4][q], acc[i][5][q]), max_raw(acc[i][6][q], acc[i][7][q]));
-        m = row16_max(ok ? m : kNegInf);
-        if (n == 0) e.hmax[wn][local_row(i, q)] = m;
+        for (int q = 0; q < 4; ++q) {
+          const float v = max3_raw(max3_raw(acc[i][0][q], acc[i][1][q], acc[i][2][q]),
+                                   max3_raw(acc[i][3][q], acc[i][4][q], acc[i][5][q]),
+                                   max_raw(acc[i][6][q], acc[i][7][q]));
+          m[4 * i + q] = ok ? v : kNegInf;
+        }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m[r] = max_raw(m[r], dpp_f<kDppXor8>(m[r]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m[r] = max_raw(m[r], dpp_f<kDppRor4>(m[r]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m[r] = max_raw(m[r], dpp_f<kDppXor2>(m[r]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m[r] = max_raw(m[r], dpp_f<kDppXor1>(m[r]));
+      if (n == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e.hmax[wn][local_row(r >> 2, r & 3)] = m[r];
       }
+    }
     __syncthreads();
 
-    // phase 2: the block Gumbels (thread: blocks 2 (tid >> 8) + {0, 1} of
-    // local row tid & 255; the Philox call of block j is at counter j with
-    // bits 9-10 cleared, word (j >> 9) & 3), and against ref = tile max * c
-    // the half-block sums and the first position of the tile maximum
+    // phase 2: against ref = tile max * c, the half-block sums and the first
+    // position of the tile maximum (reductions batched as in phase 1)
     {
-      const int lr = tid & (kBM - 1);
+      float sv[16], wv[16];
+      int kv[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lr = local_row(i, q);
+          const float tm = max_raw(e.hmax[0][lr], e.hmax[1][lr]);
+          const float c = e.c[lr];
+          const float ref = __fmul_rn(tm, c);
+          float ex[8];
+          float w4[4] = {0.f, 0.f, 0.f, 0.f};
+          int kf = 8;
+#pragma unroll
+          for (int t = 7; t >= 0; --t) kf = acc[i][t][q] == tm ? t : kf;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float tt = fmaf(acc[i][t][q], c, -ref);
+            ex[t] = __builtin_amdgcn_exp2f(tt);
+            w4[t & 3] = fmaf(tt, ex[t], w4[t & 3]);
+          }
+          const float s = ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
+          const float w = (w4[0] + w4[1]) + (w4[2] + w4[3]);
+          sv[4 * i + q] = ok ? s : 0.0f;
+          wv[4 * i + q] = ok ? w : 0.0f;
+          kv[4 * i + q] = ok && kf < 8 ? key0 + kf : 0x7FFFFFFF;
+        }
+      // half-block sums over lanes n, n ^ 4, n ^ 8, n ^ 12 (lane i adds lane
+      // i ^ 8, then lane (i - 4) mod 16: the same bits in all four), and the
+      // first position over the row's 16 lanes
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sv[r] += dpp_f<kDppXor8>(sv[r]);
+        wv[r] += dpp_f<kDppXor8>(wv[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sv[r] += dpp_f<kDppRor4>(sv[r]);
+        wv[r] += dpp_f<kDppRor4>(wv[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) kv[r] = min(kv[r], dpp_i<kDppXor8>(kv[r]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) kv[r] = min(kv[r], dpp_i<kDppRor4>(kv[r]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) kv[r] = min(kv[r], dpp_i<kDppXor2>(kv[r]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) kv[r] = min(kv[r], dpp_i<kDppXor1>(kv[r]));
+      if (n < 4) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = local_row(r >> 2, r & 3);
+          e.hs[wn][lr][n] = sv[r];
+          e.hw[wn][lr][n] = wv[r];
+        }
+      }
+      if (n == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e.hkey[wn][local_row(r >> 2, r & 3)] = kv[r];
+      }
+      if (tid < kBM) e.hint[tid] = rc_hint;
+    }
+    __syncthreads();
+
+    // phase 3: thread t takes blocks 2 (t & 1) + {0, 1} of local row t >> 1
+    // (its partner lane t ^ 1 the other two): their Gumbels (the Philox call
+    // of block j is at counter j with bits 9-10 cleared, word (j >> 9) & 3),
+    // sums and scores, then over the pair the tile's best block, its sums in
+    // fp64, the first id of its maximum, and whether to draw
+    {
+      const int lr = tid >> 1;
+      const int ub = 2 * (tid & 1);
+      const float tm = max_raw(e.hmax[0][lr], e.hmax[1][lr]);
+      const float ref = __fmul_rn(tm, e.c[lr]);
+      const uint32_t pos = static_cast<uint32_t>(e.pos[lr]), stp = static_cast<uint32_t>(e.step[lr]);
+      const uint32_t k0 = e.k0[lr], k1 = e.k1[lr];
+      uint64_t kb = 0;
+      double s = 0.0, w = 0.0;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int ub = 2 * (tid >> 8) + h;
-        const uint32_t j = static_cast<uint32_t>(ch * kSlots + 4 * qb + ub);
-        const Words4 w = philox4x32_10(j & ~0x600u, static_cast<uint32_t>(e.pos[lr]),
-                                       static_cast<uint32_t>(e.step[lr]), kTagBlock, e.k0[lr], e.k1[lr]);
-        e.g2[lr][ub] = kLog2e * gumbel(word_of(w, static_cast<int>((j >> 9) & 3)));
+        const int ub2 = ub + h;
+        const uint32_t j = static_cast<uint32_t>(ch * kSlots + 4 * qb + ub2);
+        const Words4 wd = philox4x32_10(j & ~0x600u, pos, stp, kTagBlock, k0, k1);
+        const float g2 = kLog2e * gumbel(word_of(wd, static_cast<int>((j >> 9) & 3)));
+        const float sb = e.hs[0][lr][ub2] + e.hs[1][lr][ub2];
+        const float wb = e.hw[0][lr][ub2] + e.hw[1][lr][ub2];
+        const float score = sb > 0.0f ? ref + __log2f(sb) + g2 : kNegInf;
+        kb = max_u64(kb, argmax_key(score, ub2));
+        s += static_cast<double>(sb);
+        w += static_cast<double>(wb);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr = local_row(i, q);
-        const float tm = max_raw(e.hmax[0][lr], e.hmax[1][lr]);
-        const float c = e.c[lr];
-        const float ref = __fmul_rn(tm, c);
-        float ex[8];
-        float w4[4] = {0.f, 0.f, 0.f, 0.f};
-        int kf = 8;
-#pragma unroll
-        for (int t = 7; t >= 0; --t) kf = acc[i][t][q] == tm ? t : kf;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float tt = fmaf(acc[i][t][q], c, -ref);
-          ex[t] = __builtin_amdgcn_exp2f(tt);
-          w4[t & 3] = fmaf(tt, ex[t], w4[t & 3]);
-        }
-        float s = ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
-        float w = (w4[0] + w4[1]) + (w4[2] + w4[3]);
-        s = block_half_sum(ok ? s : 0.0f);
-        w = block_half_sum(ok ? w : 0.0f);
-        const int key = row16_min(ok && kf < 8 ? key0 + kf : 0x7FFFFFFF);
-        if (n < 4) {
-          e.hs[wn][lr][n] = s;
-          e.hw[wn][lr][n] = w;
-        }
-        if (n == 0) e.hkey[wn][lr] = key;
-      }
-    __syncthreads();
-
-    // phase 3 (wave (wm, wn) takes MFMA row tiles 2 wn, 2 wn + 1 of its 64
-    // rows): block sums and scores, the tile's best block, its sums in fp64,
-    // the first id of its maximum, and whether to draw
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr = local_row(2 * wn + ii, q);
-        const float tm = max_raw(e.hmax[0][lr], e.hmax[1][lr]);
-        const float ref = __fmul_rn(tm, e.c[lr]);
-        const float sb = e.hs[0][lr][u] + e.hs[1][lr][u];
-        const float wb = e.hw[0][lr][u] + e.hw[1][lr][u];
-        const float score = sb > 0.0f ? ref + __log2f(sb) + e.g2[lr][u] : kNegInf;
+      kb = max_u64(kb, dpp_mov_u64<kDppXor1>(kb));
+      s += dpp_mov_f64<kDppXor1>(s);
+      w += dpp_mov_f64<kDppXor1>(w);
+      if ((tid & 1) == 0) {
         float best;
         int ubest;
-        argmax_unkey(quad_max_u64(argmax_key(score, u)), best, ubest);
-        const double s = quad_sum(static_cast<double>(sb));
-        const double w = quad_sum(static_cast<double>(wb));
-        if (n == 0) {
-          const int key = min(e.hkey[0][lr], e.hkey[1][lr]);
-          RowPartial f;
-          f.s = s;
-          f.w = w;
-          f.ref = tm == kNegInf ? kNegInf : ref;
-          f.m = tm;
-          f.argmax = key == 0x7FFFFFFF ? 0x7FFFFFFF
-                                       : ch * kChunkIds + (key >> 5) * kStripeIds +
-                                             (4 * qb + ((key >> 3) & 3)) * kSlotIds + (key & 7);
-          const bool has = best != kNegInf;
-          f.best = best;
-          f.bestj = has ? ch * kSlots + 4 * qb + ubest : 0x7FFFFFFF;
-          f.sample = 0x7FFFFFFF;
-          // draw unless an earlier tile's best block of this row beats this
-          // one's strictly: the row's best block then always draws
-          const uint32_t ob = ordered_bits(best);
-          const bool draw = has && ob >= e.hint[lr];
-          const int32_t row = m0 + lr;
-          if (draw && row < g.rows)
-            __hip_atomic_fetch_max(&g.hint[row], ob, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          e.draw_u[lr] = draw ? ubest : -1;
-          e.fin[lr] = f;
-        }
+        argmax_unkey(kb, best, ubest);
+        const int key = min(e.hkey[0][lr], e.hkey[1][lr]);
+        RowPartial f;
+        f.s = s;
+        f.w = w;
+        f.ref = tm == kNegInf ? kNegInf : ref;
+        f.m = tm;
+        f.argmax = key == 0x7FFFFFFF ? 0x7FFFFFFF
+                                     : ch * kChunkIds + (key >> 5) * kStripeIds +
+                                           (4 * qb + ((key >> 3) & 3)) * kSlotIds + (key & 7);
+        const bool has = best != kNegInf;
+        f.best = best;
+        f.bestj = has ? ch * kSlots + 4 * qb + ubest : 0x7FFFFFFF;
+        f.sample = 0x7FFFFFFF;
+        // draw unless an earlier tile's best block of this row beats this
+        // one's strictly: the row's best block then always draws
+        const uint32_t ob = ordered_bits(best);
+        const bool draw = has && ob >= e.hint[lr];
+        const int32_t row = m0 + lr;
+        if (draw && row < g.rows)
+          __hip_atomic_fetch_max(&g.hint[row], ob, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        e.draw_u[lr] = draw ? ubest : -1;
+        e.fin[lr] = f;
       }
+    }
     __syncthreads();
 
-    // phase 4: the in-block draw, argmax of z/T + G over the block's 64 ids
+    // phase 4: the in-block draws, argmax of z/T + G over the block's 64 ids
     // (lowest id on ties), G from the Philox call at counter id >> 2, word
-    // id & 3; the lanes of the drawn block take two calls for their 8 ids
+    // id & 3. The lanes holding a drawn block park its logits in LDS; then
+    // each DPP row of 16 lanes takes one drawing row, a lane per 4 ids (one
+    // Philox call), so that the work scales with the number of draws.
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -460,26 +496,49 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
         const int lr = local_row(i, q);
         const int ud = e.draw_u[lr];
         if (__builtin_amdgcn_ballot_w64(ud >= 0) == 0) continue;
+        if (ud == u) {
+          float* dst = &e.blk[lr][(4 * wn + (n >> 2)) * kSlotIds];
+          reinterpret_cast<float4*>(dst)[0] = ok ? make_float4(acc[i][0][q], acc[i][1][q], acc[i][2][q], acc[i][3][q])
+                                                 : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+          reinterpret_cast<float4*>(dst)[1] = ok ? make_float4(acc[i][4][q], acc[i][5][q], acc[i][6][q], acc[i][7][q])
+                                                 : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+        }
+      }
+    __syncthreads();
+    {
+      const int quad = tid & 15;   // ids 4 quad .. 4 quad + 3 of the block: stripe quad / 2
+#pragma unroll 1
+      for (int it = 0; it < kBM / (kGemmThreads / 16); ++it) {
+        const int lr = it * (kGemmThreads / 16) + (tid >> 4);
+        const int ud = e.draw_u[lr];
+        if (__builtin_amdgcn_ballot_w64(ud >= 0) == 0) continue;
         float sc = kNegInf;
         int32_t id = 0x7FFFFFFF;
-        if (ud == u && ok) {
+        if (ud >= 0) {
+          const int32_t q0 = ch * kChunkIds + (quad >> 1) * kStripeIds + (4 * qb + ud) * kSlotIds + 4 * (quad & 1);
+          const Words4 wd = philox4x32_10(static_cast<uint32_t>(q0 >> 2), static_cast<uint32_t>(e.pos[lr]),
+                                          static_cast<uint32_t>(e.step[lr]), kTagElem, e.k0[lr], e.k1[lr]);
+          const float4 z = reinterpret_cast<const float4*>(&e.blk[lr][4 * quad])[0];
           const float inv_t = e.inv_t[lr];
-          const uint32_t pos = static_cast<uint32_t>(e.pos[lr]), stp = static_cast<uint32_t>(e.step[lr]);
-          const uint32_t k0 = e.k0[lr], k1 = e.k1[lr];
-          const Words4 wa = philox4x32_10(static_cast<uint32_t>(id0 >> 2), pos, stp, kTagElem, k0, k1);
-          const Words4 wb = philox4x32_10(static_cast<uint32_t>(id0 >> 2) + 1u, pos, stp, kTagElem, k0, k1);
+          const float zz[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float v = acc[i][t][q] * inv_t + gumbel(t < 4 ? wa.w[t] : wb.w[t - 4]);
+          for (int t = 0; t < 4; ++t) {
+            const float v = zz[t] * inv_t + gumbel(wd.w[t]);
             if (v > sc) {
               sc = v;
-              id = id0 + t;
+              id = q0 + t;
             }
           }
         }
         const uint64_t k = row16_max_u64(argmax_key(sc, id));
-        if (n == 0 && ud >= 0) e.draw[wn][lr] = k;
+        if (quad == 0 && ud >= 0) {
+          float best;
+          int32_t smp;
+          argmax_unkey(k, best, smp);
+          e.sample[lr] = smp;
+        }
       }
+    }
     __syncthreads();
 
     // phase 5: threads 0..255 write the partials of their local rows
@@ -487,12 +546,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
       const int32_t row = m0 + tid;
       if (row < g.rows) {
         RowPartial f = e.fin[tid];
-        if (e.draw_u[tid] >= 0) {
-          float sc;
-          int32_t id;
-          argmax_unkey(max_u64(e.draw[0][tid], e.draw[1][tid]), sc, id);
-          f.sample = id;
-        }
+        if (e.draw_u[tid] >= 0) f.sample = e.sample[tid];
         g.partials[static_cast<int64_t>(row) * g.ntiles + nt] = f;
       }
     }
