@@ -31,6 +31,8 @@
 //   - one slice per row tile: the workgroup divides by S and writes out;
 //     otherwise it writes its unnormalised partial tile, and a second kernel
 //     sums the slices in a fixed order and divides.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -70,67 +72,64 @@ struct ZTile {
   static constexpr int kBytes = kScRowTile * kStride;
 };
 
-// This thread's pieces of a chunk, loaded with whole lines per row: piece
-// p = tid + kScThreads * i is 16-byte piece p % kPiecesPerRow of tile row
-// p / kPiecesPerRow. Rows past the batch or of inactive canvases, and ids at or past `end`, read as
-// -inf, so their probability is exactly 0 and no later step needs a bound
-// check; only a piece that straddles `end` (V not a multiple of the piece) is
-// masked element by element. Pieces never cross the row's padded end: the row
-// stride is a multiple of 16 bytes and every piece that is read starts below
-// `end` <= V.
+// f(std::integral_constant<int, i>) for i = 0 .. N-1: the indices are
+// constants from the start, so that arrays indexed by them stay in registers
+// (a loop unrolled later would leave them in scratch memory).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 // Whether `row` takes part: inside the batch and of an active canvas.
 __device__ __forceinline__ bool row_live(const SelfCondArgs& a, int32_t row) {
   return row < a.rows && (a.active == nullptr || a.active[row / a.canvas_len] != 0);
 }
 
+// (clang vector type, not HIP's uint4 struct: struct copies between address
+// spaces become memory copies that keep the array out of registers)
 template <bool kBf16>
 struct Raw {
-  uint4 q[ZTile<kBf16>::kPieces];
+  u32x4_t q[ZTile<kBf16>::kPieces];
 };
 
+// This thread's pieces of a chunk, loaded with whole lines per row: piece
+// p = tid + kScThreads * i is 16-byte piece p % kPiecesPerRow of tile row
+// p / kPiecesPerRow. Every load is unconditional, so that all of them are in
+// flight at once: rows past the batch are clamped onto the last row and ids
+// past the row's stride onto its last piece. What those clamped pieces hold
+// never counts: a row that does not take part has zero probability everywhere
+// (see the kernel), and ids at or past the slice end are masked where the
+// probabilities are formed.
 template <bool kBf16>
-__device__ __forceinline__ void load_chunk(const SelfCondArgs& a, int32_t row0, int64_t kc, int64_t end,
-                                           int tid, Raw<kBf16>& r) {
+__device__ __forceinline__ void load_chunk(const SelfCondArgs& a, int32_t row0, int64_t kc, int tid,
+                                           Raw<kBf16>& r) {
   using G = ZTile<kBf16>;
-  constexpr uint32_t kNegInf2 = kBf16 ? 0xFF80FF80u : 0xFF800000u;  // one 32-bit word of -inf
-#pragma unroll
-  for (int i = 0; i < G::kPieces; ++i) {
+  static_for<G::kPieces>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
     const int piece = tid + kScThreads * i;
-    const int32_t row = row0 + piece / G::kPiecesPerRow;
-    const int64_t id = kc + static_cast<int64_t>(piece % G::kPiecesPerRow) * G::kPerPiece;
-    uint4 w = make_uint4(kNegInf2, kNegInf2, kNegInf2, kNegInf2);
-    if (row_live(a, row) && id < end) {
-      const int64_t off = static_cast<int64_t>(row) * a.row_stride + id;
-      if constexpr (kBf16)
-        w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.logits) + off);
-      else
-        w = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.logits) + off);
-      if (id + G::kPerPiece > end) {  // the piece that straddles the end of the row
-        uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int e = 0; e < G::kPerPiece; ++e) {
-          if (id + e < end) continue;
-          if constexpr (kBf16)
-            u[e >> 1] = (e & 1) ? (u[e >> 1] & 0x0000FFFFu) | 0xFF800000u : (u[e >> 1] & 0xFFFF0000u) | 0xFF80u;
-          else
-            u[e] = 0xFF800000u;
-        }
-        w = make_uint4(u[0], u[1], u[2], u[3]);
-      }
-    }
-    r.q[i] = w;
-  }
+    const int32_t row = min(row0 + piece / G::kPiecesPerRow, a.rows - 1);
+    int64_t id = kc + static_cast<int64_t>(piece % G::kPiecesPerRow) * G::kPerPiece;
+    id = id < a.row_stride - G::kPerPiece ? id : a.row_stride - G::kPerPiece;
+    const int64_t off = static_cast<int64_t>(row) * a.row_stride + id;
+    if constexpr (kBf16)
+      r.q[i] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.logits) + off);
+    else
+      r.q[i] = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(a.logits) + off);
+  });
 }
 
 template <bool kBf16>
 __device__ __forceinline__ void store_chunk(uint8_t* s_z, int tid, const Raw<kBf16>& r) {
   using G = ZTile<kBf16>;
-#pragma unroll
-  for (int i = 0; i < G::kPieces; ++i) {
+  static_for<G::kPieces>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
     const int piece = tid + kScThreads * i;
-    *reinterpret_cast<uint4*>(s_z + (piece / G::kPiecesPerRow) * G::kStride + (piece % G::kPiecesPerRow) * 16) =
+    *reinterpret_cast<u32x4_t*>(s_z + (piece / G::kPiecesPerRow) * G::kStride + (piece % G::kPiecesPerRow) * 16) =
         r.q[i];
-  }
+  });
 }
 
 // The 8 logits of k-step t of tile row `trow` for this half-wave, as fp32.
@@ -182,25 +181,30 @@ __device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) {
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // The chunk's embedding tile as this thread stages it: column n = t % 32,
-// ids kc + 4 (t / 32) .. +3, each split into its three parts.
-__device__ __forceinline__ void load_embed(const SelfCondArgs& a, int64_t kc, int64_t k_end, int tid,
-                                           float (&ev)[4]) {
+// ids kc + 4 (t / 32) .. +3 (E[v, n] below d, ones at d, zeros above). The
+// loads are unconditional, with ids clamped onto the last embedding row:
+// ids at or past the slice end get zero probability.
+__device__ __forceinline__ void load_embed(const SelfCondArgs& a, int64_t kc, int tid, float (&ev)[4]) {
   const int n = tid & 31;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t v = kc + 4 * (tid >> 5) + i;
-    float e = 0.0f;
-    if (v < k_end) e = n < a.d ? a.embed[v * a.d + n] : (n == a.d ? 1.0f : 0.0f);
-    ev[i] = e;
-  }
+  const int nc = n < a.d ? n : a.d - 1;
+  static_for<4>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    int64_t v = kc + 4 * (tid >> 5) + i;
+    v = v < a.vocab ? v : a.vocab - 1;
+    const float e = a.embed[v * a.d + nc];
+    ev[i] = n < a.d ? e : (n == a.d ? 1.0f : 0.0f);
+  });
 }
 
 template <bool kBf16>
 __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
   static_assert(kScThreads == 32 * (kScChunk / 4), "embedding staging covers the tile once");
   using G = ZTile<kBf16>;
-  __shared__ __attribute__((aligned(16))) uint8_t s_z[G::kBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[3][32 * kScBRow];
+  // LDS slots of the staged tiles: two for bf16 logits; fp32 tiles are twice
+  // as large and take one (160 KiB per CU)
+  constexpr int kZSlots = kBf16 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t s_z[kZSlots][G::kBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[kZSlots][3][32 * kScBRow];
   const int32_t tile = static_cast<int32_t>(blockIdx.x) / a.nslice;
   const int32_t slice = static_cast<int32_t>(blockIdx.x) % a.nslice;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
@@ -209,9 +213,9 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
   const int trow = wave * 32 + (lane & 31);  // this lane's row in the tile
   const int32_t row = row0 + trow;
 
-  // rows past the batch or of inactive canvases are all -inf in the tile:
-  // with c = 1 and zmax*c = 0 their probabilities are exactly 0
-  float c = 1.0f, mc = 0.0f;
+  // rows past the batch or of inactive canvases get zmax*c = +inf, so that
+  // every probability of theirs is exactly 0 whatever their tile holds
+  float c = 1.0f, mc = __builtin_inff();
   if (row_live(a, row)) {
     const int64_t off = static_cast<int64_t>(row) * a.row_stride;
     int32_t am = a.argmax[row];
@@ -222,60 +226,110 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
   const int64_t k_begin = static_cast<int64_t>(slice) * a.kslice;
   const int64_t k_end = k_begin + a.kslice < a.vocab ? k_begin + a.kslice : a.vocab;
 
-  // software pipeline: chunk i + 1 is loaded into registers while chunk i is
-  // multiplied out of LDS; two barriers per chunk guard the single LDS tiles
-  Raw<kBf16> raw;
-  float ev[4];
-  load_chunk<kBf16>(a, row0, k_begin, k_end, tid, raw);
-  load_embed(a, k_begin, k_end, tid, ev);
+  // software pipeline: chunk i + 2 is loaded into registers while chunk i is
+  // multiplied out of LDS. With two LDS slots one barrier per chunk both
+  // publishes chunk i and retires the reads of chunk i - 1 (whose slot chunk
+  // i + 1 takes next); with one slot a second barrier guards the slot.
+  Raw<kBf16> raw0, raw1;
+  float ev0[4], ev1[4];
+  load_chunk<kBf16>(a, row0, k_begin, tid, raw0);
+  load_embed(a, k_begin, tid, ev0);
+  if (k_begin + kScChunk < k_end) {
+    load_chunk<kBf16>(a, row0, k_begin + kScChunk, tid, raw1);
+    load_embed(a, k_begin + kScChunk, tid, ev1);
+  }
   f32x16_t acc0 = {}, acc1 = {};
   const int sn = tid & 31, sk = 4 * (tid >> 5);
   const int bo = (lane & 31) * kScBRow + 8 * half;
-  for (int64_t kc = k_begin; kc < k_end; kc += kScChunk) {
-    __syncthreads();  // the previous chunk's LDS reads are done
-    store_chunk<kBf16>(s_z, tid, raw);
+  // kTail: the slice's last chunk reaches past its end; ids there get zero
+  // probability
+  auto run_chunk = [&](auto slot, auto tail, int64_t kc, Raw<kBf16>& raw, float(&ev)[4])
+                       __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    constexpr bool kTail = decltype(tail)::value;
+    constexpr int Z = kZSlots == 2 ? S : 0;
+    uint8_t* zb = s_z[Z];
+    uint16_t(*bb)[32 * kScBRow] = s_b[Z];
+    if constexpr (kZSlots == 1) __syncthreads();  // the previous chunk's LDS reads are done
+    store_chunk<kBf16>(zb, tid, raw);
     {  // this chunk's embedding parts: 4 consecutive ids of one column
       const Split3 e0 = split3(ev[0]), e1 = split3(ev[1]), e2 = split3(ev[2]), e3 = split3(ev[3]);
       const int o = sn * kScBRow + sk;
-      *reinterpret_cast<uint2*>(&s_b[0][o]) = make_uint2(pack2(e0.hi, e1.hi), pack2(e2.hi, e3.hi));
-      *reinterpret_cast<uint2*>(&s_b[1][o]) = make_uint2(pack2(e0.mid, e1.mid), pack2(e2.mid, e3.mid));
-      *reinterpret_cast<uint2*>(&s_b[2][o]) = make_uint2(pack2(e0.lo, e1.lo), pack2(e2.lo, e3.lo));
+      *reinterpret_cast<uint2*>(&bb[0][o]) = make_uint2(pack2(e0.hi, e1.hi), pack2(e2.hi, e3.hi));
+      *reinterpret_cast<uint2*>(&bb[1][o]) = make_uint2(pack2(e0.mid, e1.mid), pack2(e2.mid, e3.mid));
+      *reinterpret_cast<uint2*>(&bb[2][o]) = make_uint2(pack2(e0.lo, e1.lo), pack2(e2.lo, e3.lo));
     }
-    const int64_t kn = kc + kScChunk;
+    const int64_t kn = kc + 2 * kScChunk;
     if (kn < k_end) {
-      load_chunk<kBf16>(a, row0, kn, k_end, tid, raw);
-      load_embed(a, kn, k_end, tid, ev);
+      load_chunk<kBf16>(a, row0, kn, tid, raw);
+      load_embed(a, kn, tid, ev);
     }
-    __syncthreads();  // this chunk's tiles are in LDS
-#pragma unroll
-    for (int t = 0; t < kScSteps; ++t) {
-      // this lane's 8 factors of k-step t, split into three parts
+    __syncthreads();  // chunk kc is in LDS (and, with two slots, every wave is done with the chunk before it)
+    // this lane's 8 factors of k-step t, split into three parts
+    auto factors = [&](int t, bf16x8_t& xh, bf16x8_t& xm, bf16x8_t& xl) __attribute__((always_inline)) {
       float z[8];
-      read_step<kBf16>(s_z, trow, half, t, z);
+      read_step<kBf16>(zb, trow, half, t, z);
       uint32_t h[8], m[8], l[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const Split3 sp = split3(__builtin_amdgcn_exp2f(__builtin_fmaf(z[j], c, -mc)));
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z[j], c, -mc));
+        if constexpr (kTail) e = kc + 16 * t + 8 * half + j < k_end ? e : 0.0f;
+        const Split3 sp = split3(e);
         h[j] = sp.hi;
         m[j] = sp.mid;
         l[j] = sp.lo;
       }
-      const bf16x8_t xh = as_bf16x8(u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]),
-                                            pack2(h[6], h[7])});
-      const bf16x8_t xm = as_bf16x8(u32x4_t{pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]),
-                                            pack2(m[6], m[7])});
-      const bf16x8_t xl = as_bf16x8(u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]),
-                                            pack2(l[6], l[7])});
-      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&s_b[0][bo + 16 * t]);
-      const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(&s_b[1][bo + 16 * t]);
-      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&s_b[2][bo + 16 * t]);
+      xh = as_bf16x8(u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])});
+      xm = as_bf16x8(u32x4_t{pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]), pack2(m[6], m[7])});
+      xl = as_bf16x8(u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])});
+    };
+    // the factors of k-step t + 1 are formed while the matrix cores take the
+    // products of step t: the six products are spread through that VALU work
+    bf16x8_t xh, xm, xl;
+    factors(0, xh, xm, xl);
+#pragma unroll
+    for (int t = 0; t < kScSteps; ++t) {
+      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&bb[0][bo + 16 * t]);
+      const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(&bb[1][bo + 16 * t]);
+      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&bb[2][bo + 16 * t]);
+      bf16x8_t nh = xh, nm = xm, nl = xl;
+      if (t + 1 < kScSteps) factors(t + 1, nh, nm, nl);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, bh, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xm, bm, acc1, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, bl, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xm, bh, acc1, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, bm, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, bh, acc1, 0, 0, 0);
+      if (t + 1 < kScSteps) {
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix-core product
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then VALU work of the next step
+        }
+      }
+      xh = nh;
+      xm = nm;
+      xl = nl;
     }
+  };
+  // chunk i of the slice takes register slot i % 2: a loop over pairs of
+  // whole chunks keeps every slot index a constant; then at most one whole
+  // chunk and the partial one
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+  const int64_t full_end = k_begin + (k_end - k_begin) / kScChunk * kScChunk;
+  int64_t kc = k_begin;
+  for (; kc + kScChunk < full_end; kc += 2 * kScChunk) {
+    run_chunk(Slot0{}, Full{}, kc, raw0, ev0);
+    run_chunk(Slot1{}, Full{}, kc + kScChunk, raw1, ev1);
+  }
+  if (kc < full_end) {
+    run_chunk(Slot0{}, Full{}, kc, raw0, ev0);
+    if (kc + kScChunk < k_end) run_chunk(Slot1{}, Tail{}, kc + kScChunk, raw1, ev1);
+  } else if (kc < k_end) {
+    run_chunk(Slot0{}, Tail{}, kc, raw0, ev0);
   }
   const f32x16_t acc = acc0 + acc1;
   // lane l, register r holds D[i][n] with n = l % 32 and
