@@ -573,6 +573,31 @@ def lmhead_leg(args, torch, B, synth, keep=None):
     return rec
 
 
+def _step_buffers(torch, n, L):
+    """Device buffers for every output of one step of n canvases."""
+    dev = "cuda"
+    return dict(canvas_out=torch.empty(n * L, dtype=torch.int32, device=dev),
+                argmax_out=torch.empty(n * L, dtype=torch.int32, device=dev),
+                sample_out=torch.empty(n * L, dtype=torch.int32, device=dev),
+                accept_out=torch.empty(n * L, dtype=torch.uint8, device=dev),
+                entropy_out=torch.empty(n * L, device=dev),
+                n_accept_out=torch.empty(n, dtype=torch.int32, device=dev),
+                mean_entropy_out=torch.empty(n, device=dev),
+                stop_out=torch.empty(n, dtype=torch.uint8, device=dev))
+
+
+def _host_outputs(bufs, n, L):
+    """Per-canvas host dicts of one step's outputs."""
+    g = {k: v.cpu().numpy() for k, v in bufs.items()}
+    out = []
+    for c in range(n):
+        sl = slice(c * L, (c + 1) * L)
+        out.append(dict(entropy=g["entropy_out"][sl], argmax=g["argmax_out"][sl], sample=g["sample_out"][sl],
+                        accept=g["accept_out"][sl], n_accept=g["n_accept_out"][c], canvas=g["canvas_out"][sl],
+                        mean_entropy=g["mean_entropy_out"][c], stop=g["stop_out"][c]))
+    return out
+
+
 def cpu_baseline_leg(torch, B, synth, c2, c5):
     """The oracle on the host cores, on bounded samples of each workload, and
     its agreement with the GPU on the very same inputs.
