@@ -29,7 +29,9 @@
 // they never wait behind the stream. Per element the loop costs one convert,
 // half a max, one fma, one v_exp_f32, one add and one fma; per block one
 // wave-uniform test for the rare cases, one log2 and two ballots. The block
-// Gumbels are not drawn in the stream: the workgroup draws those of a whole
+// Gumbels: in the one-row kernel each wave draws its own as it goes (one
+// Philox call per four of its blocks, kept as a shift register, no barrier
+// before the stream); in the row loop the workgroup draws those of a whole
 // segment of 64 chunks into LDS beforehand (the first while the first loads
 // are in flight, the next ones before the barrier that ends a segment or a
 // row). When a block ends its logits are still in registers, so nothing is
@@ -40,6 +42,9 @@
 // 40-byte partials. A row split over several workgroups (for very short
 // batches) is merged by the last workgroup to finish (atomic ticket,
 // release/acquire at agent scope).
+//
+// partials_merge_kernel merges, one wave per row and in a fixed order, the
+// per-tile partials that the LM-head product's statistics epilogue writes.
 #include <type_traits>
 
 #include "device_common.h"
