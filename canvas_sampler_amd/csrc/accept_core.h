@@ -2,6 +2,9 @@
 // sampler step), run by accept_renoise_kernel with one workgroup per canvas.
 //
 // One thread per position, kAcceptThreads (256) positions at most:
+//   - only positions with H <= b can come before the last accepted one, so
+//     when fewer than 64 have it, one wave sorts those alone (plus the
+//     smallest key above b); otherwise:
 //   - sort the L keys (entropy bits << 32 | position) ascending with a
 //     bitonic network, in-wave steps by DPP and permlane swaps (no LDS round
 //     trip) and the cross-wave steps through LDS (entropies are >= +0, so
@@ -98,6 +101,9 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   __shared__ int32_t s_same[kWaves];
   __shared__ int32_t s_wmin[kWaves];
   __shared__ uint8_t s_acc[kAcceptThreads];
+  __shared__ int32_t s_ccount[kWaves];
+  __shared__ uint64_t s_omin[kWaves];
+  __shared__ int32_t s_kstar;
 
   const int tid = threadIdx.x;
   const bool part = tid < kAcceptThreads;   // owns a key slot
@@ -127,60 +133,133 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
                                     static_cast<uint32_t>(in.seed >> 32));
     renoise = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
   }
-  // bitonic sort of 256 keys, ascending. Compare-exchange partners closer
-  // than a wave are reached with lane shuffles; only the three steps whose
-  // partner lies in another wave go through LDS.
   uint64_t key = valid ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(tid))
                        : ~0ull;
-#pragma unroll
-  for (int k = 2; k <= kAcceptThreads; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t other;
-      if (j >= kWave) {
-        if (part) s_key[tid] = key;
-        __syncthreads();
-        other = part ? s_key[tid ^ j] : key;
-        __syncthreads();
-      } else {
-        other = key_xor(key, j);
-      }
-      const bool ascending = (tid & k) == 0;
-      const bool lower = (tid & j) == 0;
-      const uint64_t lo = key < other ? key : other;
-      const uint64_t hi = key < other ? other : key;
-      key = (lower == ascending) ? lo : hi;
+  // Only entropies <= b can precede the last accepted position: the
+  // exclusive prefix sum before sorted rank r is at least the entropy at rank
+  // r - 1. So the accepted set is a prefix of the sorted set C = {H <= b},
+  // followed at most by the smallest key outside C. When C holds fewer than
+  // 64 positions (all but the last steps of a run), one wave sorts C alone;
+  // its scan is the full sort's first-wave scan, so both paths give the same
+  // bits. Otherwise the whole canvas is sorted.
+  const bool in_c = valid && h <= a.bound;
+  const uint64_t cmask = __builtin_amdgcn_ballot_w64(in_c);
+  const uint64_t omin_w = ~wave_max_u64(~((valid && !in_c) ? key : ~0ull));
+  if (part && lane == 0) {
+    s_ccount[wave] = __builtin_popcountll(cmask);
+    s_omin[wave] = omin_w;
+  }
+  if (part) s_acc[tid] = 0;
+  __syncthreads();
+  int32_t n_c = 0, c_off = 0;
+  uint64_t omin = ~0ull;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) c_off += s_ccount[w];
+    n_c += s_ccount[w];
+    omin = s_omin[w] < omin ? s_omin[w] : omin;
+  }
+  int32_t kstar;
+  if (n_c < kWave) {
+    if (in_c) {
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cmask >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cmask), 0));
+      s_key[c_off + below] = key;
     }
+    __syncthreads();
+    if (wave == 0) {
+      // lanes 0..n_c-1: C's keys; lane n_c: the smallest key outside C (all
+      // of C's keys are below it); the rest empty
+      uint64_t k2 = lane < n_c ? s_key[lane] : (lane == n_c ? omin : ~0ull);
+#pragma unroll
+      for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          const uint64_t other = key_xor(k2, j);
+          const bool ascending = (lane & k) == 0;
+          const bool lower = (lane & j) == 0;
+          const uint64_t lo = k2 < other ? k2 : other;
+          const uint64_t hi = k2 < other ? other : k2;
+          k2 = (lower == ascending) ? lo : hi;
+        }
+      }
+      const bool real = k2 != ~0ull;
+      const double hs = real ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(k2 >> 32))) : 0.0;
+      double incl = hs;
+      incl += shifted_in_row<0x111>(incl);
+      incl += shifted_in_row<0x112>(incl);
+      incl += shifted_in_row<0x114>(incl);
+      incl += shifted_in_row<0x118>(incl);
+      {
+        const double t0 = read_lane_f64(incl, 15), t1 = read_lane_f64(incl, 31), t2 = read_lane_f64(incl, 47);
+        const int row = lane >> 4;
+        incl += row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+      }
+      const bool ok = real && (incl - hs) <= static_cast<double>(a.bound);
+      // the rank after the smallest key outside C (rank n_c + 1, which may lie
+      // past the last lane) is never acceptable: its prefix holds an entropy
+      // above b; nor is an empty lane
+      int32_t first_bad = (real && !ok) || !real ? lane : L;
+      first_bad = wave_min_int(first_bad);
+      const int32_t ks = min(first_bad, min(n_c + 1, L));
+      if (real && lane < ks) s_acc[static_cast<uint32_t>(k2)] = 1;
+      if (lane == 0) s_kstar = ks;
+    }
+    __syncthreads();
+    kstar = s_kstar;
+  } else {
+    // bitonic sort of 256 keys, ascending. Compare-exchange partners closer
+    // than a wave are reached with lane shuffles; only the three steps whose
+    // partner lies in another wave go through LDS.
+#pragma unroll
+    for (int k = 2; k <= kAcceptThreads; k <<= 1) {
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint64_t other;
+        if (j >= kWave) {
+          if (part) s_key[tid] = key;
+          __syncthreads();
+          other = part ? s_key[tid ^ j] : key;
+          __syncthreads();
+        } else {
+          other = key_xor(key, j);
+        }
+        const bool ascending = (tid & k) == 0;
+        const bool lower = (tid & j) == 0;
+        const uint64_t lo = key < other ? key : other;
+        const uint64_t hi = key < other ? other : key;
+        key = (lower == ascending) ? lo : hi;
+      }
+    }
+
+    // inclusive fp64 scan of sorted entropies: rows of 16 lanes by DPP shifts,
+    // then row offsets, then wave offsets
+    const double hs = valid ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(key >> 32))) : 0.0;
+    double incl = hs;
+    incl += shifted_in_row<0x111>(incl);
+    incl += shifted_in_row<0x112>(incl);
+    incl += shifted_in_row<0x114>(incl);
+    incl += shifted_in_row<0x118>(incl);
+    {
+      const double t0 = read_lane_f64(incl, 15), t1 = read_lane_f64(incl, 31), t2 = read_lane_f64(incl, 47);
+      const int row = lane >> 4;
+      incl += row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+    }
+    if (part && lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    for (int w = 0; w < wave && w < kWaves; ++w) incl += s_wsum[w];
+
+    // first sorted index that is not acceptable; k* = that index (or L)
+    const bool ok = valid && (incl - hs) <= static_cast<double>(a.bound);
+    int32_t first_bad = (valid && !ok) ? tid : L;
+    first_bad = wave_min_int(first_bad);
+    __syncthreads();
+    if (part && lane == 0) s_wmin[wave] = first_bad;
+    __syncthreads();
+    kstar = s_wmin[0];
+    for (int w = 1; w < kWaves; ++w) kstar = min(kstar, s_wmin[w]);
+    if (valid) s_acc[static_cast<uint32_t>(key)] = static_cast<uint8_t>(tid < kstar);
+    __syncthreads();  // accept flags scattered by position (the one-wave path's are published above)
   }
-
-  // inclusive fp64 scan of sorted entropies: rows of 16 lanes by DPP shifts,
-  // then row offsets, then wave offsets
-  const double hs = valid ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(key >> 32))) : 0.0;
-  double incl = hs;
-  incl += shifted_in_row<0x111>(incl);
-  incl += shifted_in_row<0x112>(incl);
-  incl += shifted_in_row<0x114>(incl);
-  incl += shifted_in_row<0x118>(incl);
-  {
-    const double t0 = read_lane_f64(incl, 15), t1 = read_lane_f64(incl, 31), t2 = read_lane_f64(incl, 47);
-    const int row = lane >> 4;
-    incl += row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
-  }
-  if (part && lane == kWave - 1) s_wsum[wave] = incl;
-  __syncthreads();
-  for (int w = 0; w < wave && w < kWaves; ++w) incl += s_wsum[w];
-
-  // first sorted index that is not acceptable; k* = that index (or L)
-  const bool ok = valid && (incl - hs) <= static_cast<double>(a.bound);
-  int32_t first_bad = (valid && !ok) ? tid : L;
-  first_bad = wave_min_int(first_bad);
-  __syncthreads();
-  if (part && lane == 0) s_wmin[wave] = first_bad;
-  __syncthreads();
-  int32_t kstar = s_wmin[0];
-  for (int w = 1; w < kWaves; ++w) kstar = min(kstar, s_wmin[w]);
-  if (valid) s_acc[static_cast<uint32_t>(key)] = static_cast<uint8_t>(tid < kstar);
-
   double total = 0.0;
   int all_same = 1;
   for (int w = 0; w < kWaves; ++w) {
@@ -188,7 +267,6 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
     all_same &= s_same[w];
   }
   const double mean_h = total / static_cast<double>(L);
-  __syncthreads();  // accept flags scattered by position
 
   if (valid) {
     const bool accepted = s_acc[tid] != 0;

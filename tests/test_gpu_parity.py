@@ -237,13 +237,25 @@ def _accept_case(rng, L, kind):
         return np.zeros(L, dtype=np.float32)
     if kind == "equal_small":
         return np.full(L, np.float32(0.03125))
+    if kind.startswith("c"):
+        # n positions at or below the bound b = 0.1, the rest above it: the
+        # acceptance's one-wave path holds up to 63 such positions, the full
+        # sort takes over from 64. "cN" spreads the small ones up to b, so the
+        # prefix stops inside them; "cN_all" makes them tiny, so the prefix
+        # runs through all of them and takes the smallest entropy above b too
+        n = min(int(kind[1:].split("_")[0]), L)
+        h = (1.0 + rng.random(L)).astype(np.float32)
+        small = rng.choice(L, size=n, replace=False)
+        h[small] = (rng.random(n) * (1e-5 if kind.endswith("_all") else 0.1)).astype(np.float32)
+        return h
     raise ValueError(kind)
 
 
 @pytest.mark.parametrize("L", [256, 100, 1])
 def test_accept_renoise_stop_exact_from_given_entropies(L):
     V = 262144
-    kinds = ["random", "ties", "uniform", "zeros", "equal_small", "random"]
+    kinds = ["random", "ties", "uniform", "zeros", "equal_small", "random", "c63", "c64", "c65", "c63_all",
+             "c64_all", "c1_all"]
     Bn = len(kinds)
     ctx = _ctx(L, V, max_batch=Bn)
     rng = np.random.default_rng(L)
@@ -252,7 +264,7 @@ def test_accept_renoise_stop_exact_from_given_entropies(L):
     prev = am.copy()
     prev[1, 0] ^= 1                          # canvas 1 not stable
     smp = rng.integers(0, V, size=(Bn, L)).astype(np.int32)
-    seeds = [11, 12, 13, 14, 15, 2**63]
+    seeds = [11, 12, 13, 14, 15, 2**63, 16, 17, 18, 19, 20, 21]
     step = 5
     dev = lambda a, dt: torch.as_tensor(a, dtype=dt, device="cuda")
     canvas = torch.full((Bn, L), -1, dtype=torch.int32, device="cuda")
