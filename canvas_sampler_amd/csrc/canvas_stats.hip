@@ -40,11 +40,14 @@
 // its stream the wave draws the sample in its best block and finds the first
 // id of its maximum from the parked logits. The workgroup then merges eight
 // 40-byte partials. A row split over several workgroups (for very short
-// batches) is merged by the last workgroup to finish (atomic ticket,
-// release/acquire at agent scope).
+// batches) writes one partial per split.
 //
 // partials_merge_kernel merges, one wave per row and in a fixed order, the
-// per-tile partials that the LM-head product's statistics epilogue writes.
+// partials of split rows and the per-tile partials that the LM-head
+// product's statistics epilogue writes. It runs as the next kernel on the
+// stream: the kernel boundary orders the partials' stores before its loads,
+// so no atomic ticket or agent-scope fence is needed (those cost about 24 us
+// per launch at two splits per row).
 #include <type_traits>
 
 #include "device_common.h"
@@ -827,17 +830,9 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   if (lane != 0) return;
 
   if (a.nsplit > 1) {
-    // the last workgroup of the row (atomic ticket, release/acquire at agent
-    // scope) merges every split's partial
+    // a split's partial; partials_merge_kernel, next on the stream, merges them
     a.partials[static_cast<int64_t>(r) * a.nsplit + split] = p;
-    __threadfence();
-    const uint32_t prev = __hip_atomic_fetch_add(&a.tickets[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev != static_cast<uint32_t>(a.nsplit - 1)) return;
-    __hip_atomic_store(&a.tickets[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const RowPartial* parts = a.partials + static_cast<int64_t>(r) * a.nsplit;
-    p = parts[0];
-    for (int sidx = 1; sidx < a.nsplit; ++sidx) merge_partial(p, parts[sidx]);
+    return;
   }
   row_output(a, r, p);
 }
@@ -1053,19 +1048,18 @@ hipError_t launch_partials_merge(const StatsArgs& a, const RowPartial* partials,
 
 int32_t choose_nsplit(int32_t rows, int32_t vocab) {
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
-  // Split only while the split workgroups stay within about half of the 256
-  // CUs: the agent-scope fences of the merge cost a few microseconds per
-  // workgroup, and a workgroup streams a row at a bounded rate. Measured at
-  // V = 262144 bf16 (one / two workgroups per row): L = 16 20.4 / 16.5 us,
-  // L = 64 22.1 / 20.3 us, L = 96 22.3 / 23.4 us, L = 128 22.5 / 27.5 us.
-  // At most one split per 32 chunks: splits start at multiples of 32 chunks,
-  // where the groups of four block draws start.
-  int32_t want = 128 / rows;
+  // Split a row over two workgroups while the splits stay within the 256
+  // CUs' one resident workgroup each: the splits' partials are merged by the
+  // next kernel on the stream. Measured at V = 262144 bf16, statistics and
+  // merge, one / two / four workgroups per row: L = 16 21.5 / 18.3 / 18.8 us,
+  // L = 32 22.0 / 18.3 / 18.7 us, L = 64 22.2 / 18.7 / 19.4 us, L = 128
+  // 22.5 / 21.3 / 33.2 us, L = 256 26.5 / 36.0 / 60.4 us. At most one split
+  // per 32 chunks: splits start at multiples of 32 chunks, where the groups of
+  // four block draws start.
+  int32_t want = rows <= 128 ? 2 : 1;
   int32_t cap = nchunk / kDrawGroupChunks;
   if (cap < 1) cap = 1;
-  if (want > cap) want = cap;
-  if (want > 8) want = 8;
-  return want < 1 ? 1 : want;
+  return want > cap ? cap : want;
 }
 
 int32_t stats_row_grid(int32_t rows, int32_t vocab, int32_t nsplit, bool has_active, int32_t cu_count) {

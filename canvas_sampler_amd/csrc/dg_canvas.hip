@@ -23,7 +23,6 @@ struct dg_ctx {
   int32_t cu_count = 0;                 // compute units of the device
   // device scratch
   dg::RowPartial* partials = nullptr;   // [max_rows * nsplit_max]
-  uint32_t* tickets = nullptr;          // [max_rows], zero between launches
   float* entropy = nullptr;             // [max_rows]
   int32_t* argmax[2] = {nullptr, nullptr};
   int32_t* sample = nullptr;
@@ -159,7 +158,6 @@ struct StepScratch {
   int32_t nsplit;
   int32_t cu_count;
   dg::RowPartial* partials;
-  uint32_t* tickets;
 };
 
 dg::StatsArgs make_stats_args(const dg_params& p, const StepScratch& sc, int32_t B, const void* logits,
@@ -182,7 +180,6 @@ dg::StatsArgs make_stats_args(const dg_params& p, const StepScratch& sc, int32_t
   a.argmax = argmax;
   a.sample = sample;
   a.partials = sc.partials;
-  a.tickets = sc.tickets;
   a.row_grid = dg::stats_row_grid(a.rows, a.vocab, a.nsplit, active != nullptr, sc.cu_count);
   return a;
 }
@@ -191,7 +188,7 @@ dg::StatsArgs stats_args(const dg_ctx* ctx, int32_t B, const void* logits, int64
                          const float* temperature, int32_t step, const int32_t* steps,
                          const uint64_t* seeds, const uint8_t* active, float* entropy, int32_t* argmax,
                          int32_t* sample) {
-  const StepScratch sc{effective_nsplit(ctx, B * ctx->p.canvas_len), ctx->cu_count, ctx->partials, ctx->tickets};
+  const StepScratch sc{effective_nsplit(ctx, B * ctx->p.canvas_len), ctx->cu_count, ctx->partials};
   return make_stats_args(ctx->p, sc, B, logits, row_stride, temperature, step, steps, seeds, active, entropy,
                          argmax, sample);
 }
@@ -203,6 +200,7 @@ dg_status enqueue_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dty
   const dg::StatsArgs a = stats_args(ctx, B, logits, row_stride, temperature, step, steps, seeds, active,
                                      entropy, argmax, sample);
   DG_CHECK_HIP(ctx, dg::launch_canvas_stats(a, dtype == DG_DTYPE_BF16, stream));
+  if (a.nsplit > 1) DG_CHECK_HIP(ctx, dg::launch_partials_merge(a, a.partials, a.nsplit, stream));
   return DG_OK;
 }
 
@@ -345,7 +343,6 @@ hipError_t dev_alloc(T** p, size_t n) {
 void free_ctx(dg_ctx* c) {
   if (!c) return;
   hipFree(c->partials);
-  hipFree(c->tickets);
   hipFree(c->entropy);
   hipFree(c->argmax[0]);
   hipFree(c->argmax[1]);
@@ -431,7 +428,7 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
   c->p = *params;
   const size_t rows = static_cast<size_t>(max_batch) * params->canvas_len;
   bool ok = dev_alloc(&c->partials, rows * c->nsplit_max) == hipSuccess &&
-            dev_alloc(&c->tickets, rows) == hipSuccess && dev_alloc(&c->entropy, rows) == hipSuccess &&
+            dev_alloc(&c->entropy, rows) == hipSuccess &&
             dev_alloc(&c->argmax[0], rows) == hipSuccess && dev_alloc(&c->argmax[1], rows) == hipSuccess &&
             dev_alloc(&c->sample, rows) == hipSuccess && dev_alloc(&c->canvas, rows) == hipSuccess &&
             dev_alloc(&c->finished, rows) == hipSuccess && dev_alloc(&c->seeds, max_batch) == hipSuccess &&
@@ -458,11 +455,6 @@ dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params
     free_ctx(c);
     (void)hipGetLastError();
     return set_err(nullptr, DG_ERR_OUT_OF_MEMORY, "could not allocate scratch for max_batch = %d", max_batch);
-  }
-  if (hipMemset(c->tickets, 0, rows * sizeof(uint32_t)) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
-    free_ctx(c);
-    return set_err(nullptr, DG_ERR_DEVICE, "could not clear the ticket scratch");
   }
   *out = c;
   return DG_OK;
@@ -918,7 +910,7 @@ dg_status dg_tokens_per_forward(const int32_t* steps_used, int32_t n_canvases, i
 
 // ---- One step that allocates nothing (dg_sampler_step_noalloc) ----
 //
-// The step's intermediate statistics, split-row partials and tickets live in
+// The step's intermediate statistics and split-row partials live in
 // `scratch`, a static array of device memory that every GPU the library runs
 // on holds until the process ends. Host code never passes the array's name to
 // a kernel: on the host that name is a stand-in, not a device address. Its
@@ -929,13 +921,11 @@ namespace {
 
 constexpr int32_t kNoAllocMaxRows = 16384;     // B * L at most: 64 canvases of 256 positions
 constexpr int32_t kNoAllocMaxPartials = 256;   // split rows: rows * nsplit <= 128 when nsplit > 1
-constexpr int32_t kNoAllocMaxTickets = 256;
 constexpr size_t kNoAllocEntropyOff = 0;
 constexpr size_t kNoAllocArgmaxOff = kNoAllocEntropyOff + sizeof(float) * kNoAllocMaxRows;
 constexpr size_t kNoAllocSampleOff = kNoAllocArgmaxOff + sizeof(int32_t) * kNoAllocMaxRows;
 constexpr size_t kNoAllocPartialOff = kNoAllocSampleOff + sizeof(int32_t) * kNoAllocMaxRows;
-constexpr size_t kNoAllocTicketOff = kNoAllocPartialOff + sizeof(dg::RowPartial) * kNoAllocMaxPartials;
-constexpr size_t kNoAllocBytes = kNoAllocTicketOff + sizeof(uint32_t) * kNoAllocMaxTickets;
+constexpr size_t kNoAllocBytes = kNoAllocPartialOff + sizeof(dg::RowPartial) * kNoAllocMaxPartials;
 static_assert(kNoAllocPartialOff % 256 == 0, "partials stay 256-byte aligned");
 
 }  // namespace
@@ -1005,20 +995,18 @@ dg_status dg_sampler_step_noalloc(const dg_params* params, int32_t B, const void
   if ((st = noalloc_device(&d)) != DG_OK) return st;
   const int32_t rows = B * p.canvas_len;
   int32_t nsplit = dg::choose_nsplit(rows, p.vocab);
-  if (nsplit > 1 && (static_cast<int64_t>(rows) * nsplit > kNoAllocMaxPartials || rows > kNoAllocMaxTickets))
+  if (nsplit > 1 && static_cast<int64_t>(rows) * nsplit > kNoAllocMaxPartials)
     return set_err(nullptr, DG_ERR_DEVICE, "split of %d rows over %d workgroups exceeds the static scratch "
                    "(internal error)", rows, nsplit);
-  StepScratch sc{nsplit, d.cu_count, reinterpret_cast<dg::RowPartial*>(d.base + kNoAllocPartialOff),
-                 reinterpret_cast<uint32_t*>(d.base + kNoAllocTicketOff)};
+  StepScratch sc{nsplit, d.cu_count, reinterpret_cast<dg::RowPartial*>(d.base + kNoAllocPartialOff)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ent = out->entropy_out ? out->entropy_out : reinterpret_cast<float*>(d.base + kNoAllocEntropyOff);
   int32_t* am = out->argmax_out ? out->argmax_out : reinterpret_cast<int32_t*>(d.base + kNoAllocArgmaxOff);
   int32_t* smp = out->sample_out ? out->sample_out : reinterpret_cast<int32_t*>(d.base + kNoAllocSampleOff);
-  // the split merge counts arrivals from zero: start every call from cleared tickets
-  if (nsplit > 1) DG_CHECK_HIP(nullptr, dg::launch_fill_u32(sc.tickets, rows, 0u, s));
   const dg::StatsArgs a = make_stats_args(p, sc, B, logits, row_stride, temperature, step, nullptr, seeds, active,
                                           ent, am, smp);
   DG_CHECK_HIP(nullptr, dg::launch_canvas_stats(a, dtype == DG_DTYPE_BF16, s));
+  if (a.nsplit > 1) DG_CHECK_HIP(nullptr, dg::launch_partials_merge(a, a.partials, a.nsplit, s));
   const dg::AcceptArgs acc = make_accept_args(p, ent, am, smp, step, nullptr, seeds, prev_argmax, active, out, false);
   DG_CHECK_HIP(nullptr, dg::launch_accept_renoise(acc, B, s));
   return DG_OK;

@@ -72,8 +72,7 @@ struct StatsArgs {
   float* entropy;
   int32_t* argmax;
   int32_t* sample;
-  RowPartial* partials;    // [rows * nsplit] when nsplit > 1
-  uint32_t* tickets;       // [rows], zero between launches
+  RowPartial* partials;    // [rows * nsplit] when nsplit > 1: merged by launch_partials_merge
   int32_t row_grid;        // > 0: a persistent grid of this many workgroups loops over the rows
 };
 

@@ -121,7 +121,7 @@ dg_status dg_params_check(const dg_params* p);
 
 /* Creates a context on HIP device `device` for batches of up to max_batch
  * canvases (1..65536) with parameters *params (copied). Allocates the device
- * scratch (per-row partials, tickets, argmax ping-pong buffers) and a small
+ * scratch (per-row partials, argmax ping-pong buffers) and a small
  * pinned host buffer. On failure *out is set to NULL and the message is
  * available from dg_last_error(NULL). */
 dg_status dg_create(dg_ctx** out, int device, int32_t max_batch, const dg_params* params);
