@@ -171,7 +171,13 @@ dg_status dg_canvas_init(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t*
  *   temperature  device, fp32 [B], each > 0 and finite
  *   step         >= 0 (enters the random counters)
  *   seeds        device, uint64 [B]
- *   active       device, uint8 [B] (0 = skip canvas) or NULL = all active
+ *   active       device, uint8 [B] (0 = skip canvas) or NULL = all active.
+ *                The kernels read each flag through the aligned 32-bit word
+ *                that holds it (a scalar load), so they may read up to 3
+ *                bytes before the array's start and 3 after its end, all
+ *                inside the same 4-byte-aligned words; the array must lie in
+ *                readable device memory that those words cover (any device
+ *                allocation does), and the extra bytes are never used
  *   entropy, argmax, sample  device outputs [B*L]; none may be NULL */
 dg_status dg_canvas_stats(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype dtype,
                           int64_t row_stride, const float* temperature, int32_t step,
