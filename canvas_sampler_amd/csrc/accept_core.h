@@ -3,8 +3,11 @@
 //
 // One thread per position, kAcceptThreads (256) positions at most:
 //   - only positions with H <= b can come before the last accepted one, so
-//     when fewer than 64 have it, one wave sorts those alone (plus the
-//     smallest key above b); otherwise:
+//     when fewer than 64 have it (every wave counts them from the whole
+//     canvas's entropies, which each wave loads), wave 0 sorts those alone
+//     (plus the smallest key above b) with the smallest bitonic network that
+//     holds them, while the other waves draw the renoise tokens, and a
+//     single barrier ends the step; otherwise:
 //   - sort the L keys (entropy bits << 32 | position) ascending with a
 //     bitonic network, in-wave steps by DPP and permlane swaps (no LDS round
 //     trip) and the cross-wave steps through LDS (entropies are >= +0, so
@@ -64,12 +67,15 @@ __device__ __forceinline__ double read_lane_f64(double v, int lane) {
 
 // Per-thread inputs of accept_canvas, loaded by the caller up front so that
 // every load of the kernel is in flight at once: position t's entropy,
-// argmax, sample and previous argmax (t < L), and the canvas's seed and step.
+// argmax, sample and previous argmax (t < L), the canvas's seed and step,
+// and the entropies of positions 4 (t % 64) .. +3, so that every wave holds
+// the whole canvas's entropies.
 struct AcceptInputs {
   float h = 0.0f;
   int32_t am = 0, smp = 0, prev = 0;
   uint64_t seed = 0;
   int32_t step = 0;
+  float hv[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // entropies of positions 4 (t % 64) + i (every wave holds all)
 };
 
 // Issues every load accept_canvas needs for thread t of `canvas`.
@@ -81,6 +87,12 @@ __device__ __forceinline__ AcceptInputs load_accept_inputs(const AcceptArgs& a, 
     in.am = a.argmax[at];
     in.smp = a.sample[at];
     if (a.prev_argmax != nullptr) in.prev = a.prev_argmax[at];
+  }
+  const int lane = t & (kWave - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 4 * lane + i;
+    if (p < a.canvas_len) in.hv[i] = a.entropy[static_cast<int64_t>(canvas) * a.canvas_len + p];
   }
   in.seed = a.seeds[canvas];
   in.step = a.steps != nullptr ? a.steps[canvas] : a.step;
@@ -101,8 +113,7 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   __shared__ int32_t s_same[kWaves];
   __shared__ int32_t s_wmin[kWaves];
   __shared__ uint8_t s_acc[kAcceptThreads];
-  __shared__ int32_t s_ccount[kWaves];
-  __shared__ uint64_t s_omin[kWaves];
+  __shared__ int32_t s_ren[kWave];
   __shared__ int32_t s_kstar;
 
   const int tid = threadIdx.x;
@@ -115,9 +126,8 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
   const float h = in.h;
   const int32_t am = in.am, smp = in.smp;
 
-  // Independent of the order: mean entropy (fp64, in position order), argmax
-  // stability and the renoise token. Formed before the sort so that they
-  // overlap it; the per-wave parts are published by the sort's LDS barriers.
+  // Independent of the order: mean entropy (fp64, in position order) and
+  // argmax stability, published by the last barrier of either path.
   double hsum = valid ? static_cast<double>(h) : 0.0;
   hsum = wave_sum(hsum);
   const bool same = !valid || (a.prev_argmax != nullptr && in.prev == am);
@@ -126,52 +136,62 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
     s_hsum[wave] = hsum;
     s_same[wave] = wave_same ? 1 : 0;
   }
-  int32_t renoise = 0;
-  if (valid) {
-    const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(tid), static_cast<uint32_t>(in.step),
+  auto renoise_of = [&](int pos) -> int32_t {
+    const Words4 rw = philox4x32_10(0u, static_cast<uint32_t>(pos), static_cast<uint32_t>(in.step),
                                     kTagRenoise, static_cast<uint32_t>(in.seed),
                                     static_cast<uint32_t>(in.seed >> 32));
-    renoise = uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
-  }
-  uint64_t key = valid ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(tid))
-                       : ~0ull;
+    return uniform_token(rw.w[0], static_cast<uint32_t>(a.vocab));
+  };
   // Only entropies <= b can precede the last accepted position: the
   // exclusive prefix sum before sorted rank r is at least the entropy at rank
   // r - 1. So the accepted set is a prefix of the sorted set C = {H <= b},
-  // followed at most by the smallest key outside C. When C holds fewer than
-  // 64 positions (all but the last steps of a run), one wave sorts C alone;
-  // its scan is the full sort's first-wave scan, so both paths give the same
-  // bits. Otherwise the whole canvas is sorted.
-  const bool in_c = valid && h <= a.bound;
-  const uint64_t cmask = __builtin_amdgcn_ballot_w64(in_c);
-  const uint64_t omin_w = ~wave_max_u64(~((valid && !in_c) ? key : ~0ull));
-  if (part && lane == 0) {
-    s_ccount[wave] = __builtin_popcountll(cmask);
-    s_omin[wave] = omin_w;
-  }
-  if (part) s_acc[tid] = 0;
-  __syncthreads();
-  int32_t n_c = 0, c_off = 0;
-  uint64_t omin = ~0ull;
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) c_off += s_ccount[w];
-    n_c += s_ccount[w];
-    omin = s_omin[w] < omin ? s_omin[w] : omin;
+  // followed at most by the smallest key outside C. Every wave counts C from
+  // the canvas-wide entropies it holds, so all of them take the same path
+  // without a barrier. When C holds fewer than 64 positions (all but the last
+  // steps of a run), wave 0 sorts C alone while the other waves draw the
+  // renoise tokens, and one barrier ends the step; its scan is the full
+  // sort's first-wave scan, so both paths give the same bits. Otherwise the
+  // whole canvas is sorted.
+  uint64_t cball[4];
+  int32_t n_c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 4 * lane + i;
+    cball[i] = __builtin_amdgcn_ballot_w64(p < L && in.hv[i] <= a.bound);
+    n_c += __builtin_popcountll(cball[i]);
   }
   int32_t kstar;
+  int32_t renoise = 0;
   if (n_c < kWave) {
-    if (in_c) {
-      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cmask >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cmask), 0));
-      s_key[c_off + below] = key;
-    }
-    __syncthreads();
     if (wave == 0) {
-      // lanes 0..n_c-1: C's keys; lane n_c: the smallest key outside C (all
-      // of C's keys are below it); the rest empty
+      // lanes 0..n_c-1: C's keys (placed through LDS by this wave alone);
+      // lane n_c: the smallest key outside C (all of C's keys are below it);
+      // the rest empty
+      uint64_t outside = ~0ull;
+      int32_t off = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = 4 * lane + i;
+        const uint64_t k = (static_cast<uint64_t>(__float_as_uint(in.hv[i])) << 32) | static_cast<uint32_t>(p);
+        const bool in_c = ((cball[i] >> lane) & 1) != 0;
+        if (in_c) {
+          const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cball[i] >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cball[i]), 0));
+          s_key[off + below] = k;
+        } else if (p < L) {
+          outside = k < outside ? k : outside;
+        }
+        off += __builtin_popcountll(cball[i]);
+        if (p < kAcceptThreads) s_acc[p] = 0;
+      }
+      const uint64_t omin = ~wave_max_u64(~outside);
       uint64_t k2 = lane < n_c ? s_key[lane] : (lane == n_c ? omin : ~0ull);
+      // bitonic sort of the first m lanes, m the smallest power of two above
+      // n_c (lanes m.. hold empty keys, so the result is the full network's)
+      const int m = n_c == 0 ? 1 : 1 << (32 - __builtin_clz(static_cast<uint32_t>(n_c)));
 #pragma unroll
       for (int k = 2; k <= kWave; k <<= 1) {
+        if (k > m) break;
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
           const uint64_t other = key_xor(k2, j);
@@ -203,10 +223,19 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
       const int32_t ks = min(first_bad, min(n_c + 1, L));
       if (real && lane < ks) s_acc[static_cast<uint32_t>(k2)] = 1;
       if (lane == 0) s_kstar = ks;
+    } else {
+      // the renoise tokens: each wave its own positions, wave 1 also wave 0's
+      if (valid) renoise = renoise_of(tid);
+      if (wave == 1 && lane < L) s_ren[lane] = renoise_of(lane);
     }
     __syncthreads();
+    if (wave == 0 && valid) renoise = s_ren[lane];
     kstar = s_kstar;
   } else {
+    if (valid) renoise = renoise_of(tid);
+    uint64_t key = valid ? ((static_cast<uint64_t>(__float_as_uint(h)) << 32) | static_cast<uint32_t>(tid))
+                         : ~0ull;
+    if (part) s_acc[tid] = 0;
     // bitonic sort of 256 keys, ascending. Compare-exchange partners closer
     // than a wave are reached with lane shuffles; only the three steps whose
     // partner lies in another wave go through LDS.
@@ -258,7 +287,7 @@ __device__ __forceinline__ void accept_canvas(const AcceptArgs& a, int32_t canva
     kstar = s_wmin[0];
     for (int w = 1; w < kWaves; ++w) kstar = min(kstar, s_wmin[w]);
     if (valid) s_acc[static_cast<uint32_t>(key)] = static_cast<uint8_t>(tid < kstar);
-    __syncthreads();  // accept flags scattered by position (the one-wave path's are published above)
+    __syncthreads();  // accept flags scattered by position
   }
   double total = 0.0;
   int all_same = 1;
