@@ -254,8 +254,10 @@ def _accept_case(rng, L, kind):
 @pytest.mark.parametrize("L", [256, 100, 1])
 def test_accept_renoise_stop_exact_from_given_entropies(L):
     V = 262144
+    # c15/c16, c31/c32: the one-wave path's sorting network grows at 16 and
+    # 32 keys (the candidates plus the smallest key above b)
     kinds = ["random", "ties", "uniform", "zeros", "equal_small", "random", "c63", "c64", "c65", "c63_all",
-             "c64_all", "c1_all"]
+             "c64_all", "c1_all", "c1", "c15", "c16", "c31", "c32", "c15_all", "c16_all", "c31_all", "c32_all"]
     Bn = len(kinds)
     ctx = _ctx(L, V, max_batch=Bn)
     rng = np.random.default_rng(L)
@@ -264,7 +266,7 @@ def test_accept_renoise_stop_exact_from_given_entropies(L):
     prev = am.copy()
     prev[1, 0] ^= 1                          # canvas 1 not stable
     smp = rng.integers(0, V, size=(Bn, L)).astype(np.int32)
-    seeds = [11, 12, 13, 14, 15, 2**63, 16, 17, 18, 19, 20, 21]
+    seeds = [11, 12, 13, 14, 15, 2**63, 16, 17, 18, 19, 20, 21] + list(range(22, 22 + Bn - 12))
     step = 5
     dev = lambda a, dt: torch.as_tensor(a, dtype=dt, device="cuda")
     canvas = torch.full((Bn, L), -1, dtype=torch.int32, device="cuda")
