@@ -41,8 +41,8 @@ def test_noalloc_step_equals_sampler_step_on_two_calls():
     require_gpu()
     # first a large call (3 canvases x 256 rows, ragged V, one workgroup per
     # row), then a smaller one (one canvas of 40 rows: each row split over
-    # three workgroups, so the static partials and tickets are used), then
-    # the large one again
+    # two workgroups, so the static partials and the merge kernel are used),
+    # then the large one again
     cases = [(256, 70001 + 7, 3, torch.bfloat16, 11, 4), (40, 4096 * 96, 1, torch.float32, 23, 2),
              (256, 70001 + 7, 3, torch.bfloat16, 11, 4)]
     for L, V, Bn, dtype, gen, step in cases:
