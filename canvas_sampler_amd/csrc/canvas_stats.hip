@@ -17,9 +17,11 @@
 //
 // Layout and schedule (gfx950, wave64): rows are V-contiguous. A workgroup of
 // eight waves handles a row (or one split of it); with more rows than
-// compute units a persistent grid loops over the rows. Wave w streams chunks
-// w, w + 8, ... so the workgroup reads eight consecutive 4096-id chunks at a
-// time. Each lane issues one 16-byte load per 512-id stripe (bf16; two for
+// compute units a persistent grid loops over the rows. In the row loop wave
+// w streams chunks w, w + 8, ... so the workgroup reads eight consecutive
+// 4096-id chunks at a time; in the one-row kernel the two waves of a SIMD
+// share its chunks s + 4p unevenly, the younger wave taking a quarter (the
+// SIMD's arbiter favours the older one). Each lane issues one 16-byte load per 512-id stripe (bf16; two for
 // fp32); a batch is 4 stripes and a block 2 batches, and a register ring
 // holds two blocks: one is reduced while the other is in flight. The loops
 // take the blocks in pairs so that every path into them leaves the two
@@ -30,8 +32,8 @@
 // half a max, one fma, one v_exp_f32, one add and one fma; per block one
 // wave-uniform test for the rare cases, one log2 and two ballots. The block
 // Gumbels: in the one-row kernel each wave draws its own as it goes (one
-// Philox call per four of its blocks, kept as a shift register, no barrier
-// before the stream); in the row loop the workgroup draws those of a whole
+// Philox call per draw group of four chunks, kept in one of two register
+// sets, no barrier before the stream); in the row loop the workgroup draws those of a whole
 // segment of 64 chunks into LDS beforehand (the first while the first loads
 // are in flight, the next ones before the barrier that ends a segment or a
 // row). When a block ends its logits are still in registers, so nothing is
@@ -483,26 +485,88 @@ __device__ __forceinline__ void fill_gumbels(float* g2, int32_t seg0, int32_t cb
   }
 }
 
-// The Gumbels of a wave's own blocks in the one-row kernel, where wave w
-// takes chunks c_begin + w + 8i (c_begin a multiple of 32): its blocks
-// 4m .. 4m + 3 are one group of the draws above, so one Philox call at block
-// 4m gives all four, kept as a shift register (block i takes g0).
-struct WaveGumbels {
-  float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f;
-  __device__ __forceinline__ float take(int32_t i, int32_t chunk, int lane, const RowConsts& rc) {
-    if ((i & 3) == 0) {
-      const Words4 w = philox4x32_10(static_cast<uint32_t>(chunk * kSlots + lane), static_cast<uint32_t>(rc.pos),
+// The one-row kernel's chunk shares. The SIMD that runs waves s and s + 4
+// owns the chunks s + 4p of every 64-chunk stretch (p < 16). Its arbiter
+// favours the older wave (s): with equal shares (the younger wave on the odd
+// p) the older waves end their streams at about 14 us of a 21 us pass and
+// the younger ones stream the rest alone. So the younger wave takes only the
+// positions in kYoungPositions, the older wave the others, each in increasing
+// order. Measured at 256 x 262144 bf16 (statistics pass alone, the same run):
+// 4 of 16 (the draw group of chunks s + 4 + 8q) 25.4-26.0 us against
+// 25.9-26.6 us for equal shares; 5, 6 or a spread 5 of 16 were slower than 4.
+constexpr uint32_t kYoungPositions = (1u << 1) | (1u << 3) | (1u << 5) | (1u << 7);
+
+// The positions p of a 16-bit mask in increasing order, 4 bits each.
+constexpr uint64_t packed_positions(uint32_t mask) {
+  uint64_t r = 0;
+  int n = 0;
+  for (int p = 0; p < 16; ++p)
+    if ((mask >> p) & 1u) r |= static_cast<uint64_t>(p) << (4 * n++);
+  return r;
+}
+
+struct ChunkShare {
+  int32_t c_begin;
+  int sim;        // the SIMD's chunk residue s (wave & 3)
+  uint32_t mask;  // the wave's positions in a stretch
+  uint64_t pos;   // the same, packed
+  int per;        // how many
+  __device__ __forceinline__ ChunkShare(int32_t cb, int wave) : c_begin(cb), sim(wave & 3) {
+    mask = wave >= 4 ? kYoungPositions : (~kYoungPositions & 0xFFFFu);
+    pos = wave >= 4 ? packed_positions(kYoungPositions) : packed_positions(~kYoungPositions & 0xFFFFu);
+    per = __builtin_popcount(mask);
+  }
+  // the chunk of the wave's block i
+  __device__ __forceinline__ int32_t chunk(int32_t i) const {
+    const int32_t k = i / per, n = i - k * per;
+    return c_begin + 64 * k + sim + 4 * static_cast<int32_t>((pos >> (4 * n)) & 15u);
+  }
+  // the wave's blocks in chunks [c_begin, c_end)
+  __device__ __forceinline__ int32_t count(int32_t c_end) const {
+    const int32_t n = c_end - c_begin, full = n >> 6, rem = n & 63;
+    const int32_t P = rem > sim ? (rem - sim + 3) >> 2 : 0;   // positions of the last, partial stretch
+    return per * full + __builtin_popcount(mask & ((1u << P) - 1u));
+  }
+};
+
+// The block Gumbels of a wave under ChunkShare: one Philox call per draw group
+// (chunks c0 + 8q, c0 with bits 3-4 clear; c_begin is a multiple of 32), kept
+// in one of two register sets; a wave's increasing chunks interleave at most
+// two groups (the older wave's second half takes both groups of its residue),
+// so no group is drawn twice.
+struct ShareGumbels {
+  int32_t ga = -1, gb = -1;   // the group in each set
+  bool last_b = true;         // set b served the last block
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+  __device__ __forceinline__ float take(int32_t chunk, int lane, const RowConsts& rc) {
+    const int32_t c0 = chunk & ~0x18;
+    const int q = (chunk >> 3) & 3;
+    bool use_a = c0 == ga;
+    if (!use_a && c0 != gb) {
+      const Words4 w = philox4x32_10(static_cast<uint32_t>(c0 * kSlots + lane), static_cast<uint32_t>(rc.pos),
                                      static_cast<uint32_t>(rc.step), kTagBlock, rc.k0, rc.k1);
-      g0 = kLog2e * gumbel(w.w[0]);
-      g1 = kLog2e * gumbel(w.w[1]);
-      g2 = kLog2e * gumbel(w.w[2]);
-      g3 = kLog2e * gumbel(w.w[3]);
+      const float v0 = kLog2e * gumbel(w.w[0]), v1 = kLog2e * gumbel(w.w[1]);
+      const float v2 = kLog2e * gumbel(w.w[2]), v3 = kLog2e * gumbel(w.w[3]);
+      // the set not used last takes the group; selects, not a branch (a
+      // branch lets the compiler turn the two sets into an indexed array in
+      // scratch memory)
+      use_a = last_b;
+      a0 = use_a ? v0 : a0;
+      a1 = use_a ? v1 : a1;
+      a2 = use_a ? v2 : a2;
+      a3 = use_a ? v3 : a3;
+      b0 = use_a ? b0 : v0;
+      b1 = use_a ? b1 : v1;
+      b2 = use_a ? b2 : v2;
+      b3 = use_a ? b3 : v3;
+      ga = use_a ? c0 : ga;
+      gb = use_a ? gb : c0;
     }
-    const float g = g0;
-    g0 = g1;
-    g1 = g2;
-    g2 = g3;
-    return g;
+    last_b = !use_a;
+    const float x0 = use_a ? a0 : b0, x1 = use_a ? a1 : b1;
+    const float x2 = use_a ? a2 : b2, x3 = use_a ? a3 : b3;
+    return q == 0 ? x0 : q == 1 ? x1 : q == 2 ? x2 : x3;
   }
 };
 
@@ -714,9 +778,9 @@ __device__ __forceinline__ RowConsts row_consts(const StatsArgs& a, int32_t r) {
 
 // One workgroup per row (or per split of a row). NB stripes per batch; the
 // register ring holds RING blocks (one is reduced while the others are in
-// flight). Wave w streams chunks c_begin + w + 8i, so the workgroup reads one
-// stretch of eight consecutive chunks at a time, and draws the Gumbels of its
-// own blocks as it goes (no barrier before the stream starts).
+// flight). The waves share the chunks as ChunkShare says (a SIMD's chunks
+// s + 4p, a quarter of them for its younger wave), and each draws the Gumbels
+// of its own blocks as it goes (no barrier before the stream starts).
 template <bool kBf16, int NB, int RING>
 __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a) {
   constexpr int LPS = Geometry<kBf16>::kLoadsPerStripe;
@@ -740,16 +804,18 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const __amdgpu_buffer_rsrc_t rsrc = row_rsrc<kBf16>(a, r);
   const uint32_t lane_bytes = static_cast<uint32_t>(lane * kSlotIds) * kEB;
 
-  // The split's chunks [c_begin, c_end), cut at multiples of 32 chunks. Wave
-  // w takes chunks c_begin + w + 8i in increasing order; only the row's last
-  // chunk can be partial, and it is the last block of the wave that holds it.
+  // The split's chunks [c_begin, c_end), cut at multiples of 32 chunks. Each
+  // wave takes its share (ChunkShare) in increasing order; only the row's
+  // last chunk can be partial, and it is the last block of the wave that
+  // holds it.
   const int32_t nchunk = (vocab + kChunkIds - 1) / kChunkIds;
   const int32_t ngroup = (nchunk + kDrawGroupChunks - 1) / kDrawGroupChunks;
   const int32_t c_begin = static_cast<int32_t>((static_cast<int64_t>(split) * ngroup) / a.nsplit) * kDrawGroupChunks;
   const int32_t c_end = min(static_cast<int32_t>((static_cast<int64_t>(split + 1) * ngroup) / a.nsplit) *
                             kDrawGroupChunks, nchunk);
-  const int32_t nblk = c_end - c_begin > wave ? (c_end - c_begin - wave + kWaves - 1) / kWaves : 0;
-  auto chunk_of = [&](int32_t i) { return c_begin + wave + kWaves * i; };
+  const ChunkShare cs(c_begin, wave);
+  const int32_t nblk = cs.count(c_end);
+  auto chunk_of = [&](int32_t i) { return cs.chunk(i); };
   auto base_of = [&](int32_t i) { return static_cast<int64_t>(chunk_of(i)) * kChunkIds; };
   // Block i's byte offset for this lane; batches wholly past V point beyond
   // the resource, where buffer loads return zero without touching memory, so
@@ -774,13 +840,13 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   const RowConsts rc = row_consts(a, r);
   LaneState st;
   WaveResult wr;
-  WaveGumbels gw;
+  ShareGumbels gw;
 
   // Full blocks: reduce, close, and refill the ring slot with block i + RING.
   auto run_block = [&](auto slot, int32_t i) {
     constexpr int H = decltype(slot)::value;
     const float bmax = reduce_block<kBf16, NB, H>(buf, base_of(i), vocab, rc.c, st, lane);
-    const float g2 = gw.take(i, chunk_of(i), lane, rc);
+    const float g2 = gw.take(chunk_of(i), lane, rc);
     close_block<kBf16, NB, H>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, g2, st, wr, s_blk[wave],
                               s_amx[wave], lane);
 #pragma unroll
@@ -817,7 +883,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
       const int64_t f = base_of(i) + t * NB * kStripeIds;
       if (f < vocab) bmax = fmaxf(bmax, tail_batch<kBf16, NB>(buf[0][t], f + lane * kSlotIds, vocab, rc.c, st));
     }
-    const float g2 = gw.take(i, chunk_of(i), lane, rc);
+    const float g2 = gw.take(chunk_of(i), lane, rc);
     close_block<kBf16, NB, 0>(buf, base_of(i), chunk_of(i) * kSlots + lane, bmax, g2, st, wr, s_blk[wave],
                               s_amx[wave], lane);
   }
