@@ -17,11 +17,10 @@
 //
 // Layout and schedule (gfx950, wave64): rows are V-contiguous. A workgroup of
 // eight waves handles a row (or one split of it); with more rows than
-// compute units a persistent grid loops over the rows. In the row loop wave
-// w streams chunks w, w + 8, ... so the workgroup reads eight consecutive
-// 4096-id chunks at a time; in the one-row kernel the two waves of a SIMD
-// share its chunks s + 4p unevenly, the younger wave taking a quarter (the
-// SIMD's arbiter favours the older one). Each lane issues one 16-byte load per 512-id stripe (bf16; two for
+// compute units a persistent grid loops over the rows. The two waves of a
+// SIMD share its chunks s + 4p unevenly, the younger wave taking a quarter
+// (the SIMD's arbiter favours the older one), so the workgroup reads nearby
+// 4096-id chunks at any moment. Each lane issues one 16-byte load per 512-id stripe (bf16; two for
 // fp32); a batch is 4 stripes and a block 2 batches, and a register ring
 // holds two blocks: one is reduced while the other is in flight. The loops
 // take the blocks in pairs so that every path into them leaves the two
@@ -930,11 +929,16 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
   const int32_t first_row = static_cast<int32_t>(blockIdx.x);
   const int32_t my_rows = (a.rows - first_row + grid - 1) / grid;  // >= 1
   const int32_t nchunk = vocab / kChunkIds;
-  auto blocks_below = [&](int32_t c) { return c > wave ? (c - wave + kWaves - 1) / kWaves : 0; };
+  // the wave's chunks of a row as in the one-row kernel (ChunkShare); the
+  // segments' Gumbel tables serve any share. Measured (same process, N(0,1)
+  // bf16 rows of 262144): 16 canvases 340.7-340.9 us against 341.1-343.7 with
+  // equal shares, 64 canvases 1.324-1.325 ms against 1.338-1.339.
+  const ChunkShare cs(0, wave);
+  auto blocks_below = [&](int32_t c) { return cs.count(c); };
   const int32_t nblk = blocks_below(nchunk);  // per row
   const int64_t total = static_cast<int64_t>(my_rows) * nblk;
 
-  // Block g of the wave's sequence is block g % nblk (chunk wave + 8 (g % nblk))
+  // Block g of the wave's sequence is block g % nblk (chunk cs.chunk(g % nblk))
   // of row first_row + (g / nblk) * grid; past the sequence, loads read nothing.
   Ring<kBf16, NB, RING> buf;
   auto fetch = [&](auto slot, int64_t g) {
@@ -944,7 +948,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
     const bool live = g < total;
     if (live) {
       r = first_row + static_cast<int32_t>(g / nblk) * grid;
-      byte0 = static_cast<uint32_t>(wave + kWaves * static_cast<int32_t>(g % nblk)) * (kChunkIds * kEB) + lane_bytes;
+      byte0 = static_cast<uint32_t>(cs.chunk(static_cast<int32_t>(g % nblk))) * (kChunkIds * kEB) + lane_bytes;
     }
     load_block<kBf16, NB, H>(buf, row_rsrc<kBf16>(a, r), byte0, live);
   };
@@ -964,7 +968,7 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_rows_kernel(StatsA
     // block i of the row, block gi of the wave's sequence, in ring slot gi % 2
     auto run_block = [&](auto slot, int32_t i, int64_t gi, int32_t seg0) {
       constexpr int H = decltype(slot)::value;
-      const int32_t chunk = wave + kWaves * i;
+      const int32_t chunk = cs.chunk(i);
       const float gv = s_g2[tp][(chunk - seg0) * kSlots + lane];
       const int64_t base = static_cast<int64_t>(chunk) * kChunkIds;
       const float bmax = reduce_block<kBf16, NB, H>(buf, base, vocab, rc.c, st, lane);
