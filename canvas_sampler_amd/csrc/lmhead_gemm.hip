@@ -489,12 +489,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
     // id & 3. The lanes holding a drawn block park its logits in LDS; then
     // each DPP row of 16 lanes takes one drawing row, a lane per 4 ids (one
     // Philox call), so that the work scales with the number of draws.
+    // the draw decisions of the lane's 16 row slots, read at once (draws are
+    // rare, and one read per slot in the loop would wait on each in turn)
+    int udv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) udv[r] = e.draw_u[local_row(r >> 2, r & 3)];
+    bool any_draw = false;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) any_draw = any_draw || udv[r] >= 0;
+    if (__builtin_amdgcn_ballot_w64(any_draw) != 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int lr = local_row(i, q);
-        const int ud = e.draw_u[lr];
+        const int ud = udv[4 * i + q];
         if (__builtin_amdgcn_ballot_w64(ud >= 0) == 0) continue;
         if (ud == u) {
           float* dst = &e.blk[lr][(4 * wn + (n >> 2)) * kSlotIds];
@@ -504,13 +513,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void lmhead_gemm_kernel(GemmArgs g
                                                  : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
         }
       }
+    }
     __syncthreads();
     {
       const int quad = tid & 15;   // ids 4 quad .. 4 quad + 3 of the block: stripe quad / 2
-#pragma unroll 1
-      for (int it = 0; it < kBM / (kGemmThreads / 16); ++it) {
+      constexpr int kIters = kBM / (kGemmThreads / 16);
+      int udr[kIters];
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) udr[it] = e.draw_u[it * (kGemmThreads / 16) + (tid >> 4)];
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
         const int lr = it * (kGemmThreads / 16) + (tid >> 4);
-        const int ud = e.draw_u[lr];
+        const int ud = udr[it];
         if (__builtin_amdgcn_ballot_w64(ud >= 0) == 0) continue;
         float sc = kNegInf;
         int32_t id = 0x7FFFFFFF;
