@@ -17,17 +17,23 @@
 //     v_mfma_f32_32x32x16_bf16 sums them in fp32. Six bf16 products cost
 //     less than a third of one fp32 matrix-core product on this chip;
 //   - a workgroup owns 256 rows (8 waves x 32) and a slice of the vocabulary;
-//   - per 64-id chunk (four 16-id k-steps) the workgroup loads its 256 rows'
+//   - per 64-id chunk (four 16-id k-steps) each wave loads its own 32 rows'
 //     64 logits with whole 128-byte lines per row and instruction (8 lanes per
-//     row), stages them in a padded LDS tile and reads them back in matrix
-//     layout: lane l takes row l % 32, ids 16 t + 8 (l / 32) + 0..7 of k-step
-//     t, one 16-byte read; it turns them into e = 2^(z c - zmax c),
+//     row), stages them in its own padded LDS tile and reads them back in
+//     matrix layout: lane l takes row l % 32, ids 16 t + 8 (l / 32) + 0..7 of
+//     k-step t, one 16-byte read; it turns them into e = 2^(z c - zmax c),
 //     c = log2(e)/T, with zmax the row's largest logit (read at the argmax
-//     the statistics pass found), so e <= 1;
-//   - the chunk's 64 embedding rows are split and staged once per workgroup
-//     in LDS, transposed (column n's 64 values contiguous, three parts), as 32
-//     columns: E[v, 0..d-1], a column of ones at d (its sum is the normaliser
-//     S = sum_v e_v) and zeros above;
+//     the statistics pass found), so e <= 1. No wave waits for another's
+//     tile;
+//   - the embedding rows of four chunks (two for fp32 logits) are split and
+//     staged together in LDS, transposed (column n's 64 values of a chunk
+//     contiguous, three parts), as 32 columns: E[v, 0..d-1], a column of ones
+//     at d (its sum is the normaliser S = sum_v e_v) and zeros above, and
+//     zeros for ids past the slice; the workgroup meets at one barrier per
+//     such group;
+//   - every load is unconditional (clamped addresses), so each wait is for
+//     exactly the data it needs: the next group's embedding and the chunks
+//     two and three ahead stay in flight while a chunk is multiplied;
 //   - one slice per row tile: the workgroup divides by S and writes out;
 //     otherwise it writes its unnormalised partial tile, and a second kernel
 //     sums the slices in a fixed order and divides.
@@ -58,9 +64,10 @@ __device__ __forceinline__ float logit_at(const void* base, int64_t i) {
   }
 }
 
-// Geometry of the staged logits tile of one chunk: 256 rows of 64 ids, each
-// row padded by 16 bytes so that the 16-byte matrix-layout reads of 8
-// consecutive rows fall on distinct banks.
+// Geometry of one wave's staged logits tile of a chunk: the wave's 32 rows of
+// 64 ids, each row padded by 16 bytes so that the 16-byte matrix-layout reads
+// of 8 consecutive rows fall on distinct banks. The wave loads, stores and
+// reads its own tile, so no other wave waits for it.
 template <bool kBf16>
 struct ZTile {
   static constexpr int kElem = kBf16 ? 2 : 4;
@@ -68,9 +75,16 @@ struct ZTile {
   static constexpr int kStride = kRowBytes + 16;
   static constexpr int kPiecesPerRow = kRowBytes / 16;
   static constexpr int kPerPiece = 16 / kElem;
-  static constexpr int kPieces = kScRowTile * kPiecesPerRow / kScThreads;  // per thread
-  static constexpr int kBytes = kScRowTile * kStride;
+  static constexpr int kPieces = 32 * kPiecesPerRow / 64;  // 16-byte pieces per lane
+  static constexpr int kBytes = 32 * kStride;
+  // chunks per staged embedding group: the workgroup meets at one barrier per
+  // group (two LDS slots of kGroup chunks; fp32 tiles leave room for two)
+  static constexpr int kGroup = kBf16 ? 4 : 2;
 };
+
+// One chunk's embedding tile in LDS: three bf16 parts of 32 columns, each
+// column's 64 values contiguous (padded to kScBRow).
+constexpr int kEChunk = 3 * 32 * kScBRow;
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1: the indices are
 // constants from the start, so that arrays indexed by them stay in registers
@@ -95,22 +109,23 @@ struct Raw {
   u32x4_t q[ZTile<kBf16>::kPieces];
 };
 
-// This thread's pieces of a chunk, loaded with whole lines per row: piece
-// p = tid + kScThreads * i is 16-byte piece p % kPiecesPerRow of tile row
-// p / kPiecesPerRow. Every load is unconditional, so that all of them are in
-// flight at once: rows past the batch are clamped onto the last row and ids
-// past the row's stride onto its last piece. What those clamped pieces hold
-// never counts: a row that does not take part has zero probability everywhere
-// (see the kernel), and ids at or past the slice end are masked where the
-// probabilities are formed.
+// This lane's pieces of a chunk of the wave's rows, loaded with whole lines
+// per row and instruction: piece p = lane + 64 i is 16-byte piece
+// p % kPiecesPerRow of wave row p / kPiecesPerRow. Every load is
+// unconditional, so that the number of loads in flight is the same on every
+// path and each wait is for exactly the chunk it needs: rows past the batch
+// are clamped onto the last row and ids past the row's stride onto its last
+// piece. What those clamped pieces hold never counts: a row that does not
+// take part has zero probability everywhere (see the kernel), and ids at or
+// past the slice end meet zero embedding rows.
 template <bool kBf16>
-__device__ __forceinline__ void load_chunk(const SelfCondArgs& a, int32_t row0, int64_t kc, int tid,
+__device__ __forceinline__ void load_chunk(const SelfCondArgs& a, int32_t wrow0, int64_t kc, int lane,
                                            Raw<kBf16>& r) {
   using G = ZTile<kBf16>;
   static_for<G::kPieces>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const int piece = tid + kScThreads * i;
-    const int32_t row = min(row0 + piece / G::kPiecesPerRow, a.rows - 1);
+    const int piece = lane + 64 * i;
+    const int32_t row = min(wrow0 + piece / G::kPiecesPerRow, a.rows - 1);
     int64_t id = kc + static_cast<int64_t>(piece % G::kPiecesPerRow) * G::kPerPiece;
     id = id < a.row_stride - G::kPerPiece ? id : a.row_stride - G::kPerPiece;
     const int64_t off = static_cast<int64_t>(row) * a.row_stride + id;
@@ -122,45 +137,23 @@ __device__ __forceinline__ void load_chunk(const SelfCondArgs& a, int32_t row0, 
 }
 
 template <bool kBf16>
-__device__ __forceinline__ void store_chunk(uint8_t* s_z, int tid, const Raw<kBf16>& r) {
+__device__ __forceinline__ void store_chunk(uint8_t* s_z, int lane, const Raw<kBf16>& r) {
   using G = ZTile<kBf16>;
   static_for<G::kPieces>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const int piece = tid + kScThreads * i;
+    const int piece = lane + 64 * i;
     *reinterpret_cast<u32x4_t*>(s_z + (piece / G::kPiecesPerRow) * G::kStride + (piece % G::kPiecesPerRow) * 16) =
         r.q[i];
   });
-}
-
-// The 8 logits of k-step t of tile row `trow` for this half-wave, as fp32.
-template <bool kBf16>
-__device__ __forceinline__ void read_step(const uint8_t* s_z, int trow, int half, int t, float (&z)[8]) {
-  using G = ZTile<kBf16>;
-  const uint8_t* base = s_z + trow * G::kStride + (16 * t + 8 * half) * G::kElem;
-  if constexpr (kBf16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(base);
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      z[2 * h] = __uint_as_float(u[h] << 16);
-      z[2 * h + 1] = __uint_as_float(u[h] & 0xFFFF0000u);
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint4 w = *reinterpret_cast<const uint4*>(base + 16 * g);
-      z[4 * g + 0] = __uint_as_float(w.x);
-      z[4 * g + 1] = __uint_as_float(w.y);
-      z[4 * g + 2] = __uint_as_float(w.z);
-      z[4 * g + 3] = __uint_as_float(w.w);
-    }
-  }
 }
 
 // Exact three-part split of an fp32 value x = hi + mid + lo into bf16 values,
 // each given as the fp32 pattern whose high 16 bits are that bf16: hi is x
 // truncated to its top 16 bits, mid likewise of r1 = x - hi, and lo = r1 - mid
 // (at most 8 significant bits, so its low 16 bits are already zero).
+// (A split by the packed bf16 conversion, with the residuals as bf16 dot
+// products, takes fewer instructions but runs slower beside the matrix-core
+// products: those dot products compete with them.)
 struct Split3 {
   uint32_t hi, mid, lo;
 };
@@ -180,120 +173,174 @@ __device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// The chunk's embedding tile as this thread stages it: column n = t % 32,
-// ids kc + 4 (t / 32) .. +3 (E[v, n] below d, ones at d, zeros above). The
-// loads are unconditional, with ids clamped onto the last embedding row:
-// ids at or past the slice end get zero probability.
-__device__ __forceinline__ void load_embed(const SelfCondArgs& a, int64_t kc, int tid, float (&ev)[4]) {
+// The embedding values this thread stages for a group of kGroup chunks from
+// id kg: column n = tid % 32 (clamped onto column d - 1; the staging puts the
+// ones and zeros above d), ids kg + 64 c + 4 (tid / 32) .. +3 of chunk c.
+// The loads are unconditional, ids clamped onto the last embedding row; ids
+// at or past the slice end are zeroed when the group is staged.
+template <int kG>
+__device__ __forceinline__ void load_embed(const SelfCondArgs& a, int64_t kg, int tid, float (&ev)[kG][4]) {
   const int n = tid & 31;
   const int nc = n < a.d ? n : a.d - 1;
-  static_for<4>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    int64_t v = kc + 4 * (tid >> 5) + i;
-    v = v < a.vocab ? v : a.vocab - 1;
-    const float e = a.embed[v * a.d + nc];
-    ev[i] = n < a.d ? e : (n == a.d ? 1.0f : 0.0f);
+  static_for<kG>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    static_for<4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      int64_t v = kg + 64 * c + 4 * (tid >> 5) + i;
+      v = v < a.vocab ? v : a.vocab - 1;
+      ev[c][i] = a.embed[v * a.d + nc];
+    });
+  });
+}
+
+// Stages a group's embedding tiles: E[v, n] below d, ones at d, zeros above,
+// and zeros for ids at or past the slice end (so that the probabilities
+// formed there, from clamped or neighbouring logits, never count), split into
+// three parts, column n's 4 ids as one 8-byte write per part.
+template <int kG>
+__device__ __forceinline__ void stage_embed(uint16_t* eb, const SelfCondArgs& a, int64_t kg, int64_t k_end,
+                                            int tid, const float (&ev)[kG][4]) {
+  const int n = tid & 31, sk = 4 * (tid >> 5);
+  static_for<kG>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = n < a.d ? ev[c][i] : (n == a.d ? 1.0f : 0.0f);
+      x[i] = kg + 64 * c + sk + i < k_end ? e : 0.0f;
+    }
+    const Split3 e0 = split3(x[0]), e1 = split3(x[1]), e2 = split3(x[2]), e3 = split3(x[3]);
+    uint16_t* b = eb + c * kEChunk + n * kScBRow + sk;
+    *reinterpret_cast<uint2*>(b) = make_uint2(pack2(e0.hi, e1.hi), pack2(e2.hi, e3.hi));
+    *reinterpret_cast<uint2*>(b + 32 * kScBRow) = make_uint2(pack2(e0.mid, e1.mid), pack2(e2.mid, e3.mid));
+    *reinterpret_cast<uint2*>(b + 64 * kScBRow) = make_uint2(pack2(e0.lo, e1.lo), pack2(e2.lo, e3.lo));
   });
 }
 
 template <bool kBf16>
 __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
-  static_assert(kScThreads == 32 * (kScChunk / 4), "embedding staging covers the tile once");
+  static_assert(kScThreads == 32 * (kScChunk / 4), "embedding staging covers a chunk's tile once");
   using G = ZTile<kBf16>;
-  // LDS slots of the staged tiles: two for bf16 logits; fp32 tiles are twice
-  // as large and take one (160 KiB per CU)
-  constexpr int kZSlots = kBf16 ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t s_z[kZSlots][G::kBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[kZSlots][3][32 * kScBRow];
+  constexpr int kG = G::kGroup;
+  static_assert(kG % 2 == 0, "a group holds whole pairs of chunks (two register slots)");
+  __shared__ __attribute__((aligned(16))) uint8_t s_z[kScThreads / 64][G::kBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kG * kEChunk];
   const int32_t tile = static_cast<int32_t>(blockIdx.x) / a.nslice;
   const int32_t slice = static_cast<int32_t>(blockIdx.x) % a.nslice;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t row0 = tile * kScRowTile;
-  const int trow = wave * 32 + (lane & 31);  // this lane's row in the tile
-  const int32_t row = row0 + trow;
+  const int32_t wrow0 = row0 + wave * 32;
+  const int wr = lane & 31;  // this lane's row among the wave's 32
+  const int32_t row = wrow0 + wr;
+  uint8_t* zw = s_z[wave];
 
-  // rows past the batch or of inactive canvases get zmax*c = +inf, so that
-  // every probability of theirs is exactly 0 whatever their tile holds
-  float c = 1.0f, mc = __builtin_inff();
-  if (row_live(a, row)) {
-    const int64_t off = static_cast<int64_t>(row) * a.row_stride;
-    int32_t am = a.argmax[row];
-    am = am < 0 ? 0 : (am >= a.vocab ? a.vocab - 1 : am);
-    c = kLog2eSc / a.temperature[row / a.canvas_len];
-    mc = logit_at<kBf16>(a.logits, off + am) * c;
-  }
   const int64_t k_begin = static_cast<int64_t>(slice) * a.kslice;
   const int64_t k_end = k_begin + a.kslice < a.vocab ? k_begin + a.kslice : a.vocab;
+  const int32_t nch = static_cast<int32_t>((k_end - k_begin + kScChunk - 1) / kScChunk);
+  const int32_t ngroups = (nch + kG - 1) / kG;
+  // chunk and group starts; past the slice they repeat the last one (loads
+  // that hit the cache and are never used), so every load is issued
+  auto kc_of = [&](int32_t j) { return k_begin + static_cast<int64_t>(j < nch ? j : nch - 1) * kScChunk; };
+  auto kg_of = [&](int32_t g) {
+    return k_begin + static_cast<int64_t>(g < ngroups ? g : ngroups - 1) * kG * kScChunk;
+  };
 
-  // software pipeline: chunk i + 2 is loaded into registers while chunk i is
-  // multiplied out of LDS. With two LDS slots one barrier per chunk both
-  // publishes chunk i and retires the reads of chunk i - 1 (whose slot chunk
-  // i + 1 takes next); with one slot a second barrier guards the slot.
+  // the row's constants: its argmax, temperature and canvas flag are loaded
+  // first (unconditionally, the row clamped into the batch; without a flag
+  // array the argmax word stands in for it), the logit at the argmax once the
+  // argmax is in, behind the pipeline's first loads
+  const int32_t rc = row < a.rows ? row : a.rows - 1;
+  const int32_t canvas = rc / a.canvas_len;
+  const uint8_t* flag =
+      a.active != nullptr ? a.active + canvas : reinterpret_cast<const uint8_t*>(a.argmax + rc);
+  const uint8_t act = *flag;
+  int32_t am = a.argmax[rc];
+  const float temp = a.temperature[canvas];
+
+  // software pipeline: the embedding of group g + 1 and chunk j + 2 are in
+  // flight in registers while chunk j is multiplied
+  // (in this order: the scheduler barriers keep each wait exact)
   Raw<kBf16> raw0, raw1;
-  float ev0[4], ev1[4];
-  load_chunk<kBf16>(a, row0, k_begin, tid, raw0);
-  load_embed(a, k_begin, tid, ev0);
-  if (k_begin + kScChunk < k_end) {
-    load_chunk<kBf16>(a, row0, k_begin + kScChunk, tid, raw1);
-    load_embed(a, k_begin + kScChunk, tid, ev1);
-  }
+  float ev[kG][4];
+  __builtin_amdgcn_sched_barrier(0);
+  load_embed<kG>(a, kg_of(0), tid, ev);
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk<kBf16>(a, wrow0, kc_of(0), lane, raw0);
+  load_chunk<kBf16>(a, wrow0, kc_of(1), lane, raw1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  am = am < 0 ? 0 : (am >= a.vocab ? a.vocab - 1 : am);
+  const float zmax = logit_at<kBf16>(a.logits, static_cast<int64_t>(rc) * a.row_stride + am);
+  // rows past the batch or of inactive canvases get zmax*c = +inf, so that
+  // every probability of theirs is exactly 0 whatever their tile holds
+  const bool live = row < a.rows && (a.active == nullptr || act != 0);
+  const float c = live ? kLog2eSc / temp : 1.0f;
+  const float mc = live ? zmax * c : __builtin_inff();
+
   f32x16_t acc0 = {}, acc1 = {};
-  const int sn = tid & 31, sk = 4 * (tid >> 5);
-  const int bo = (lane & 31) * kScBRow + 8 * half;
-  // kTail: the slice's last chunk reaches past its end; ids there get zero
-  // probability
-  auto run_chunk = [&](auto slot, auto tail, int64_t kc, Raw<kBf16>& raw, float(&ev)[4])
-                       __attribute__((always_inline)) {
-    constexpr int S = decltype(slot)::value;
-    constexpr bool kTail = decltype(tail)::value;
-    constexpr int Z = kZSlots == 2 ? S : 0;
-    uint8_t* zb = s_z[Z];
-    uint16_t(*bb)[32 * kScBRow] = s_b[Z];
-    if constexpr (kZSlots == 1) __syncthreads();  // the previous chunk's LDS reads are done
-    store_chunk<kBf16>(zb, tid, raw);
-    {  // this chunk's embedding parts: 4 consecutive ids of one column
-      const Split3 e0 = split3(ev[0]), e1 = split3(ev[1]), e2 = split3(ev[2]), e3 = split3(ev[3]);
-      const int o = sn * kScBRow + sk;
-      *reinterpret_cast<uint2*>(&bb[0][o]) = make_uint2(pack2(e0.hi, e1.hi), pack2(e2.hi, e3.hi));
-      *reinterpret_cast<uint2*>(&bb[1][o]) = make_uint2(pack2(e0.mid, e1.mid), pack2(e2.mid, e3.mid));
-      *reinterpret_cast<uint2*>(&bb[2][o]) = make_uint2(pack2(e0.lo, e1.lo), pack2(e2.lo, e3.lo));
-    }
-    const int64_t kn = kc + 2 * kScChunk;
-    if (kn < k_end) {
-      load_chunk<kBf16>(a, row0, kn, tid, raw);
-      load_embed(a, kn, tid, ev);
-    }
-    __syncthreads();  // chunk kc is in LDS (and, with two slots, every wave is done with the chunk before it)
-    // this lane's 8 factors of k-step t, split into three parts
-    auto factors = [&](int t, bf16x8_t& xh, bf16x8_t& xm, bf16x8_t& xl) __attribute__((always_inline)) {
-      float z[8];
-      read_step<kBf16>(zb, trow, half, t, z);
-      uint32_t h[8], m[8], l[8];
+  const int bo = wr * kScBRow + 8 * half;
+  // a chunk's operands as this lane reads them from LDS, all at the chunk's
+  // start: its row's logits of the four k-steps and the embedding parts of
+  // its column, in k-step order (LDS answers a wave in order, so each k-step
+  // waits for its own reads only)
+  constexpr int kZq = kBf16 ? 1 : 2;  // 16-byte reads of a k-step's 8 logits
+  struct Operands {
+    u32x4_t z[kScSteps][kZq];
+    bf16x8_t b[kScSteps][3];
+  };
+  auto read_operands = [&](const uint16_t* ec, Operands& o) __attribute__((always_inline)) {
+    static_for<kScSteps>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      const uint8_t* zb = zw + wr * G::kStride + (16 * t + 8 * half) * G::kElem;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z[j], c, -mc));
-        if constexpr (kTail) e = kc + 16 * t + 8 * half + j < k_end ? e : 0.0f;
-        const Split3 sp = split3(e);
-        h[j] = sp.hi;
-        m[j] = sp.mid;
-        l[j] = sp.lo;
+      for (int q = 0; q < kZq; ++q) o.z[t][q] = *reinterpret_cast<const u32x4_t*>(zb + 16 * q);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) o.b[t][p] = *reinterpret_cast<const bf16x8_t*>(ec + 32 * kScBRow * p + bo + 16 * t);
+    });
+  };
+  // this lane's 8 factors of k-step t, split into three parts
+  auto factors = [&](const Operands& o, int t, bf16x8_t& xh, bf16x8_t& xm, bf16x8_t& xl)
+                     __attribute__((always_inline)) {
+    float z[8];
+    if constexpr (kBf16) {
+      const u32x4_t w = o.z[t][0];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        z[2 * h] = __uint_as_float(w[h] << 16);
+        z[2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
       }
-      xh = as_bf16x8(u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])});
-      xm = as_bf16x8(u32x4_t{pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]), pack2(m[6], m[7])});
-      xl = as_bf16x8(u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])});
-    };
-    // the factors of k-step t + 1 are formed while the matrix cores take the
-    // products of step t: the six products are spread through that VALU work
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) z[4 * q + h] = __uint_as_float(o.z[t][q][h]);
+    }
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const Split3 sp = split3(__builtin_amdgcn_exp2f(__builtin_fmaf(z[j], c, -mc)));
+      h[j] = sp.hi;
+      m[j] = sp.mid;
+      l[j] = sp.lo;
+    }
+    xh = as_bf16x8(u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])});
+    xm = as_bf16x8(u32x4_t{pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]), pack2(m[6], m[7])});
+    xl = as_bf16x8(u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])});
+  };
+  // the products of one chunk; the factors of k-step t + 1 are formed while
+  // the matrix cores take the six products of step t, spread through that
+  // VALU work
+  auto multiply = [&](const Operands& o) __attribute__((always_inline)) {
+    // every LDS read of the chunk first, so that each k-step waits for its own
+    __builtin_amdgcn_sched_group_barrier(0x100, kScSteps * (kZq + 3), 0);
     bf16x8_t xh, xm, xl;
-    factors(0, xh, xm, xl);
+    factors(o, 0, xh, xm, xl);
 #pragma unroll
     for (int t = 0; t < kScSteps; ++t) {
-      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&bb[0][bo + 16 * t]);
-      const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(&bb[1][bo + 16 * t]);
-      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&bb[2][bo + 16 * t]);
       bf16x8_t nh = xh, nm = xm, nl = xl;
-      if (t + 1 < kScSteps) factors(t + 1, nh, nm, nl);
+      if (t + 1 < kScSteps) factors(o, t + 1, nh, nm, nl);
+      const bf16x8_t bh = o.b[t][0], bm = o.b[t][1], bl = o.b[t][2];
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, bh, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xm, bm, acc1, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, bl, acc0, 0, 0, 0);
@@ -312,30 +359,44 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
       xl = nl;
     }
   };
-  // chunk i of the slice takes register slot i % 2: a loop over pairs of
-  // whole chunks keeps every slot index a constant; then at most one whole
-  // chunk and the partial one
-  using Slot0 = std::integral_constant<int, 0>;
-  using Slot1 = std::integral_constant<int, 1>;
-  using Full = std::integral_constant<bool, false>;
-  using Tail = std::integral_constant<bool, true>;
-  const int64_t full_end = k_begin + (k_end - k_begin) / kScChunk * kScChunk;
-  int64_t kc = k_begin;
-  for (; kc + kScChunk < full_end; kc += 2 * kScChunk) {
-    run_chunk(Slot0{}, Full{}, kc, raw0, ev0);
-    run_chunk(Slot1{}, Full{}, kc + kScChunk, raw1, ev1);
+
+  // The wave's tile holds chunk 0 before the first group; chunk 2 goes into
+  // its register slot.
+  store_chunk<kBf16>(zw, lane, raw0);
+  load_chunk<kBf16>(a, wrow0, kc_of(2), lane, raw0);
+
+  // Group g: stage its embedding into slot g % 2 (every wave finished reading
+  // that slot, group g - 2, before the barrier of group g - 1), put the next
+  // group's loads in flight, and meet at the group's one barrier. Then each
+  // wave runs the group's chunks on its own tile. Chunk j reads its operands,
+  // then writes chunk j + 1 into the tile (a wave's LDS operations run in
+  // order, so the reads see chunk j), reloads that chunk's register slot,
+  // (j + 1) % 2, a constant since groups hold whole pairs, with chunk j + 3,
+  // and multiplies.
+  for (int32_t g = 0; g < ngroups; ++g) {
+    uint16_t* eb = s_b[g & 1];
+    stage_embed<kG>(eb, a, k_begin + static_cast<int64_t>(g) * kG * kScChunk, k_end, tid, ev);
+    load_embed<kG>(a, kg_of(g + 1), tid, ev);
+    __syncthreads();
+    static_for<kG>([&](auto cc) {
+      constexpr int ci = decltype(cc)::value;
+      const int32_t j = g * kG + ci;
+      Operands o;
+      read_operands(eb + ci * kEChunk, o);
+      Raw<kBf16>& next = ci % 2 == 0 ? raw1 : raw0;
+      store_chunk<kBf16>(zw, lane, next);
+      load_chunk<kBf16>(a, wrow0, kc_of(j + 3), lane, next);
+      // (a chunk past the slice end, in its last group only, meets an all-zero
+      // embedding tile and adds exactly zero; multiplying it anyway keeps the
+      // group's code one block, so its reads are issued here)
+      multiply(o);
+    });
   }
-  if (kc < full_end) {
-    run_chunk(Slot0{}, Full{}, kc, raw0, ev0);
-    if (kc + kScChunk < k_end) run_chunk(Slot1{}, Tail{}, kc + kScChunk, raw1, ev1);
-  } else if (kc < k_end) {
-    run_chunk(Slot0{}, Tail{}, kc, raw0, ev0);
-  }
+
   const f32x16_t acc = acc0 + acc1;
   // lane l, register r holds D[i][n] with n = l % 32 and
   // i = 8 (r / 4) + 4 (l / 32) + r % 4 (the 32x32 fp32 accumulator layout)
   const int n = lane & 31;
-  const int32_t wrow0 = row0 + wave * 32;
   if (a.nslice == 1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -354,44 +415,56 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
 }
 
 // out[r, n] = (sum over slices of partial[s][r][n]) / (same for column d).
-// One workgroup per row: thread t takes columns 4 (t % 8) .. +3 of the slices
-// s = 16 g .. 16 g + 15 of group g = t / 8 (32 groups of 16 slices at a
-// time, more rounds when there are more slices), then the groups' sums are
-// combined in LDS in group order, so the result does not depend on timing.
+// One workgroup per row: thread t takes columns 4 (t % 8) .. +3 of the
+// slices s = g, g + 32, g + 64, ... of group g = t / 8, all its loads in
+// flight at once (rows of inactive canvases are read too and not written, so
+// that no load waits for the flag). The 32 group sums are then combined in a
+// fixed pattern (lanes 8, 16 and 32 apart within each wave, then the four
+// waves in order), so the result does not depend on timing.
 __global__ __launch_bounds__(256) void self_cond_reduce_kernel(SelfCondArgs a) {
-  __shared__ float4 s_part[32][8];
+  constexpr int kPerRound = 8;  // loads per thread and round: 256 slices in one round
+  __shared__ float4 s_wave[4][8];
   const int32_t r = static_cast<int32_t>(blockIdx.x);
-  if (a.active != nullptr && a.active[r / a.canvas_len] == 0) return;  // uniform over the workgroup
-  const int t = threadIdx.x, quad = t & 7, group = t >> 3;
+  const int t = threadIdx.x, quad = t & 7, group = t >> 3, lane = t & 63, wave = t >> 6;
   const int64_t stride = static_cast<int64_t>(a.rows_pad) * 32;
   const float* base = a.partials + static_cast<int64_t>(r) * 32 + 4 * quad;
   float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int32_t s0 = 16 * group; s0 < a.nslice; s0 += 16 * 32) {
-    float4 v[16];
+  for (int32_t s0 = group; s0 < a.nslice; s0 += 32 * kPerRound) {
+    float4 v[kPerRound];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = s0 + i < a.nslice ? *reinterpret_cast<const float4*>(base + (s0 + i) * stride)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < kPerRound; ++i) {
+      const int32_t sl = s0 + 32 * i;
+      v[i] = *reinterpret_cast<const float4*>(base + (sl < a.nslice ? sl : a.nslice - 1) * stride);
+    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sum.x += v[i].x;
-      sum.y += v[i].y;
-      sum.z += v[i].z;
-      sum.w += v[i].w;
+    for (int i = 0; i < kPerRound; ++i) {
+      if (s0 + 32 * i < a.nslice) {
+        sum.x += v[i].x;
+        sum.y += v[i].y;
+        sum.z += v[i].z;
+        sum.w += v[i].w;
+      }
     }
   }
-  s_part[group][quad] = sum;
+#pragma unroll
+  for (int m = 8; m < 64; m <<= 1) {
+    sum.x += __shfl_xor(sum.x, m);
+    sum.y += __shfl_xor(sum.y, m);
+    sum.z += __shfl_xor(sum.z, m);
+    sum.w += __shfl_xor(sum.w, m);
+  }
+  if (lane < 8) s_wave[wave][lane] = sum;
   __syncthreads();
   if (t < 32) {
-    float tot = 0.0f, den = 0.0f;
-    for (int g = 0; g < 32; ++g) {
-      const float4 q = s_part[g][t >> 2];
-      const float4 qd = s_part[g][a.d >> 2];
-      const int k = t & 3, kd = a.d & 3;
-      tot += k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
-      den += kd == 0 ? qd.x : kd == 1 ? qd.y : kd == 2 ? qd.z : qd.w;
-    }
-    if (t < a.d) a.out[static_cast<int64_t>(r) * a.d + t] = tot / den;
+    auto col = [&](int w, int k) {
+      const float4 q = s_wave[w][k >> 2];
+      const int e = k & 3;
+      return e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+    };
+    const float tot = ((col(0, t) + col(1, t)) + col(2, t)) + col(3, t);
+    const float den = ((col(0, a.d) + col(1, a.d)) + col(2, a.d)) + col(3, a.d);
+    if (t < a.d && (a.active == nullptr || a.active[r / a.canvas_len] != 0))
+      a.out[static_cast<int64_t>(r) * a.d + t] = tot / den;
   }
 }
 
