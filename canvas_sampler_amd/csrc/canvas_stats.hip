@@ -39,13 +39,18 @@
 // read twice: if the block beats the wave's best block, or a lane of it holds
 // a new wave maximum, that lane parks the block's 64 logits in LDS, and after
 // its stream the wave finds the first id of its maximum from the parked
-// logits. The workgroup then merges eight 40-byte partials. The sample is
-// drawn in the best block: in the one-row kernel once, by wave 1 in the
-// row's (or split's) best block while wave 0 merges the sums, so the last
-// wave to end its stream does not draw first (measured at 256 x 262144 bf16:
-// 25.9 us against 26.4 us with a draw per wave); in the row loop each wave
-// draws in its own best block before the merge. A row split over several
-// workgroups (for very short batches) writes one partial per split.
+// logits. In the row loop each wave then finds the first id of its maximum,
+// draws the sample in its best block and reduces its sums, and the workgroup
+// merges eight 40-byte partials. In the one-row kernel each wave only
+// publishes its lane sums and wave-level results, and after the barrier three
+// waves finish the row at once: wave 0 the sums and the entropy, wave 1 the
+// sample (drawn once, in the row's best block), wave 2 the first id of the
+// maximum. The last wave to end its stream so reduces, searches and draws
+// nothing before the barrier (measured at 256 x 262144 bf16, each change
+// against the one before in one process: moving the draw off it 26.4 -> 25.9
+// us, then the search and the sums 26.6 -> 26.1 us). A row split over
+// several workgroups (for very short batches) writes one partial per split,
+// its fields by those three waves.
 //
 // partials_merge_kernel merges, one wave per row and in a fixed order, the
 // partials of split rows and the per-tile partials that the LM-head
@@ -437,6 +442,19 @@ struct WaveResult {
   int64_t best_base = 0;
 };
 
+// A wave's results as it ends its stream, published for the row's finish
+// (one-row kernel): its maximum with its first id when already known
+// (exact ties between lanes) or the lane whose parked block holds it, and
+// its best block.
+struct WaveEnd {
+  float m;
+  int32_t wam;
+  int32_t am_lane;
+  int64_t am_base;
+  float best;
+  int32_t bestj;
+};
+
 // Per-row constants of a pass.
 struct RowConsts {
   int32_t pos;      // canvas position (counter word 1)
@@ -660,12 +678,10 @@ __device__ __forceinline__ int32_t draw_in_block(int64_t base, int32_t j, int32_
   return id2;
 }
 
-// The wave's partial once its blocks are done: the parked blocks give the
-// first id of its maximum and (kDraw) the sample inside its best block; the
+// The wave's partial once its blocks are done (row loop): the parked blocks
+// give the first id of its maximum and the sample inside its best block; the
 // sums are rescaled to the wave's largest reference. Every lane returns it.
-// Without kDraw the sample is left to draw_best, after the waves' partials
-// are merged.
-template <bool kBf16, bool kDraw = true>
+template <bool kBf16>
 __device__ __forceinline__ RowPartial wave_partial(const LaneState& st, const WaveResult& wr, int32_t vocab,
                                                    const RowConsts& rc, const uint4* park_best,
                                                    const uint4* park_max, int lane) {
@@ -685,9 +701,7 @@ __device__ __forceinline__ RowPartial wave_partial(const LaneState& st, const Wa
     }
   }
   p.sample = 0x7FFFFFFF;
-  if constexpr (kDraw) {
-    if (wr.wbestj != 0x7FFFFFFF) p.sample = draw_in_block<kBf16>(wr.best_base, wr.wbestj, vocab, rc, park_best, lane);
-  }
+  if (wr.wbestj != 0x7FFFFFFF) p.sample = draw_in_block<kBf16>(wr.best_base, wr.wbestj, vocab, rc, park_best, lane);
   const float rr = wave_max(st.ref);
   double s = 0.0, w = 0.0;
   if (st.ref != kNegInf) {
@@ -710,9 +724,9 @@ __device__ __forceinline__ RowPartial wave_partial(const LaneState& st, const Wa
 // the block its wave parked; 0x7FFFFFFF when no block has a score. Every
 // lane returns it.
 template <bool kBf16>
-__device__ __forceinline__ int32_t draw_best(const RowPartial* s_part, const uint4 (*park)[kChunkStripes * Geometry<kBf16>::kLoadsPerStripe],
+__device__ __forceinline__ int32_t draw_best(const WaveEnd* s_we, const uint4 (*park)[kChunkStripes * Geometry<kBf16>::kLoadsPerStripe],
                                              int32_t vocab, const RowConsts& rc, int lane) {
-  const RowPartial& q = s_part[lane & (kWaves - 1)];
+  const WaveEnd& q = s_we[lane & (kWaves - 1)];
   uint64_t kb = argmax_key(q.best, q.bestj);
   uint32_t wv = static_cast<uint32_t>(lane & (kWaves - 1));
 #define DG_BEST_STEP(J)                  \
@@ -726,9 +740,63 @@ __device__ __forceinline__ int32_t draw_best(const RowPartial* s_part, const uin
   DG_BEST_STEP(4) DG_BEST_STEP(2) DG_BEST_STEP(1)
 #undef DG_BEST_STEP
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(wv));
-  const int32_t j = __builtin_amdgcn_readfirstlane(s_part[w].bestj);
+  const int32_t j = __builtin_amdgcn_readfirstlane(s_we[w].bestj);
   if (j == 0x7FFFFFFF) return 0x7FFFFFFF;
   return draw_in_block<kBf16>(static_cast<int64_t>(j / kSlots) * kChunkIds, j, vocab, rc, park[w], lane);
+}
+
+// The row's maximum and the first id holding it, over the eight waves'
+// published results (wave w's candidates in lanes 8 w .. 8 w + 7, lane 8 w + k
+// searching stripe k of the block wave w parked); every lane returns them.
+template <bool kBf16>
+__device__ __forceinline__ void row_argmax(const WaveEnd* s_we,
+                                           const uint4 (*park)[kChunkStripes * Geometry<kBf16>::kLoadsPerStripe],
+                                           int32_t vocab, int lane, float& m, int32_t& am) {
+  const int w = lane >> 3, sq = lane & 7;
+  const WaveEnd& q = s_we[w];
+  int32_t id = q.wam;
+  if (q.am_lane >= 0) {
+    id = 0x7FFFFFFF;
+    const int64_t id0 = q.am_base + sq * kStripeIds + q.am_lane * kSlotIds;
+#pragma unroll
+    for (int e = 7; e >= 0; --e)
+      id = id0 + e < vocab && parked_logit<kBf16>(park[w], sq, e) == q.m ? static_cast<int32_t>(id0 + e) : id;
+  }
+  id = min(id, static_cast<int32_t>(lane_xor<4>(static_cast<uint32_t>(id))));
+  id = min(id, static_cast<int32_t>(lane_xor<2>(static_cast<uint32_t>(id))));
+  id = min(id, static_cast<int32_t>(lane_xor<1>(static_cast<uint32_t>(id))));
+  if (id == 0x7FFFFFFF) id = q.wam;  // (the holding lane's block always holds it below V)
+  uint64_t k = argmax_key(q.m, id);
+  k = max_u64(k, lane_xor64<8>(k));
+  k = max_u64(k, lane_xor64<16>(k));
+  k = max_u64(k, lane_xor64<32>(k));
+  argmax_unkey(k, m, am);
+}
+
+// The row's sums over the 512 lanes' published sums, each rescaled once to
+// the largest reference (lane l adds waves 0..7 of its column in order, then
+// the wave sums the lanes); every lane returns them.
+__device__ __forceinline__ void row_sums(const double (*s_ls)[kWave], const double (*s_lw)[kWave],
+                                         const float (*s_lr)[kWave], int lane, double& s, double& w, float& ref) {
+  float rl = kNegInf;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) rl = max_raw(rl, s_lr[v][lane]);
+  const float r = wave_max(rl);
+  double ls = 0.0, lw = 0.0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    const float q = s_lr[v][lane];
+    if (q != kNegInf) {
+      const double d = static_cast<double>(q) - static_cast<double>(r);
+      const double f = scale_of(d);
+      const double qs = s_ls[v][lane];
+      ls += f * qs;
+      lw += f * (s_lw[v][lane] + d * qs);
+    }
+  }
+  s = wave_sum(ls);
+  w = wave_sum(lw);
+  ref = r;
 }
 
 // Reduces the batches of a full block in ring slot H into the lane state and
@@ -828,7 +896,11 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
   constexpr uint32_t kEB = Geometry<kBf16>::kElemBytes;
   constexpr int kBB = kChunkStripes / NB;  // batches per block
   static_assert(kChunkStripes % NB == 0, "a block is a whole number of batches");
-  __shared__ RowPartial s_part[kWaves];
+  // each wave's lane sums and wave-level results, published at its end
+  __shared__ double s_ls[kWaves][kWave];   // lane sums of 2^t
+  __shared__ double s_lw[kWaves][kWave];   // lane sums of t 2^t
+  __shared__ float s_lr[kWaves][kWave];    // their references
+  __shared__ WaveEnd s_we[kWaves];
   // per wave: the logits of its best block and of the block holding its
   // maximum (one lane's slot of a chunk each), kept for the end of the pass
   __shared__ __align__(16) uint4 s_blk[kWaves][kChunkStripes * LPS];
@@ -929,39 +1001,64 @@ __global__ __launch_bounds__(kStatsThreads) void canvas_stats_kernel(StatsArgs a
                               s_amx[wave], lane);
   }
 
-  // The sample is drawn once, in the row's best block, by wave 1 while wave
-  // 0 merges the sums: the last wave to end its stream does not draw first.
-  const RowPartial wp = wave_partial<kBf16, false>(st, wr, vocab, rc, s_blk[wave], s_amx[wave], lane);
-  if (lane == 0) s_part[wave] = wp;
+  // Each wave publishes its lane sums and wave-level results and leaves; the
+  // row's finish is then split over three waves at once: wave 0 the sums and
+  // the entropy, wave 1 the sample (drawn once, in the row's best block),
+  // wave 2 the first id of the maximum. The last wave to end its stream so
+  // does no reduction, search or draw before the barrier.
+  s_ls[wave][lane] = st.s;
+  s_lw[wave][lane] = st.w;
+  s_lr[wave][lane] = st.ref;
+  if (lane == 0) s_we[wave] = WaveEnd{wr.wm, wr.wam, wr.am_lane, wr.am_base, wr.wbest, wr.wbestj};
   __syncthreads();
-  if (wave == 1) {
-    const int32_t smp = draw_best<kBf16>(s_part, s_blk, vocab, rc, lane);
-    if (lane == 0) {
-      if (a.nsplit > 1)
-        a.partials[static_cast<int64_t>(r) * a.nsplit + split].sample = smp;
-      else
-        a.sample[r] = smp;
+  RowPartial* part = a.nsplit > 1 ? a.partials + static_cast<int64_t>(r) * a.nsplit + split : nullptr;
+  if (wave == 0) {
+    RowPartial p;
+    row_sums(s_ls, s_lw, s_lr, lane, p.s, p.w, p.ref);
+    if (lane != 0) return;
+    if (part != nullptr) {
+      // a split's partial, written by waves 0-2 field by field;
+      // partials_merge_kernel, next on the stream, merges them
+      part->s = p.s;
+      part->w = p.w;
+      part->ref = p.ref;
+      return;
     }
-    return;
+    const double h = kLn2 * (log2(p.s) - p.w / p.s);
+    const float hf = static_cast<float>(h);
+    a.entropy[r] = hf > 0.0f ? hf : 0.0f;
+  } else if (wave == 1) {
+    const int32_t smp = draw_best<kBf16>(s_we, s_blk, vocab, rc, lane);
+    if (lane != 0) return;
+    if (part != nullptr) {
+      int32_t bj = 0x7FFFFFFF;
+      float bs = kNegInf;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const uint64_t cand = argmax_key(s_we[v].best, s_we[v].bestj);
+        if (cand > argmax_key(bs, bj)) {
+          bs = s_we[v].best;
+          bj = s_we[v].bestj;
+        }
+      }
+      part->best = bs;
+      part->bestj = bj;
+      part->sample = smp;
+      return;
+    }
+    a.sample[r] = smp;
+  } else if (wave == 2) {
+    float m;
+    int32_t am;
+    row_argmax<kBf16>(s_we, s_amx, vocab, lane, m, am);
+    if (lane != 0) return;
+    if (part != nullptr) {
+      part->m = m;
+      part->argmax = am;
+      return;
+    }
+    a.argmax[r] = am;
   }
-  if (wave != 0) return;
-  RowPartial p = merge_waves(s_part, lane);
-  if (lane != 0) return;
-
-  if (a.nsplit > 1) {
-    // a split's partial (wave 1 writes its sample); partials_merge_kernel,
-    // next on the stream, merges them
-    RowPartial& d = a.partials[static_cast<int64_t>(r) * a.nsplit + split];
-    d.s = p.s;
-    d.w = p.w;
-    d.ref = p.ref;
-    d.m = p.m;
-    d.argmax = p.argmax;
-    d.best = p.best;
-    d.bestj = p.bestj;
-    return;
-  }
-  row_output(a, r, p, false);
 }
 
 // Row loop: a persistent grid of workgroups, workgroup b taking rows b,
