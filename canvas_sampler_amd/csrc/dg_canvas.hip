@@ -650,7 +650,14 @@ dg_status check_run(dg_ctx* ctx, int32_t B, const uint64_t* seeds, bool has_deno
   return DG_OK;
 }
 
-dg_status check_selfcond(dg_ctx* ctx, const float* embed, int32_t d, const float* out) {
+dg_status check_selfcond(dg_ctx* ctx, const float* embed, int32_t d, const float* out, dg_dtype dtype,
+                         int64_t row_stride) {
+  // a wave reads 32 logits rows through one buffer resource: their bytes must
+  // stay below 4 GiB
+  const int64_t elem = dtype == DG_DTYPE_BF16 ? 2 : 4;
+  if (row_stride * elem >= (int64_t{1} << 27))
+    return set_err(ctx, DG_ERR_UNSUPPORTED, "self-conditioning needs row_stride * element size below 2^27 bytes "
+                   "(got %lld elements)", static_cast<long long>(row_stride));
   if (!embed) return set_err(ctx, DG_ERR_INVALID_ARG, "embed is NULL");
   if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "selfcond output is NULL");
   if (d < 1 || d > 31) return set_err(ctx, DG_ERR_INVALID_ARG, "d = %d is outside 1..31", d);
@@ -851,7 +858,7 @@ dg_status dg_self_condition(dg_ctx* ctx, int32_t B, const void* logits, dg_dtype
   if ((st = check_logits(ctx, logits, dtype, row_stride)) != DG_OK) return st;
   if (!temperature) return set_err(ctx, DG_ERR_INVALID_ARG, "temperature is NULL");
   if (!argmax) return set_err(ctx, DG_ERR_INVALID_ARG, "argmax is NULL");
-  if ((st = check_selfcond(ctx, embed, d, out)) != DG_OK) return st;
+  if ((st = check_selfcond(ctx, embed, d, out, dtype, row_stride)) != DG_OK) return st;
   DeviceGuard guard(ctx->device);
   return enqueue_selfcond(ctx, B, logits, dtype, row_stride, temperature, argmax, nullptr, embed, d, out,
                           static_cast<hipStream_t>(stream));
@@ -871,7 +878,7 @@ dg_status dg_sampler_step_selfcond(dg_ctx* ctx, int32_t B, const void* logits, d
   if (!seeds) return set_err(ctx, DG_ERR_INVALID_ARG, "seeds is NULL");
   if (!out) return set_err(ctx, DG_ERR_INVALID_ARG, "out is NULL");
   if (!out->canvas_out) return set_err(ctx, DG_ERR_INVALID_ARG, "out->canvas_out is NULL");
-  if ((st = check_selfcond(ctx, embed, d, selfcond_out)) != DG_OK) return st;
+  if ((st = check_selfcond(ctx, embed, d, selfcond_out, dtype, row_stride)) != DG_OK) return st;
   DeviceGuard guard(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ent = out->entropy_out ? out->entropy_out : ctx->entropy;

@@ -31,9 +31,12 @@
 //     at d (its sum is the normaliser S = sum_v e_v) and zeros above, and
 //     zeros for ids past the slice; the workgroup meets at one barrier per
 //     such group;
-//   - every load is unconditional (clamped addresses), so each wait is for
-//     exactly the data it needs: the next group's embedding and the chunks
-//     two and three ahead stay in flight while a chunk is multiplied;
+//   - every load is a buffer load issued on every path, its resource ending
+//     where the data ends (rows past the batch and ids past the slice read
+//     zeros), so each wait is for exactly the data it needs: the next
+//     group's embedding and the chunks two and three ahead stay in flight
+//     while a chunk is multiplied; ids past the vocabulary (the row's
+//     padding) are set to -inf in the one chunk that holds any;
 //   - one slice per row tile: the workgroup divides by S and writes out;
 //     otherwise it writes its unnormalised partial tile, and a second kernel
 //     sums the slices in a fixed order and divides.
@@ -53,16 +56,6 @@ constexpr float kLog2eSc = 1.4426950408889634f;
 constexpr int kScChunk = 64;
 constexpr int kScSteps = kScChunk / 16;     // k-steps of 16 ids per chunk
 constexpr int kScBRow = kScChunk + 8;      // bf16 per LDS row (padding spreads the banks)
-
-template <bool kBf16>
-__device__ __forceinline__ float logit_at(const void* base, int64_t i) {
-  if constexpr (kBf16) {
-    const uint16_t b = static_cast<const uint16_t*>(base)[i];
-    return __uint_as_float(static_cast<uint32_t>(b) << 16);
-  } else {
-    return static_cast<const float*>(base)[i];
-  }
-}
 
 // Geometry of one wave's staged logits tile of a chunk: the wave's 32 rows of
 // 64 ids, each row padded by 16 bytes so that the 16-byte matrix-layout reads
@@ -109,30 +102,42 @@ struct Raw {
   u32x4_t q[ZTile<kBf16>::kPieces];
 };
 
+// The wave's 32 logits rows through one buffer resource based at its first
+// row; its records end with the batch's last row, so rows past the batch
+// read zeros (they never count: see the kernel). The 32 rows' bytes stay
+// below 4 GiB (the entry points check the row stride).
+template <bool kBf16>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const SelfCondArgs& a, int32_t wrow0) {
+  constexpr int64_t kElem = ZTile<kBf16>::kElem;
+  const int32_t left = a.rows - wrow0;
+  const int64_t nrows = left <= 0 ? 0 : (left >= 32 ? 32 : left);
+  const uintptr_t base =
+      reinterpret_cast<uintptr_t>(a.logits) + static_cast<uint64_t>(static_cast<int64_t>(wrow0) * a.row_stride * kElem);
+  // (the wave's values, kept scalar: the compiler cannot see that every lane
+  // holds the same)
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base >> 32));
+  const uint32_t num = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(nrows * a.row_stride * kElem));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0,
+                                           static_cast<int>(num), 0x00020000);
+}
+
 // This lane's pieces of a chunk of the wave's rows, loaded with whole lines
 // per row and instruction: piece p = lane + 64 i is 16-byte piece
-// p % kPiecesPerRow of wave row p / kPiecesPerRow. Every load is
-// unconditional, so that the number of loads in flight is the same on every
-// path and each wait is for exactly the chunk it needs: rows past the batch
-// are clamped onto the last row and ids past the row's stride onto its last
-// piece. What those clamped pieces hold never counts: a row that does not
-// take part has zero probability everywhere (see the kernel), and ids at or
-// past the slice end meet zero embedding rows.
+// p % kPiecesPerRow of wave row p / kPiecesPerRow, at byte offset
+// loff + i * step + kc * size (loff = the lane's offset of piece `lane` at id
+// 0, step = the bytes of the rows that 64 pieces span). Every load is issued
+// on every path, so each wait is for exactly the chunk it needs. Ids past
+// the row's end read the next row's values or zeros; they are past the
+// vocabulary, and the chunk that holds them is masked before it is staged.
 template <bool kBf16>
-__device__ __forceinline__ void load_chunk(const SelfCondArgs& a, int32_t wrow0, int64_t kc, int lane,
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rows, uint32_t loff, uint32_t step, int64_t kc,
                                            Raw<kBf16>& r) {
   using G = ZTile<kBf16>;
+  const uint32_t kb = static_cast<uint32_t>(kc) * G::kElem;
   static_for<G::kPieces>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const int piece = lane + 64 * i;
-    const int32_t row = min(wrow0 + piece / G::kPiecesPerRow, a.rows - 1);
-    int64_t id = kc + static_cast<int64_t>(piece % G::kPiecesPerRow) * G::kPerPiece;
-    id = id < a.row_stride - G::kPerPiece ? id : a.row_stride - G::kPerPiece;
-    const int64_t off = static_cast<int64_t>(row) * a.row_stride + id;
-    if constexpr (kBf16)
-      r.q[i] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.logits) + off);
-    else
-      r.q[i] = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(a.logits) + off);
+    r.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rows, loff + (i * step + kb), 0, 0);
   });
 }
 
@@ -145,6 +150,26 @@ __device__ __forceinline__ void store_chunk(uint8_t* s_z, int lane, const Raw<kB
     *reinterpret_cast<u32x4_t*>(s_z + (piece / G::kPiecesPerRow) * G::kStride + (piece % G::kPiecesPerRow) * 16) =
         r.q[i];
   });
+}
+
+// In the wave's staged tile of the chunk from id kc, ids at or past the
+// vocabulary (only the last chunk of a row holds any) become -inf, so that
+// whatever the rows' padding holds, their probabilities are exactly 0. Lane
+// l rewrites row l % 32, every other id from the first past the vocabulary.
+// (A loop of LDS writes in its own branch: the compiler does not fold it into
+// the common path.)
+template <bool kBf16>
+__device__ __forceinline__ void mask_past_vocab(uint8_t* zw, int64_t kc, int32_t vocab, int lane) {
+  using G = ZTile<kBf16>;
+  if (kc + kScChunk <= vocab) return;
+  const int first = static_cast<int>(vocab - kc);  // a chunk starts inside the vocabulary
+  uint8_t* rowp = zw + (lane & 31) * G::kStride;
+  for (int id = first + (lane >> 5); id < kScChunk; id += 2) {
+    if constexpr (kBf16)
+      *reinterpret_cast<uint16_t*>(rowp + 2 * id) = 0xFF80u;
+    else
+      *reinterpret_cast<uint32_t*>(rowp + 4 * id) = 0xFF800000u;
+  }
 }
 
 // Exact three-part split of an fp32 value x = hi + mid + lo into bf16 values,
@@ -176,19 +201,24 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 // The embedding values this thread stages for a group of kGroup chunks from
 // id kg: column n = tid % 32 (clamped onto column d - 1; the staging puts the
 // ones and zeros above d), ids kg + 64 c + 4 (tid / 32) .. +3 of chunk c.
-// The loads are unconditional, ids clamped onto the last embedding row; ids
-// at or past the slice end are zeroed when the group is staged.
+// Chunk c is read through a buffer resource of its own, based at its first
+// row and holding its rows before the slice end (none for a chunk past it),
+// so ids at or past the slice end read zeros, at the thread's fixed offsets
+// voff[i] = ((4 (tid / 32) + i) d + n) * 4 bytes: no per-load address
+// arithmetic, and every load is issued on every path.
 template <int kG>
-__device__ __forceinline__ void load_embed(const SelfCondArgs& a, int64_t kg, int tid, float (&ev)[kG][4]) {
-  const int n = tid & 31;
-  const int nc = n < a.d ? n : a.d - 1;
+__device__ __forceinline__ void load_embed(const SelfCondArgs& a, int64_t kg, int64_t k_end, const uint32_t (&voff)[4],
+                                           float (&ev)[kG][4]) {
   static_for<kG>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
+    const int64_t k0 = kg + 64 * c;
+    const int64_t left = k_end - k0;
+    const int32_t nrows = left <= 0 ? 0 : (left >= 64 ? 64 : static_cast<int32_t>(left));
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.embed) + k0 * a.d, 0, nrows * a.d * 4, 0x00020000);
     static_for<4>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      int64_t v = kg + 64 * c + 4 * (tid >> 5) + i;
-      v = v < a.vocab ? v : a.vocab - 1;
-      ev[c][i] = a.embed[v * a.d + nc];
+      ev[c][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff[i], 0, 0));
     });
   });
 }
@@ -196,25 +226,37 @@ __device__ __forceinline__ void load_embed(const SelfCondArgs& a, int64_t kg, in
 // Stages a group's embedding tiles: E[v, n] below d, ones at d, zeros above,
 // and zeros for ids at or past the slice end (so that the probabilities
 // formed there, from clamped or neighbouring logits, never count), split into
-// three parts, column n's 4 ids as one 8-byte write per part.
-template <int kG>
-__device__ __forceinline__ void stage_embed(uint16_t* eb, const SelfCondArgs& a, int64_t kg, int64_t k_end,
-                                            int tid, const float (&ev)[kG][4]) {
+// three parts, column n's 4 ids as one 8-byte write per part. The loads read
+// zeros past the slice end; only the ones column tests the ids there, and
+// only in the group that reaches past it.
+template <int kG, typename X>
+__device__ __forceinline__ void stage_parts(uint16_t* eb, int tid, X&& value) {
   const int n = tid & 31, sk = 4 * (tid >> 5);
   static_for<kG>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = n < a.d ? ev[c][i] : (n == a.d ? 1.0f : 0.0f);
-      x[i] = kg + 64 * c + sk + i < k_end ? e : 0.0f;
-    }
+    for (int i = 0; i < 4; ++i) x[i] = value(c, i);
     const Split3 e0 = split3(x[0]), e1 = split3(x[1]), e2 = split3(x[2]), e3 = split3(x[3]);
     uint16_t* b = eb + c * kEChunk + n * kScBRow + sk;
     *reinterpret_cast<uint2*>(b) = make_uint2(pack2(e0.hi, e1.hi), pack2(e2.hi, e3.hi));
     *reinterpret_cast<uint2*>(b + 32 * kScBRow) = make_uint2(pack2(e0.mid, e1.mid), pack2(e2.mid, e3.mid));
     *reinterpret_cast<uint2*>(b + 64 * kScBRow) = make_uint2(pack2(e0.lo, e1.lo), pack2(e2.lo, e3.lo));
   });
+}
+
+template <int kG>
+__device__ __forceinline__ void stage_embed(uint16_t* eb, const SelfCondArgs& a, int64_t kg, int64_t k_end, int tid,
+                                            const float (&ev)[kG][4]) {
+  const int n = tid & 31, sk = 4 * (tid >> 5);
+  const bool data = n < a.d;
+  const float one = n == a.d ? 1.0f : 0.0f;
+  if (kg + 64 * kG <= k_end) {
+    stage_parts<kG>(eb, tid, [&](int c, int i) { return data ? ev[c][i] : one; });
+  } else {
+    const int32_t lim = static_cast<int32_t>(k_end - kg) - sk;  // ids 64 c + i below lim count
+    stage_parts<kG>(eb, tid, [&](int c, int i) { return data ? ev[c][i] : (64 * c + i < lim ? one : 0.0f); });
+  }
 }
 
 template <bool kBf16>
@@ -246,32 +288,57 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
     return k_begin + static_cast<int64_t>(g < ngroups ? g : ngroups - 1) * kG * kScChunk;
   };
 
-  // the row's constants: its argmax, temperature and canvas flag are loaded
-  // first (unconditionally, the row clamped into the batch; without a flag
-  // array the argmax word stands in for it), the logit at the argmax once the
-  // argmax is in, behind the pipeline's first loads
-  const int32_t rc = row < a.rows ? row : a.rows - 1;
-  const int32_t canvas = rc / a.canvas_len;
-  const uint8_t* flag =
-      a.active != nullptr ? a.active + canvas : reinterpret_cast<const uint8_t*>(a.argmax + rc);
-  const uint8_t act = *flag;
-  int32_t am = a.argmax[rc];
-  const float temp = a.temperature[canvas];
+  // the row's constants, through buffer resources like every other load
+  // (a row past the batch reads zeros, and so does the flag without a flag
+  // array): its argmax, temperature and canvas flag first, the logit at the
+  // argmax once the argmax is in, behind the pipeline's first loads. The flag
+  // is read through the aligned 32-bit word that holds it.
+  const int32_t ncanvas = (a.rows + a.canvas_len - 1) / a.canvas_len;
+  const int32_t canvas = row / a.canvas_len;
+  const uint32_t fmis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a.active) & 3u);
+  const __amdgpu_buffer_rsrc_t r_flag = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.active) - fmis, 0, a.active != nullptr ? static_cast<int>((fmis + ncanvas + 3) & ~3u) : 0,
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t r_am =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.argmax), 0, a.rows * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t r_temp =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.temperature), 0, ncanvas * 4, 0x00020000);
+  const uint32_t fbyte = fmis + static_cast<uint32_t>(canvas);
+  const uint32_t fword = __builtin_amdgcn_raw_buffer_load_b32(r_flag, fbyte & ~3u, 0, 0);
+  int32_t am = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(r_am, static_cast<uint32_t>(row) * 4, 0, 0));
+  const float temp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_temp, static_cast<uint32_t>(canvas) * 4, 0, 0));
 
   // software pipeline: the embedding of group g + 1 and chunk j + 2 are in
   // flight in registers while chunk j is multiplied
   // (in this order: the scheduler barriers keep each wait exact)
+  const __amdgpu_buffer_rsrc_t rows = rows_rsrc<kBf16>(a, wrow0);
+  const uint32_t loff = static_cast<uint32_t>(
+      ((lane / G::kPiecesPerRow) * a.row_stride + (lane % G::kPiecesPerRow) * G::kPerPiece) * G::kElem);
+  const uint32_t lstep = static_cast<uint32_t>((64 / G::kPiecesPerRow) * a.row_stride * G::kElem);
   Raw<kBf16> raw0, raw1;
   float ev[kG][4];
+  uint32_t voff[4];
+  {
+    const int en = tid & 31;
+    const int nc = en < a.d ? en : a.d - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[i] = static_cast<uint32_t>(((4 * (tid >> 5) + i) * a.d + nc) * 4);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  load_embed<kG>(a, kg_of(0), tid, ev);
+  load_embed<kG>(a, kg_of(0), k_end, voff, ev);
   __builtin_amdgcn_sched_barrier(0);
-  load_chunk<kBf16>(a, wrow0, kc_of(0), lane, raw0);
-  load_chunk<kBf16>(a, wrow0, kc_of(1), lane, raw1);
+  load_chunk<kBf16>(rows, loff, lstep, kc_of(0), raw0);
+  load_chunk<kBf16>(rows, loff, lstep, kc_of(1), raw1);
   __builtin_amdgcn_sched_barrier(0);
 
   am = am < 0 ? 0 : (am >= a.vocab ? a.vocab - 1 : am);
-  const float zmax = logit_at<kBf16>(a.logits, static_cast<int64_t>(rc) * a.row_stride + am);
+  const uint32_t zoff = static_cast<uint32_t>((wr * a.row_stride + am) * G::kElem);
+  float zmax;
+  if constexpr (kBf16)
+    zmax = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rows, zoff, 0, 0)) << 16);
+  else
+    zmax = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows, zoff, 0, 0));
+  const uint32_t act = (fword >> (8 * (fbyte & 3u))) & 0xFFu;
   // rows past the batch or of inactive canvases get zmax*c = +inf, so that
   // every probability of theirs is exactly 0 whatever their tile holds
   const bool live = row < a.rows && (a.active == nullptr || act != 0);
@@ -363,7 +430,8 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
   // The wave's tile holds chunk 0 before the first group; chunk 2 goes into
   // its register slot.
   store_chunk<kBf16>(zw, lane, raw0);
-  load_chunk<kBf16>(a, wrow0, kc_of(2), lane, raw0);
+  mask_past_vocab<kBf16>(zw, kc_of(0), a.vocab, lane);
+  load_chunk<kBf16>(rows, loff, lstep, kc_of(2), raw0);
 
   // Group g: stage its embedding into slot g % 2 (every wave finished reading
   // that slot, group g - 2, before the barrier of group g - 1), put the next
@@ -376,7 +444,7 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
   for (int32_t g = 0; g < ngroups; ++g) {
     uint16_t* eb = s_b[g & 1];
     stage_embed<kG>(eb, a, k_begin + static_cast<int64_t>(g) * kG * kScChunk, k_end, tid, ev);
-    load_embed<kG>(a, kg_of(g + 1), tid, ev);
+    load_embed<kG>(a, kg_of(g + 1), k_end, voff, ev);
     __syncthreads();
     static_for<kG>([&](auto cc) {
       constexpr int ci = decltype(cc)::value;
@@ -385,7 +453,8 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
       read_operands(eb + ci * kEChunk, o);
       Raw<kBf16>& next = ci % 2 == 0 ? raw1 : raw0;
       store_chunk<kBf16>(zw, lane, next);
-      load_chunk<kBf16>(a, wrow0, kc_of(j + 3), lane, next);
+      mask_past_vocab<kBf16>(zw, kc_of(j + 1), a.vocab, lane);
+      load_chunk<kBf16>(rows, loff, lstep, kc_of(j + 3), next);
       // (a chunk past the slice end, in its last group only, meets an all-zero
       // embedding tile and adds exactly zero; multiplying it anyway keeps the
       // group's code one block, so its reads are issued here)

@@ -332,7 +332,10 @@ dg_status dg_generate(dg_ctx* ctx, int32_t B, const uint64_t* seeds, int32_t n_c
  * one fp32 rounding, and sums run in fp32 (order unspecified but fixed, so
  * the result is reproducible). With d = 30 at V = 262144 the embedding holds
  * 7,864,320 parameters.
- *   logits, dtype, row_stride  as for dg_canvas_stats
+ *   logits, dtype, row_stride  as for dg_canvas_stats, and row_stride times
+ *                the element size below 2^27 bytes (V up to about 64 M bf16
+ *                or 32 M fp32 ids), else DG_ERR_UNSUPPORTED; ids from V to
+ *                row_stride (the padding) never count, whatever they hold
  *   temperature  device float [B], each > 0
  *   argmax       device int32 [B*L]: the row's largest-logit id, as
  *                dg_canvas_stats writes it (the softmax is taken relative to

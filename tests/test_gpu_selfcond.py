@@ -31,7 +31,7 @@ TOL_BOUND = 1.0e-3
 TOL_TYPICAL = 2.0e-5
 
 
-def _run(L, V, Bn, dtype, d, temps, gen=31, m_max=8.0, rows_check=None, stride=None):
+def _run(L, V, Bn, dtype, d, temps, gen=31, m_max=8.0, rows_check=None, stride=None, pad=3.0):
     require_gpu()
     ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=Bn)
     z = torch.cat([synth.margin_logits(gen + c, L, V, m_max=m_max, dtype=dtype, device="cuda")
@@ -39,7 +39,7 @@ def _run(L, V, Bn, dtype, d, temps, gen=31, m_max=8.0, rows_check=None, stride=N
     if stride is None and V % 8:
         stride = (V + 7) // 8 * 8   # rows must start on 16-byte boundaries
     if stride is not None:
-        buf = torch.full((z.shape[0], stride), 3.0, dtype=dtype, device="cuda")
+        buf = torch.full((z.shape[0], stride), pad, dtype=dtype, device="cuda")
         buf[:, :V] = z
         z_in = buf
     else:
@@ -110,6 +110,15 @@ def test_row_stride_padding_is_ignored():
     _run(64, 1000, 2, torch.bfloat16, 30, [0.8, 0.5], stride=1024)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("pad", [float("nan"), float("inf"), 1.0e30])
+def test_row_padding_values_never_count(pad, dtype):
+    # whatever the ids between V and the row stride hold (NaN, +inf, a value
+    # far above every logit), they take no part in the softmax: V = 1000 with
+    # a stride of 1024 puts 24 padding ids in the last 64-id chunk of each row
+    _run(64, 1000, 2, dtype, 30, [0.8, 0.5], stride=1024, pad=pad)
+
+
 def test_rejects_bad_arguments():
     require_gpu()
     ctx = B.Context(B.params_default(canvas_len=8, vocab=64), max_batch=1)
@@ -127,6 +136,11 @@ def test_rejects_bad_arguments():
     with pytest.raises(B.DgError, match="argmax"):
         ctx._chk(B.lib().dg_self_condition(ctx.handle, 1, z.data_ptr(), B.DG_DTYPE_F32, 64, t.data_ptr(),
                                            None, E.data_ptr(), 4, out.data_ptr(), None))
+    # a wave reads 32 rows through one 32-bit buffer range: row_stride * 4
+    # bytes must stay below 2^27 (checked before anything is read)
+    st = B.lib().dg_self_condition(ctx.handle, 1, z.data_ptr(), B.DG_DTYPE_F32, 1 << 25, t.data_ptr(),
+                                   am.data_ptr(), E.data_ptr(), 4, out.data_ptr(), None)
+    assert st == B.DG_ERR_UNSUPPORTED and "row_stride" in B.lib().dg_last_error(ctx.handle).decode()
 
 
 def test_extreme_rows():
