@@ -449,6 +449,16 @@ __global__ __launch_bounds__(kScThreads) void self_cond_kernel(SelfCondArgs a) {
     static_for<kG>([&](auto cc) {
       constexpr int ci = decltype(cc)::value;
       const int32_t j = g * kG + ci;
+      // The older wave of each SIMD (waves 0-3) wins the issue arbiter and
+      // would finish the group's chunks well before the younger one, then
+      // wait at the next barrier while the younger runs alone; the younger
+      // waves take the lead for the group's first half instead.
+      if constexpr (ci == 0) {
+        if (wave >= 4) __builtin_amdgcn_s_setprio(1);
+      }
+      if constexpr (ci == kG / 2) {
+        if (wave >= 4) __builtin_amdgcn_s_setprio(0);
+      }
       Operands o;
       read_operands(eb + ci * kEChunk, o);
       Raw<kBf16>& next = ci % 2 == 0 ? raw1 : raw0;
