@@ -234,3 +234,55 @@ def test_step_with_selfcond_matches_separate_calls_and_skips_inactive(Bn, V):
         worst = max(worst, float(ratio.max()))
     assert worst <= TOL_TYPICAL, worst
     print(f"B={Bn} V={V}: step outputs identical; active rows max |err| / sum p|E| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+def test_step_with_selfcond_reads_flags_at_any_byte_offset(offset):
+    # the canvas flags start `offset` bytes into an allocation: the kernels
+    # read each flag through the aligned 32-bit word that holds it, so every
+    # canvas must still see its own flag
+    L, V, Bn, d = 256, 4096, 6, 30
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=Bn)
+    z = torch.cat([synth.margin_logits(500 + c, L, V, m_max=8.0, dtype=torch.bfloat16, device="cuda")
+                   for c in range(Bn)])
+    E = synth.selfcond_embedding(13, V, d, device="cuda")
+    t = torch.tensor([0.8, 0.6, 0.5, 0.7, 0.4, 0.9], device="cuda")
+    seeds = seeds_tensor(list(range(Bn)))
+    flags = [1, 0, 1, 1, 0, 1]
+    buf = torch.full((Bn + 8,), 0xAB, dtype=torch.uint8, device="cuda")
+    buf[offset:offset + Bn] = torch.tensor(flags, dtype=torch.uint8, device="cuda")
+    active = buf[offset:offset + Bn]
+    assert active.data_ptr() % 4 == offset % 4
+    prev = torch.zeros(Bn * L, dtype=torch.int32, device="cuda")
+
+    def outs():
+        return dict(canvas_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    argmax_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    sample_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    entropy_out=torch.full((Bn * L,), -1.0, device="cuda"),
+                    accept_out=torch.full((Bn * L,), 9, dtype=torch.uint8, device="cuda"),
+                    n_accept_out=torch.full((Bn,), -1, dtype=torch.int32, device="cuda"),
+                    stop_out=torch.full((Bn,), 9, dtype=torch.uint8, device="cuda"))
+
+    a, b = outs(), outs()
+    ctx.dg_sampler_step(z, t, 1, seeds, ctx.step_out(**a), prev_argmax=prev, active=active)
+    sc = torch.full((Bn * L, d), 7.0, device="cuda")
+    ctx.dg_sampler_step_selfcond(z, t, 1, seeds, E, sc, ctx.step_out(**b), prev_argmax=prev, active=active)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    g = sc.cpu().numpy().astype(np.float64)
+    Eh = E.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for c in range(Bn):
+        rows = slice(c * L, (c + 1) * L)
+        if not flags[c]:
+            assert np.all(g[rows] == 7.0), f"inactive canvas {c} was written"
+            continue
+        zh = host_values(z[rows])
+        T = np.float32(t[c].item())
+        ratio = np.abs(g[rows] - SC.self_condition(zh, T, Eh)) / SC.magnitude(zh, T, Eh)
+        worst = max(worst, float(ratio.max()))
+    assert worst <= TOL_TYPICAL, worst
+    print(f"flags at byte offset {offset}: step outputs identical; active rows max |err| / sum p|E| = {worst:.2e}")
