@@ -286,3 +286,57 @@ def test_step_with_selfcond_reads_flags_at_any_byte_offset(offset):
         worst = max(worst, float(ratio.max()))
     assert worst <= TOL_TYPICAL, worst
     print(f"flags at byte offset {offset}: step outputs identical; active rows max |err| / sum p|E| = {worst:.2e}")
+
+
+def test_step_with_selfcond_graph_replays():
+    # the step with the matmul (statistics, matmul and its reduction,
+    # acceptance) captured into one graph: every replay (new logits copied
+    # in, other work and a synchronisation between replays) must equal the
+    # eager call bit for bit
+    L, V, Bn, d = 256, 4096, 2, 30
+    require_gpu()
+    ctx = B.Context(B.params_default(canvas_len=L, vocab=V), max_batch=Bn)
+    zs = [torch.cat([synth.margin_logits(700 + 10 * k + c, L, V, m_max=8.0, dtype=torch.bfloat16,
+                                         device="cuda") for c in range(Bn)]) for k in range(2)]
+    E = synth.selfcond_embedding(17, V, d, device="cuda")
+    t = torch.tensor([0.8, 0.5], device="cuda")
+    seeds = seeds_tensor([3, 4])
+    prev = torch.zeros(Bn * L, dtype=torch.int32, device="cuda")
+
+    def outs():
+        return dict(canvas_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    argmax_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    sample_out=torch.full((Bn * L,), -1, dtype=torch.int32, device="cuda"),
+                    entropy_out=torch.full((Bn * L,), -1.0, device="cuda"),
+                    accept_out=torch.full((Bn * L,), 9, dtype=torch.uint8, device="cuda"),
+                    n_accept_out=torch.full((Bn,), -1, dtype=torch.int32, device="cuda"),
+                    stop_out=torch.full((Bn,), 9, dtype=torch.uint8, device="cuda"))
+
+    eager = []
+    for k in range(2):
+        o = outs()
+        sc = torch.full((Bn * L, d), 7.0, device="cuda")
+        ctx.dg_sampler_step_selfcond(zs[k], t, 1, seeds, E, sc, ctx.step_out(**o), prev_argmax=prev)
+        torch.cuda.synchronize()
+        eager.append((o, sc))
+    z = zs[0].clone()
+    o = outs()
+    sc = torch.full((Bn * L, d), 7.0, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ctx.dg_sampler_step_selfcond(z, t, 1, seeds, E, sc, ctx.step_out(**o), prev_argmax=prev)
+    torch.cuda.synchronize()
+    for k in (0, 1, 0, 1):
+        z.copy_(zs[k])
+        for v in o.values():
+            v.fill_(-1 if v.dtype != torch.uint8 else 9)
+        sc.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eo, esc = eager[k]
+        for key in o:
+            assert torch.equal(o[key], eo[key]), (k, key)
+        assert torch.equal(sc, esc), k
+    print("graph replays of the step with the matmul equal the eager calls")
